@@ -1,0 +1,314 @@
+"""Plain fp64 CPU oracle for attention-score-based KV-cache selection.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, constants or
+helpers with the HIP library; it is written from the definitions on the pages,
+slowly and obviously, in float64 numpy.
+
+What it computes (one sequence ``b`` and one KV head ``h`` at a time):
+
+1. Observation rows.  The last ``w`` prompt positions ``L-w .. L-1`` form the
+   window; optionally one decode-step row sits at position ``L`` and sees every
+   prefix key.  (SnapKV-style observation window: TideKV, "Delayed KV Eviction
+   via Layer-Wise Chunked Prefill", §4.2; decode-aware window: "DeferKV Guide:
+   Eviction Timing for KV Cache Compression", section "Phase 2: The
+   Decode-Aware Observation Window and Temporal Weighting".)
+2. Logits ``s[r, i] = scale * <q_r, k_i>`` with ``scale = 1/sqrt(d)`` by
+   default (TideKV §4.2, Eq. (4) -- the formula itself is missing from the
+   extracted page; the DeferKV guide's code divides by sqrt(d)).
+3. Causal visibility: a window row at position ``p`` sees keys ``i <= p``
+   (TideKV §4.2: keys beyond a query's causal position get -inf).  The decode
+   row sees all ``L`` prefix keys.
+4. Per-row softmax over the visible keys, computed with an explicit max and
+   sum (the plain definition; TideKV's blockwise two-pass procedure reaches the
+   same values, §4.2, and ``blockwise_row_stats`` below restates it).
+5. Aggregation: ``S[i] = sum_{g in group h} sum_r c_r * P_{g,r}[i]`` -- per
+   query-head softmax, then a sum over the group's query heads (TideKV §4.2:
+   scores aggregated at KV-head granularity) and over the window rows.  Row
+   weights ``c_r = 1`` without a decode row; with one, ``1 - alpha`` for the
+   prompt rows and ``alpha`` for the decode row (the DeferKV guide's
+   prompt-vs-decode weighting, in its two-level form).
+6. 1-D pool of odd width ``K`` and stride 1 (no page defines it; reading:
+   ``avg`` = zero-padded window sum divided by ``K``, ``max`` = max over the
+   in-range positions only).
+7. Top-k: order positions by (descending score, ascending index) and keep the
+   first ``min(k, L)``; return them in ascending position order (the DeferKV
+   guide sorts the kept indices; TideKV keeps original positions, §5).
+8. Gather: the kept rows of K and V, copied exactly (TideKV §4.2 and §5).
+
+Query-head ``g`` belongs to KV head ``g // G`` with ``G = Hq // Hkv``
+(consecutive grouping, as the DeferKV guide's code reshapes the heads).
+
+Every function is pinned by tests that do not call it to check itself:
+hand-worked 8-token examples with closed-form values, closed forms for
+constant queries, the row-sum invariant, brute-force full causal attention,
+library pooling routines, exhaustive subset enumeration for top-k and
+``numpy.take`` for the gather.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "observation_positions",
+    "visible_mask",
+    "row_weights",
+    "row_probabilities",
+    "head_scores",
+    "pool1d",
+    "select_topk",
+    "gather_rows",
+    "blockwise_row_stats",
+    "blockwise_head_scores",
+    "plan_offsets",
+    "compress",
+]
+
+
+def _check_finite(*arrays):
+    for a in arrays:
+        if not np.all(np.isfinite(a)):
+            raise ValueError("oracle inputs must be finite (NaN/Inf are undefined)")
+
+
+def observation_positions(L: int, w: int, has_decode: bool) -> np.ndarray:
+    """Absolute positions of the observation rows of one sequence.
+
+    Window rows are the last ``w`` prompt positions ``L-w .. L-1``; the
+    optional decode-step row follows at position ``L`` (DeferKV guide, Phase 2;
+    TideKV §4.2 observation queries).
+    """
+    if not (1 <= w <= L):
+        raise ValueError("need 1 <= w <= L")
+    pos = list(range(L - w, L))
+    if has_decode:
+        pos.append(L)
+    return np.asarray(pos, dtype=np.int64)
+
+
+def visible_mask(positions: np.ndarray, L: int, causal: bool) -> np.ndarray:
+    """Boolean [rows, L]: which prefix keys each observation row may attend to.
+
+    With ``causal`` a row at position ``p`` sees keys ``i <= p`` (TideKV §4.2);
+    a decode row (``p == L``) therefore sees all ``L`` keys.  Without
+    ``causal`` every row sees every prefix key (the DeferKV guide's code).
+    """
+    keys = np.arange(L)[None, :]
+    if causal:
+        return keys <= positions[:, None]
+    return np.ones((len(positions), L), dtype=bool)
+
+
+def row_weights(w: int, has_decode: bool, alpha: float) -> np.ndarray:
+    """Weights ``c_r`` of the observation rows.
+
+    All ones for a prompt-only window; with a decode row, ``1 - alpha`` for
+    each prompt row and ``alpha`` for the decode row.
+    """
+    if not has_decode:
+        return np.ones(w, dtype=np.float64)
+    c = np.full(w + 1, 1.0 - alpha, dtype=np.float64)
+    c[w] = alpha
+    return c
+
+
+def row_probabilities(q_rows: np.ndarray, K_h: np.ndarray, vis: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax attention probabilities of each observation row over the prefix.
+
+    ``q_rows`` [R, d], ``K_h`` [L, d], ``vis`` [R, L] -> P [R, L] with
+    ``P[r, i] = exp(s[r,i] - M_r) / sum_{j visible} exp(s[r,j] - M_r)`` on the
+    visible keys and 0 elsewhere, ``s = scale * q_rows @ K_h.T``.
+    """
+    logits = scale * (q_rows @ K_h.T)
+    masked = np.where(vis, logits, -np.inf)
+    m = masked.max(axis=1, keepdims=True)
+    e = np.where(vis, np.exp(masked - m), 0.0)
+    z = e.sum(axis=1, keepdims=True)
+    return e / z
+
+
+def head_scores(Q_b: np.ndarray, K_b: np.ndarray, h: int, Hkv: int, *, w: int, has_decode: bool,
+                alpha: float, causal: bool, scale: float) -> np.ndarray:
+    """Aggregated importance ``S[i]`` of one (sequence, KV head).
+
+    ``Q_b`` [w', Hq, d] observation queries of the sequence (decode row last),
+    ``K_b`` [L, Hkv, d] its keys.  Sums ``c_r * P`` over the window rows and the
+    ``G`` query heads of group ``h``.
+    """
+    L = K_b.shape[0]
+    Hq = Q_b.shape[1]
+    G = Hq // Hkv
+    pos = observation_positions(L, w, has_decode)
+    vis = visible_mask(pos, L, causal)
+    c = row_weights(w, has_decode, alpha)
+    K_h = K_b[:, h, :]
+    S = np.zeros(L, dtype=np.float64)
+    for gi in range(G):
+        g = h * G + gi
+        P = row_probabilities(Q_b[:, g, :], K_h, vis, scale)
+        S += (c[:, None] * P).sum(axis=0)
+    return S
+
+
+def pool1d(S: np.ndarray, kind: str, kernel: int) -> np.ndarray:
+    """Stride-1, odd-width 1-D pool producing one value per position.
+
+    ``avg``: sum of ``S[j]`` for ``j`` in ``[i-r, i+r]`` (positions outside the
+    sequence count as 0) divided by ``kernel``; ``max``: maximum over the
+    positions of that window that lie inside the sequence; ``none``: identity.
+    ``r = (kernel - 1) // 2``.
+    """
+    if kernel < 1 or kernel % 2 == 0:
+        raise ValueError("pool kernel must be odd and >= 1")
+    L = S.shape[0]
+    if kind == "none" or kernel == 1:
+        return S.copy()
+    r = (kernel - 1) // 2
+    out = np.empty(L, dtype=np.float64)
+    for i in range(L):
+        lo, hi = max(0, i - r), min(L, i + r + 1)
+        if kind == "avg":
+            out[i] = S[lo:hi].sum() / kernel
+        elif kind == "max":
+            out[i] = S[lo:hi].max()
+        else:
+            raise ValueError(f"unknown pool kind {kind!r}")
+    return out
+
+
+def select_topk(P: np.ndarray, k: int) -> np.ndarray:
+    """Positions of the ``min(k, L)`` largest values, ascending.
+
+    Ordering is by descending value, then ascending position, so among equal
+    values the lower position is kept.
+    """
+    L = P.shape[0]
+    keff = max(0, min(int(k), L))
+    order = np.lexsort((np.arange(L), -P))  # primary key: -P, secondary: position
+    return np.sort(order[:keff]).astype(np.int64)
+
+
+def gather_rows(X_b: np.ndarray, idx: np.ndarray, h: int) -> np.ndarray:
+    """Rows ``X_b[idx, h, :]`` (exact copies) of one sequence and KV head."""
+    return X_b[idx, h, :].copy()
+
+
+def blockwise_row_stats(q_rows: np.ndarray, K_h: np.ndarray, vis: np.ndarray, scale: float,
+                        block: int):
+    """TideKV pass 1 (§4.2): streaming max / sum of exponentials per row.
+
+    Keys are visited in blocks of ``block``; for every row the running maximum
+    ``m`` and the running sum ``Z`` of ``exp(s - m)`` are updated block by
+    block, rescaling the previous sum whenever the maximum grows (the online
+    normaliser of Milakov & Gimelshein, 2018).  Returns ``(M, Z)`` per row.
+    """
+    R, L = vis.shape
+    m = np.full(R, -np.inf)
+    Z = np.zeros(R)
+    for start in range(0, L, block):
+        stop = min(L, start + block)
+        s = scale * (q_rows @ K_h[start:stop].T)
+        v = vis[:, start:stop]
+        s = np.where(v, s, -np.inf)
+        bm = s.max(axis=1)
+        new_m = np.maximum(m, bm)
+        for r in range(R):
+            if new_m[r] == -np.inf:
+                continue  # nothing visible yet for this row
+            rescale = np.exp(m[r] - new_m[r]) if m[r] != -np.inf else 0.0
+            Z[r] = Z[r] * rescale + np.exp(s[r][v[r]] - new_m[r]).sum()
+            m[r] = new_m[r]
+    return m, Z
+
+
+def blockwise_head_scores(Q_b: np.ndarray, K_b: np.ndarray, h: int, Hkv: int, *, w: int,
+                          has_decode: bool, alpha: float, causal: bool, scale: float,
+                          block: int) -> np.ndarray:
+    """TideKV's two-pass blockwise scoring (§4.2) for one (sequence, KV head).
+
+    Pass 1 gathers ``(M_r, Z_r)`` with :func:`blockwise_row_stats`; pass 2
+    revisits the key blocks, recomputes the logits and adds
+    ``c_r * exp(s - M_r) / Z_r`` into the per-key sum.  Mathematically equal
+    to :func:`head_scores`.
+    """
+    L = K_b.shape[0]
+    Hq = Q_b.shape[1]
+    G = Hq // Hkv
+    pos = observation_positions(L, w, has_decode)
+    vis = visible_mask(pos, L, causal)
+    c = row_weights(w, has_decode, alpha)
+    K_h = K_b[:, h, :]
+    S = np.zeros(L)
+    for gi in range(G):
+        q = Q_b[:, h * G + gi, :]
+        M, Z = blockwise_row_stats(q, K_h, vis, scale, block)
+        for start in range(0, L, block):
+            stop = min(L, start + block)
+            s = scale * (q @ K_h[start:stop].T)
+            p = np.where(vis[:, start:stop], np.exp(s - M[:, None]), 0.0) / Z[:, None]
+            S[start:stop] += (c[:, None] * p).sum(axis=0)
+    return S
+
+
+def plan_offsets(seq_lens, Hkv: int, budgets) -> np.ndarray:
+    """Output segment offsets: segment ``(b, h)`` holds ``min(k_bh, L_b)`` rows.
+
+    Segments are ordered sequence-major, head-minor; returns ``B*Hkv + 1``
+    prefix offsets (TideKV §4.1: head-adaptive budgets give a flattened
+    variable-length layout with per-head offsets).
+    """
+    out = [0]
+    for b, L in enumerate(seq_lens):
+        for h in range(Hkv):
+            out.append(out[-1] + max(0, min(int(budgets[b][h]), int(L))))
+    return np.asarray(out, dtype=np.int64)
+
+
+def compress(Q, K, V, *, seq_lens, Hq: int, Hkv: int, w: int, has_decode: bool = False,
+             alpha: float = 0.0, causal: bool = True, scale=None, pool: str = "none",
+             pool_kernel: int = 1, k=None, budgets=None, heads=None):
+    """Whole path for a packed batch.
+
+    ``Q`` [B, w', Hq, d]; ``K``, ``V`` [sum L_b, Hkv, d] (sequences packed
+    back to back); float64 arrays holding the exact bf16 input values.  Either a
+    uniform ``k`` or ``budgets`` [B][Hkv].  ``heads`` optionally restricts the
+    work to a list of ``(b, h)`` pairs (the others are left out of the result).
+
+    Returns a dict keyed by ``(b, h)`` with ``scores``, ``pooled``, ``idx``,
+    ``K_out`` and ``V_out``, plus ``out_offsets``.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    _check_finite(Q, K, V)
+    B = len(seq_lens)
+    d = K.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    if budgets is None:
+        budgets = [[k] * Hkv for _ in range(B)]
+    starts = np.concatenate([[0], np.cumsum(seq_lens)])
+    want = set(heads) if heads is not None else None
+    res = {"out_offsets": plan_offsets(seq_lens, Hkv, budgets)}
+    for b in range(B):
+        K_b = K[starts[b]:starts[b + 1]]
+        V_b = V[starts[b]:starts[b + 1]]
+        for h in range(Hkv):
+            if want is not None and (b, h) not in want:
+                continue
+            S = head_scores(Q[b], K_b, h, Hkv, w=w, has_decode=has_decode, alpha=alpha,
+                            causal=causal, scale=scale)
+            P = pool1d(S, pool, pool_kernel)
+            idx = select_topk(P, budgets[b][h])
+            res[(b, h)] = {
+                "scores": S,
+                "pooled": P,
+                "idx": idx,
+                "K_out": gather_rows(K_b, idx, h),
+                "V_out": gather_rows(V_b, idx, h),
+            }
+    return res

@@ -1,0 +1,431 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Closed forms are evaluated here with ``math``; brute force uses scipy's and
+torch's own attention/softmax routines; top-k uses exhaustive enumeration;
+pooling uses torch's pooling routines.  The ``mutation`` tests plant plausible
+mistakes in the oracle (on the CPU) and check that some pin catches each one.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle.kvsel_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+E = math.e
+
+
+def _hand():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _closed_forms():
+    """Expected aggregated scores S of the hand examples (before pooling)."""
+    Z = 2 * E**2 + E + 5  # row at position 7, q=+1: logits [2,0,0,1,0,0,0,2]
+    a, b, c = E**2 / Z, 1 / Z, E / Z
+    p_plus = [a, b, b, c, b, b, b, a]
+    Z6 = E**2 + E + 5  # row at position 6 sees keys 0..6 only
+    p6 = [E**2 / Z6, 1 / Z6, 1 / Z6, E / Z6, 1 / Z6, 1 / Z6, 1 / Z6, 0.0]
+    Zm = 2 * math.exp(-2) + math.exp(-1) + 5  # q=-1: logits [-2,0,0,-1,0,0,0,-2]
+    p_minus = [math.exp(-2) / Zm, 1 / Zm, 1 / Zm, math.exp(-1) / Zm, 1 / Zm, 1 / Zm, 1 / Zm, math.exp(-2) / Zm]
+    return {
+        "ex1": p_plus,
+        "ex2": [x + y for x, y in zip(p6, p_plus)],
+        "ex3": [x + y for x, y in zip(p_plus, p_minus)],
+        "ex4": [0.5 * x + 0.5 * y for x, y in zip(p_plus, p_minus)],
+        "ex4_a025": [0.75 * x + 0.25 * y for x, y in zip(p_plus, p_minus)],
+        "p_plus": p_plus,
+        "p_minus": p_minus,
+    }
+
+
+def _run_hand(ex, keys_c0, d=128, alpha=None, scale=1.0):
+    L = len(keys_c0)
+    Hq, Hkv = ex["Hq"], ex["Hkv"]
+    K = np.zeros((L, Hkv, d))
+    K[:, :, 0] = np.asarray(keys_c0, dtype=float)[:, None]
+    V = np.zeros((L, Hkv, d))
+    V[:, :, 0] = np.arange(L)[:, None]
+    Q = np.zeros((1, len(ex["q_c0"]), Hq, d))
+    Q[0, :, :, 0] = np.asarray(ex["q_c0"], dtype=float)
+    return O.compress(Q, K, V, seq_lens=[L], Hq=Hq, Hkv=Hkv, w=ex["w"], has_decode=ex["has_decode"],
+                      alpha=ex["alpha"] if alpha is None else alpha, causal=ex["causal"], scale=scale,
+                      pool=ex["pool"], pool_kernel=ex["pool_kernel"], k=ex["k"])
+
+
+def _expected_scores(name):
+    cf = _closed_forms()
+    if name.startswith("ex1"):
+        return cf["ex1"]
+    return cf[name[:3]]
+
+
+def _expected_pooled(ex):
+    S = _expected_scores(ex["name"])
+    L, K = len(S), ex["pool_kernel"]
+    r = (K - 1) // 2
+    if ex["pool"] == "none":
+        return S
+    out = []
+    for i in range(L):
+        win = [S[j] for j in range(i - r, i + r + 1) if 0 <= j < L]
+        out.append(sum(win) / K if ex["pool"] == "avg" else max(win))
+    return out
+
+
+# ---------------------------------------------------------------- hand examples
+@pytest.mark.parametrize("ex", _hand()["examples"], ids=lambda e: e["name"])
+def test_hand_examples(ex):
+    keys = _hand()["keys_c0"]
+    res = _run_hand(ex, keys)[(0, 0)]
+    np.testing.assert_allclose(res["scores"], _expected_scores(ex["name"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(res["pooled"], _expected_pooled(ex), rtol=0, atol=1e-13)
+    assert res["idx"].tolist() == ex["expect_idx"]
+
+
+def test_hand_values_printed_in_blueprint():
+    """Six-digit values of the hand examples, as derived by hand."""
+    cf = _closed_forms()
+    np.testing.assert_allclose(cf["ex1"][:4], [0.328455, 0.044452, 0.044452, 0.120832], atol=1e-6)
+    np.testing.assert_allclose(cf["ex2"][:4], [0.817559, 0.110645, 0.110645, 0.300763], atol=1e-6)
+    np.testing.assert_allclose(cf["ex3"][:4], [0.352457, 0.221802, 0.221802, 0.186076], atol=1e-6)
+    np.testing.assert_allclose(sum(cf["ex3"]), 2.0, atol=1e-14)
+    np.testing.assert_allclose(sum(cf["ex4"]), 1.0, atol=1e-14)
+
+
+def test_decode_weight_asymmetric():
+    ex = [e for e in _hand()["examples"] if e["name"].startswith("ex4")][0]
+    res = _run_hand(ex, _hand()["keys_c0"], alpha=0.25)[(0, 0)]
+    np.testing.assert_allclose(res["scores"], _closed_forms()["ex4_a025"], atol=1e-13)
+
+
+def test_default_scale_is_inverse_sqrt_d():
+    # d = 64: scale 1/8, so q = 8 reproduces the unit-scale logits of example 1.
+    ex = dict(_hand()["examples"][0])
+    ex["q_c0"] = [[8]]
+    res = _run_hand(ex, _hand()["keys_c0"], d=64, scale=None)[(0, 0)]
+    np.testing.assert_allclose(res["scores"], _closed_forms()["ex1"], atol=1e-13)
+
+
+def test_consecutive_query_head_grouping():
+    # KV head 0 holds the example keys, KV head 1 all-zero keys.  Query heads
+    # 0,1 (group 0) use q=+1; heads 2,3 (group 1) use q=-1.
+    L, d = 8, 128
+    K = np.zeros((L, 2, d))
+    K[:, 0, 0] = _hand()["keys_c0"]
+    Q = np.zeros((1, 1, 4, d))
+    Q[0, 0, :2, 0] = 1.0
+    Q[0, 0, 2:, 0] = -1.0
+    res = O.compress(Q, K, K, seq_lens=[L], Hq=4, Hkv=2, w=1, scale=1.0, k=8)
+    np.testing.assert_allclose(res[(0, 0)]["scores"], [2 * x for x in _closed_forms()["p_plus"]], atol=1e-13)
+    np.testing.assert_allclose(res[(0, 1)]["scores"], [2 / 8] * 8, atol=1e-14)
+
+
+# ---------------------------------------------------------------- closed forms and invariants
+def test_zero_queries_give_uniform_rows():
+    L, d = 8, 16
+    rng = np.random.default_rng(0)
+    K = rng.standard_normal((L, 1, d))
+    Q = np.zeros((1, 2, 1, d))
+    res = O.compress(Q, K, K, seq_lens=[L], Hq=1, Hkv=1, w=2, k=3)[(0, 0)]
+    expect = [1 / 7 + 1 / 8] * 7 + [1 / 8]
+    np.testing.assert_allclose(res["scores"], expect, atol=1e-15)
+    assert res["idx"].tolist() == [0, 1, 2]
+
+
+def test_equal_keys_give_uniform_rows_for_any_query():
+    L, d = 11, 8
+    rng = np.random.default_rng(1)
+    K = np.tile(rng.standard_normal((1, 1, d)), (L, 1, 1))
+    Q = rng.standard_normal((1, 3, 1, d)) * 5
+    res = O.compress(Q, K, K, seq_lens=[L], Hq=1, Hkv=1, w=3, k=2)[(0, 0)]
+    expect = [sum(1 / (L - 3 + r + 1) for r in range(3))] * (L - 2) + [1 / (L - 1) + 1 / L, 1 / L]
+    np.testing.assert_allclose(res["scores"], expect, atol=1e-14)
+
+
+@pytest.mark.parametrize("has_decode,alpha", [(False, 0.0), (True, 0.3)])
+def test_rows_sum_to_one_and_total_mass(has_decode, alpha):
+    rng = np.random.default_rng(2)
+    L, d, Hq, Hkv, w = 50, 32, 6, 2, 7
+    K = rng.standard_normal((L, Hkv, d))
+    Q = rng.standard_normal((1, w + has_decode, Hq, d)) * 3
+    pos = O.observation_positions(L, w, has_decode)
+    vis = O.visible_mask(pos, L, True)
+    P = O.row_probabilities(Q[0, :, 0, :], K[:, 0, :], vis, 1 / math.sqrt(d))
+    assert np.all(np.abs(P.sum(axis=1) - 1) <= 1e-12)
+    assert np.all(P[~vis] == 0)
+    res = O.compress(Q, K, K, seq_lens=[L], Hq=Hq, Hkv=Hkv, w=w, has_decode=has_decode, alpha=alpha, k=5)
+    G = Hq // Hkv
+    mass = G * (w * (1 - alpha) + alpha) if has_decode else G * w
+    for h in range(Hkv):
+        assert abs(res[(0, h)]["scores"].sum() - mass) <= 1e-11
+
+
+# ---------------------------------------------------------------- brute force
+def test_matches_full_causal_attention_scipy():
+    """Last w rows of full L x L causal softmax attention (scipy)."""
+    rng = np.random.default_rng(3)
+    L, d, w = 40, 16, 6
+    K = rng.standard_normal((L, d))
+    Qfull = rng.standard_normal((L, d)) * 2
+    logits = Qfull @ K.T / math.sqrt(d)
+    logits[np.triu_indices(L, 1)] = -np.inf
+    A = scipy.special.softmax(logits, axis=1)
+    pos = O.observation_positions(L, w, False)
+    P = O.row_probabilities(Qfull[L - w:], K, O.visible_mask(pos, L, True), 1 / math.sqrt(d))
+    np.testing.assert_allclose(P, A[L - w:], rtol=0, atol=1e-14)
+
+
+def test_matches_torch_sdpa_attention_matrix():
+    """torch's fp64 scaled-dot-product attention with V = identity returns the
+    attention matrix itself; its causal last rows must equal the oracle's."""
+    rng = np.random.default_rng(4)
+    L, d, w, G = 33, 16, 5, 3
+    K = rng.standard_normal((L, 1, d))
+    Qfull = rng.standard_normal((G, L, d)) * 2
+    A = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Qfull)[None], torch.from_numpy(K[:, 0, :])[None, None].expand(1, G, L, d),
+        torch.eye(L, dtype=torch.float64)[None, None].expand(1, G, L, L), is_causal=True)[0].numpy()
+    Q = Qfull[:, L - w:, :].transpose(1, 0, 2)[None]  # [1, w, G, d]
+    S = O.head_scores(Q[0], K, 0, 1, w=w, has_decode=False, alpha=0.0, causal=True, scale=1 / math.sqrt(d))
+    np.testing.assert_allclose(S, A[:, L - w:, :].sum(axis=(0, 1)), rtol=0, atol=1e-13)
+
+
+def test_noncausal_decode_row_sees_whole_prefix():
+    rng = np.random.default_rng(5)
+    L, d = 20, 8
+    K = rng.standard_normal((L, d))
+    q = rng.standard_normal((1, d))
+    A = scipy.special.softmax(q @ K.T / math.sqrt(d), axis=1)
+    pos = O.observation_positions(L, 3, True)
+    vis = O.visible_mask(pos, L, True)
+    assert vis[-1].all() and pos[-1] == L
+    P = O.row_probabilities(q, K, vis[-1:], 1 / math.sqrt(d))
+    np.testing.assert_allclose(P, A, atol=1e-15)
+
+
+# ---------------------------------------------------------------- TideKV's two-pass blockwise form
+@pytest.mark.parametrize("block", [1, 3, 16, 64])
+def test_blockwise_two_pass_equals_dense(block):
+    rng = np.random.default_rng(6)
+    L, d, Hq, Hkv, w = 61, 16, 4, 2, 9
+    K = rng.standard_normal((L, Hkv, d)) * 2
+    Q = rng.standard_normal((w + 1, Hq, d)) * 3
+    kw = dict(w=w, has_decode=True, alpha=0.4, causal=True, scale=0.7)
+    for h in range(Hkv):
+        dense = O.head_scores(Q, K, h, Hkv, **kw)
+        blocked = O.blockwise_head_scores(Q, K, h, Hkv, block=block, **kw)
+        np.testing.assert_allclose(blocked, dense, rtol=1e-12, atol=1e-15)
+
+
+def test_blockwise_stats_match_logsumexp():
+    rng = np.random.default_rng(7)
+    L, d = 100, 8
+    K = rng.standard_normal((L, d)) * 4
+    q = rng.standard_normal((3, d)) * 4
+    vis = O.visible_mask(O.observation_positions(L, 3, False), L, True)
+    M, Z = O.blockwise_row_stats(q, K, vis, 1.0, 7)
+    logits = np.where(vis, q @ K.T, -np.inf)
+    np.testing.assert_allclose(M + np.log(Z), scipy.special.logsumexp(logits, axis=1), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- pool
+@pytest.mark.parametrize("kernel", [1, 3, 5, 7, 9])
+def test_pool_matches_torch(kernel):
+    rng = np.random.default_rng(kernel)
+    S = rng.random(23)
+    t = torch.from_numpy(S)[None, None]
+    avg = torch.nn.functional.avg_pool1d(t, kernel, stride=1, padding=kernel // 2, count_include_pad=True)
+    mx = torch.nn.functional.max_pool1d(t, kernel, stride=1, padding=kernel // 2)
+    np.testing.assert_allclose(O.pool1d(S, "avg", kernel), avg[0, 0].numpy(), rtol=1e-15, atol=1e-16)
+    np.testing.assert_array_equal(O.pool1d(S, "max", kernel), mx[0, 0].numpy())
+    np.testing.assert_array_equal(O.pool1d(S, "none", kernel), S)
+
+
+def test_pool_short_sequences():
+    S = np.array([0.5, 0.25])
+    np.testing.assert_allclose(O.pool1d(S, "avg", 7), [0.75 / 7, 0.75 / 7])
+    np.testing.assert_array_equal(O.pool1d(S, "max", 7), [0.5, 0.5])
+    with pytest.raises(ValueError):
+        O.pool1d(S, "avg", 4)
+
+
+# ---------------------------------------------------------------- top-k
+def _brute_topk(P, k):
+    """The unique k-subset whose every member beats every non-member
+    (higher value, or equal value and lower position)."""
+    L = len(P)
+    k = min(k, L)
+    hits = []
+    for sub in itertools.combinations(range(L), k):
+        s = set(sub)
+        if all(P[i] > P[j] or (P[i] == P[j] and i < j) for i in s for j in range(L) if j not in s):
+            hits.append(list(sub))
+    assert len(hits) == 1
+    return hits[0]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_matches_exhaustive(seed):
+    rng = np.random.default_rng(seed)
+    L = int(rng.integers(1, 11))
+    P = rng.integers(0, 4, L).astype(float) / 4  # many exact ties
+    if seed % 3 == 0:
+        P = rng.random(L)
+    for k in range(0, L + 2):
+        assert O.select_topk(P, k).tolist() == _brute_topk(P, k)
+
+
+def test_topk_clamps_and_empties():
+    P = np.array([3.0, 1.0, 2.0])
+    assert O.select_topk(P, 0).tolist() == []
+    assert O.select_topk(P, 10).tolist() == [0, 1, 2]
+
+
+# ---------------------------------------------------------------- gather and plan
+def test_gather_is_take():
+    rng = np.random.default_rng(8)
+    X = rng.standard_normal((30, 3, 4))
+    idx = np.array([0, 5, 6, 29])
+    np.testing.assert_array_equal(O.gather_rows(X, idx, 2), np.take(X[:, 2, :], idx, axis=0))
+
+
+def test_plan_offsets_by_hand():
+    off = O.plan_offsets([10, 3], 2, [[4, 20], [0, 2]])
+    assert off.tolist() == [0, 4, 14, 14, 16]
+
+
+def test_compress_ragged_consistency():
+    rng = np.random.default_rng(9)
+    lens = [12, 5, 30]
+    Hq, Hkv, d, w = 4, 2, 8, 3
+    K = rng.standard_normal((sum(lens), Hkv, d))
+    V = rng.standard_normal((sum(lens), Hkv, d))
+    Q = rng.standard_normal((3, w, Hq, d))
+    budgets = [[4, 12], [9, 0], [1, 30]]
+    res = O.compress(Q, K, V, seq_lens=lens, Hq=Hq, Hkv=Hkv, w=w, pool="max", pool_kernel=3, budgets=budgets)
+    starts = np.cumsum([0] + lens)
+    for b, L in enumerate(lens):
+        for h in range(Hkv):
+            r = res[(b, h)]
+            assert len(r["idx"]) == min(budgets[b][h], L)
+            assert np.all(np.diff(r["idx"]) > 0)
+            np.testing.assert_array_equal(r["V_out"], V[starts[b] + r["idx"], h])
+            # isolated check of this sequence alone
+            alone = O.compress(Q[b:b + 1], K[starts[b]:starts[b + 1]], V[starts[b]:starts[b + 1]], seq_lens=[L],
+                               Hq=Hq, Hkv=Hkv, w=w, pool="max", pool_kernel=3, budgets=[budgets[b]])
+            np.testing.assert_array_equal(alone[(0, h)]["idx"], r["idx"])
+
+
+def test_rejects_nonfinite():
+    K = np.zeros((4, 1, 8))
+    K[0, 0, 0] = np.nan
+    with pytest.raises(ValueError):
+        O.compress(np.zeros((1, 1, 1, 8)), K, K, seq_lens=[4], Hq=1, Hkv=1, w=1, k=1)
+
+
+# ---------------------------------------------------------------- planted mistakes
+def _pins_pass():
+    """Run the pins above in-process; return False as soon as one fails."""
+    checks = [
+        lambda: [test_hand_examples(ex) for ex in _hand()["examples"]],
+        test_decode_weight_asymmetric,
+        test_default_scale_is_inverse_sqrt_d,
+        test_consecutive_query_head_grouping,
+        test_zero_queries_give_uniform_rows,
+        lambda: test_rows_sum_to_one_and_total_mass(True, 0.3),
+        test_matches_full_causal_attention_scipy,
+        lambda: [test_pool_matches_torch(k) for k in (3, 5)],
+        lambda: [test_topk_matches_exhaustive(s) for s in range(6)],
+        test_gather_is_take,
+    ]
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            return False
+    return True
+
+
+def _no_causal(positions, L, causal):
+    return np.ones((len(positions), L), dtype=bool)
+
+
+def _mean_rows(w, has_decode, alpha):
+    c = np.ones(w + int(has_decode))
+    if has_decode:
+        c[:w] = 1 - alpha
+        c[w] = alpha
+    return c / len(c)
+
+
+def _swapped_alpha(w, has_decode, alpha):
+    c = np.ones(w + int(has_decode))
+    if has_decode:
+        c[:w] = alpha
+        c[w] = 1 - alpha
+    return c
+
+
+def _high_index_ties(P, k):
+    L = len(P)
+    keff = max(0, min(int(k), L))
+    order = np.lexsort((-np.arange(L), -P))
+    return np.sort(order[:keff])
+
+
+def _avg_exclude_pad(S, kind, kernel):
+    if kind != "avg":
+        return O.pool1d.__wrapped__(S, kind, kernel)
+    r = (kernel - 1) // 2
+    return np.array([S[max(0, i - r):i + r + 1].mean() for i in range(len(S))])
+
+
+def _off_by_one_window(L, w, has_decode):
+    pos = list(range(L - w - 1, L - 1))
+    if has_decode:
+        pos.append(L)
+    return np.asarray(pos)
+
+
+def _no_max_subtraction_sum_mismatch(q_rows, K_h, vis, scale):
+    logits = scale * (q_rows @ K_h.T)
+    e = np.where(vis, np.exp(logits), 0.0)
+    return e / e.sum()  # normalised over the whole matrix, not per row
+
+
+def _wrong_gather(X_b, idx, h):
+    return X_b[idx, (h + 1) % X_b.shape[1], :].copy()
+
+
+MUTATIONS = {
+    "no_causal_mask": ("visible_mask", _no_causal),
+    "mean_not_sum_over_rows": ("row_weights", _mean_rows),
+    "alpha_swapped": ("row_weights", _swapped_alpha),
+    "ties_to_higher_index": ("select_topk", _high_index_ties),
+    "avg_pool_excludes_padding": ("pool1d", _avg_exclude_pad),
+    "window_off_by_one": ("observation_positions", _off_by_one_window),
+    "softmax_not_per_row": ("row_probabilities", _no_max_subtraction_sum_mismatch),
+    "gather_wrong_head": ("gather_rows", _wrong_gather),
+}
+
+
+def test_pins_pass_unmutated():
+    assert _pins_pass()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    original = getattr(O, attr)
+    fn.__wrapped__ = original
+    monkeypatch.setattr(O, attr, fn)
+    assert not _pins_pass(), f"mutation {name} slipped past every pin"
