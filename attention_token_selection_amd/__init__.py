@@ -1,0 +1,20 @@
+"""kvsel: attention-score-based KV-cache selection for AMD MI355X (gfx950).
+
+The compute lives in libkvsel.so (hand-written HIP kernels behind the C ABI
+in include/kvsel.h); this package only builds and binds it.
+"""
+
+from .kvsel import (  # noqa: F401
+    KvselError,
+    Problem,
+    abi_version,
+    alloc_outputs,
+    bind_compress,
+    compress,
+    exported_functions,
+    kvsel_compress,
+    kvsel_gather,
+    kvsel_plan,
+    kvsel_pool_topk,
+    kvsel_score,
+)

@@ -1,0 +1,395 @@
+// Host side of libkvsel: validation, planning, workspace layout and kernel
+// launches behind the C ABI declared in include/kvsel.h.
+#include "kvsel.h"
+#include "kvsel_internal.h"
+
+#include <atomic>
+#include <chrono>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include <unistd.h>
+
+#define KVSEL_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace kvsel;
+
+thread_local std::string g_last_error;
+
+kvsel_status fail(kvsel_status s, const std::string &msg) {
+  g_last_error = msg;
+  return s;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Everything the launches need, derived from a validated kvsel_problem.
+struct Plan {
+  int B, Hq, Hkv, G, w, wp, R, nrt, nrg, Rpad, ks;
+  int has_decode, causal, pool, pool_kernel;
+  float alpha, cl2;
+  std::vector<int64_t> seq_off;  // B + 1
+  std::vector<int32_t> keff;     // B * Hkv
+  std::vector<int64_t> out_off;  // B * Hkv + 1
+  int64_t Lmax = 0;
+  int kb1 = 0, kb2 = 0, nblk1_max = 0, nblk2_max = 0;
+  size_t off_tickets = 0, off_partials = 0, off_bias = 0, off_scores = 0, off_pooled = 0, ws_bytes = 0;
+};
+
+int auto_key_block(int64_t head_keys, int waves_per_wg, int ks, int cap) {
+  // Aim for about 2048 waves over the launch (8 per compute unit).
+  const int64_t wgs = std::max<int64_t>(1, 2048 / waves_per_wg);
+  int64_t kb = (head_keys + wgs - 1) / wgs;
+  const int64_t unit = (int64_t)kTile * ks;
+  kb = (kb + unit - 1) / unit * unit;
+  kb = std::max<int64_t>(kb, unit * 4);
+  kb = std::min<int64_t>(kb, cap);
+  return (int)kb;
+}
+
+kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
+  if (!p) return fail(KVSEL_EINVAL, "problem pointer is NULL");
+  if (p->batch < 1) return fail(KVSEL_EINVAL, "batch must be >= 1");
+  if (p->Hkv < 1 || p->Hq < 1) return fail(KVSEL_EINVAL, "Hq and Hkv must be >= 1");
+  if (p->Hq % p->Hkv != 0) return fail(KVSEL_EINVAL, "Hq must be a multiple of Hkv");
+  if (p->d < 1) return fail(KVSEL_EINVAL, "d must be >= 1");
+  if (p->w < 1) return fail(KVSEL_EINVAL, "w must be >= 1");
+  if (p->has_decode != 0 && p->has_decode != 1) return fail(KVSEL_EINVAL, "has_decode must be 0 or 1");
+  if (p->causal != 0 && p->causal != 1) return fail(KVSEL_EINVAL, "causal must be 0 or 1");
+  if (p->has_decode && !(p->alpha >= 0.0f && p->alpha <= 1.0f)) return fail(KVSEL_EINVAL, "alpha must lie in [0, 1]");
+  if (!std::isfinite(p->scale)) return fail(KVSEL_EINVAL, "scale must be finite");
+  if (p->pool < KVSEL_POOL_NONE || p->pool > KVSEL_POOL_MAX) return fail(KVSEL_EINVAL, "unknown pool kind");
+  if (p->pool != KVSEL_POOL_NONE && (p->pool_kernel < 1 || p->pool_kernel % 2 == 0))
+    return fail(KVSEL_EINVAL, "pool_kernel must be odd and >= 1");
+  if (p->key_chunk < 0 || p->key_chunk % kTile != 0) return fail(KVSEL_EINVAL, "key_chunk must be 0 or a positive multiple of 16");
+  if (!p->budgets_h && p->k < 0) return fail(KVSEL_EINVAL, "k must be >= 0");
+
+  P.B = p->batch;
+  P.Hq = p->Hq;
+  P.Hkv = p->Hkv;
+  P.G = p->Hq / p->Hkv;
+  P.w = p->w;
+  P.wp = p->w + p->has_decode;
+  P.seq_off.assign(P.B + 1, 0);
+  if (p->seq_offsets_h) {
+    if (p->seq_offsets_h[0] != 0) return fail(KVSEL_EINVAL, "seq_offsets_h[0] must be 0");
+    for (int b = 0; b < P.B; ++b) {
+      const int64_t Lb = p->seq_offsets_h[b + 1] - p->seq_offsets_h[b];
+      if (Lb < 1) return fail(KVSEL_EINVAL, "every sequence needs at least one key (seq_offsets_h must increase)");
+      P.seq_off[b + 1] = p->seq_offsets_h[b + 1];
+    }
+  } else {
+    if (p->L < 1) return fail(KVSEL_EINVAL, "L must be >= 1");
+    for (int b = 0; b < P.B; ++b) P.seq_off[b + 1] = P.seq_off[b] + p->L;
+  }
+  for (int b = 0; b < P.B; ++b) {
+    const int64_t Lb = P.seq_off[b + 1] - P.seq_off[b];
+    if (Lb > (int64_t)INT32_MAX / 2) return fail(KVSEL_EUNSUPPORTED, "sequence longer than 2^30 keys");
+    if (p->w > Lb) return fail(KVSEL_EINVAL, "w must not exceed any sequence length");
+    P.Lmax = std::max(P.Lmax, Lb);
+  }
+  P.keff.assign((size_t)P.B * P.Hkv, 0);
+  P.out_off.assign((size_t)P.B * P.Hkv + 1, 0);
+  for (int b = 0; b < P.B; ++b) {
+    const int64_t Lb = P.seq_off[b + 1] - P.seq_off[b];
+    for (int h = 0; h < P.Hkv; ++h) {
+      const int64_t kb = p->budgets_h ? p->budgets_h[(size_t)b * P.Hkv + h] : p->k;
+      if (kb < 0) return fail(KVSEL_EINVAL, "budgets must be >= 0");
+      const int s = b * P.Hkv + h;
+      P.keff[s] = (int32_t)std::min<int64_t>(kb, Lb);
+      P.out_off[s + 1] = P.out_off[s] + P.keff[s];
+    }
+  }
+  if (p->d != kHeadDim) return fail(KVSEL_EUNSUPPORTED, "this build supports d = 128 only");
+  if (P.Hkv > kMaxSeg) return fail(KVSEL_EUNSUPPORTED, "at most 64 KV heads");
+  P.R = P.G * P.wp;
+  if (P.R > kMaxRows) return fail(KVSEL_EUNSUPPORTED, "at most 512 observation rows (Hq/Hkv * w') per KV head");
+
+  P.has_decode = p->has_decode;
+  P.causal = p->causal;
+  P.alpha = p->alpha;
+  P.pool = p->pool;
+  P.pool_kernel = (p->pool == KVSEL_POOL_NONE) ? 1 : p->pool_kernel;
+  const float scale = (p->scale == 0.0f) ? 1.0f / std::sqrt((float)p->d) : p->scale;
+  P.cl2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+
+  P.nrt = (P.R + kTile - 1) / kTile;
+  P.nrg = (P.nrt + kRowTilesPerWave - 1) / kRowTilesPerWave;
+  P.Rpad = P.nrg * kRowTilesPerWave * kTile;
+  P.ks = std::max(1, 4 / P.nrg);
+  const int64_t head_keys = P.seq_off[P.B] * P.Hkv;
+  const int waves = P.nrg * P.ks;
+  P.kb1 = p->key_chunk > 0 ? p->key_chunk : auto_key_block(head_keys, waves, P.ks, 4096);
+  P.kb2 = auto_key_block(head_keys, waves, P.ks, std::min(4096, 16384 / P.nrg));
+  P.nblk1_max = (int)((P.Lmax + P.kb1 - 1) / P.kb1);
+  P.nblk2_max = (int)((P.Lmax + P.kb2 - 1) / P.kb2);
+
+  const size_t nseg = (size_t)P.B * P.Hkv;
+  size_t off = 0;
+  P.off_tickets = off;
+  off = align_up(off + nseg * sizeof(unsigned long long), 256);
+  P.off_partials = off;
+  off = align_up(off + nseg * P.nblk1_max * P.Rpad * sizeof(float2), 256);
+  P.off_bias = off;
+  off = align_up(off + nseg * P.Rpad * sizeof(float), 256);
+  P.off_scores = off;
+  off = align_up(off + (size_t)head_keys * sizeof(float), 256);
+  P.off_pooled = off;
+  off = align_up(off + (size_t)head_keys * sizeof(float), 256);
+  P.ws_bytes = off;
+  return KVSEL_OK;
+}
+
+std::atomic<uint32_t> g_epoch{0};
+std::atomic<int> g_device_ok[256];
+
+uint32_t next_epoch() {
+  static bool seeded = [] {
+    const uint64_t t = (uint64_t)std::chrono::high_resolution_clock::now().time_since_epoch().count();
+    g_epoch.store((uint32_t)(t ^ (t >> 32) ^ ((uint64_t)getpid() << 16)));
+    return true;
+  }();
+  (void)seeded;
+  uint32_t e;
+  do {
+    e = g_epoch.fetch_add(1) + 1;
+  } while (e == 0);
+  return e;
+}
+
+kvsel_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVSEL_EHIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= 256) return fail(KVSEL_EUNSUPPORTED, "device ordinal out of range");
+  int st = g_device_ok[dev].load();
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(KVSEL_EHIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_ok[dev].store(st);
+  }
+  if (st != 1) return fail(KVSEL_EUNSUPPORTED, "kernels are built for gfx950 (MI355X) only");
+  return KVSEL_OK;
+}
+
+kvsel_status check_ptr(const void *ptr, const char *name) {
+  if (!ptr) return fail(KVSEL_EINVAL, std::string(name) + " is NULL");
+  if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return fail(KVSEL_EINVAL, std::string(name) + " is not 16-byte aligned");
+  return KVSEL_OK;
+}
+
+kvsel_status check_ws(const Plan &P, const void *ws, size_t ws_bytes) {
+  kvsel_status s = check_ptr(ws, "workspace");
+  if (s != KVSEL_OK) return s;
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(KVSEL_EINVAL, "workspace is not 256-byte aligned");
+  if (ws_bytes < P.ws_bytes)
+    return fail(KVSEL_EINVAL, "workspace too small: need " + std::to_string(P.ws_bytes) + " bytes");
+  return KVSEL_OK;
+}
+
+kvsel_status hip_fail(hipError_t e, const char *what) {
+  return fail(KVSEL_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Sequence groups whose segments fit one launch's table.
+template <typename F>
+kvsel_status for_each_group(const Plan &P, F &&f) {
+  const int per = std::max(1, kMaxSeg / P.Hkv);
+  for (int s0 = 0; s0 < P.B; s0 += per) {
+    SegTable t;
+    std::memset(&t, 0, sizeof(t));
+    t.nseq = std::min(per, P.B - s0);
+    t.seq0 = s0;
+    t.seg0 = s0 * P.Hkv;
+    int64_t lmax = 0;
+    for (int i = 0; i <= t.nseq; ++i) t.key_off[i] = P.seq_off[s0 + i];
+    for (int i = 0; i < t.nseq; ++i) lmax = std::max(lmax, t.key_off[i + 1] - t.key_off[i]);
+    t.kmax = 0;
+    for (int i = 0; i < t.nseq * P.Hkv; ++i) {
+      t.keff[i] = P.keff[t.seg0 + i];
+      t.out_off[i] = P.out_off[t.seg0 + i];
+      t.kmax = std::max(t.kmax, t.keff[i]);
+    }
+    kvsel_status s = f(t, lmax);
+    if (s != KVSEL_OK) return s;
+  }
+  return KVSEL_OK;
+}
+
+ScoreParams score_params(const Plan &P, const void *Q, const void *K, float *scores, char *ws) {
+  ScoreParams sp;
+  std::memset(&sp, 0, sizeof(sp));
+  sp.Q = static_cast<const uint16_t *>(Q);
+  sp.K = static_cast<const uint16_t *>(K);
+  sp.scores = scores;
+  sp.partials = reinterpret_cast<float2 *>(ws + P.off_partials);
+  sp.bias = reinterpret_cast<float *>(ws + P.off_bias);
+  sp.tickets = reinterpret_cast<unsigned long long *>(ws + P.off_tickets);
+  sp.Hq = P.Hq;
+  sp.Hkv = P.Hkv;
+  sp.G = P.G;
+  sp.w = P.w;
+  sp.wp = P.wp;
+  sp.R = P.R;
+  sp.Rpad = P.Rpad;
+  sp.nrt = P.nrt;
+  sp.has_decode = P.has_decode;
+  sp.causal = P.causal;
+  sp.cl2 = P.cl2;
+  sp.alpha = P.alpha;
+  sp.nblk1_max = P.nblk1_max;
+  sp.nrg = P.nrg;
+  sp.ks = P.ks;
+  return sp;
+}
+
+kvsel_status run_score(const Plan &P, const void *Q, const void *K, float *scores, char *ws, hipStream_t st) {
+  ScoreParams sp = score_params(P, Q, K, scores, ws);
+  return for_each_group(P, [&](const SegTable &t, int64_t lmax) {
+    sp.key_block = P.kb1;
+    sp.epoch = next_epoch();
+    hipError_t e = launch_score_pass1(sp, t, (int)((lmax + P.kb1 - 1) / P.kb1), st);
+    if (e != hipSuccess) return hip_fail(e, "score pass 1 launch");
+    sp.key_block = P.kb2;
+    e = launch_score_pass2(sp, t, (int)((lmax + P.kb2 - 1) / P.kb2), st);
+    if (e != hipSuccess) return hip_fail(e, "score pass 2 launch");
+    return KVSEL_OK;
+  });
+}
+
+kvsel_status run_select(const Plan &P, const float *scores, float *pooled, int32_t *idx, hipStream_t st) {
+  SelectParams sp;
+  sp.scores = scores;
+  sp.pooled = pooled;
+  sp.idx = idx;
+  sp.Hkv = P.Hkv;
+  sp.pool = P.pool;
+  sp.pool_kernel = P.pool_kernel;
+  return for_each_group(P, [&](const SegTable &t, int64_t) {
+    hipError_t e = launch_pool_topk(sp, t, st);
+    if (e != hipSuccess) return hip_fail(e, "pool/top-k launch");
+    return KVSEL_OK;
+  });
+}
+
+kvsel_status run_gather(const Plan &P, const int32_t *idx, const void *K, const void *V, void *Ko, void *Vo,
+                        hipStream_t st) {
+  GatherParams gp;
+  gp.idx = idx;
+  gp.K = static_cast<const uint4 *>(K);
+  gp.V = static_cast<const uint4 *>(V);
+  gp.K_out = static_cast<uint4 *>(Ko);
+  gp.V_out = static_cast<uint4 *>(Vo);
+  gp.Hkv = P.Hkv;
+  return for_each_group(P, [&](const SegTable &t, int64_t) {
+    hipError_t e = launch_gather(gp, t, st);
+    if (e != hipSuccess) return hip_fail(e, "gather launch");
+    return KVSEL_OK;
+  });
+}
+
+bool any_kept(const Plan &P) { return P.out_off.back() > 0; }
+
+}  // namespace
+
+KVSEL_API int kvsel_abi_version(void) { return KVSEL_ABI_VERSION; }
+
+KVSEL_API const char *kvsel_status_string(kvsel_status s) {
+  switch (s) {
+    case KVSEL_OK: return "ok";
+    case KVSEL_EINVAL: return "invalid argument";
+    case KVSEL_EUNSUPPORTED: return "unsupported";
+    case KVSEL_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+KVSEL_API const char *kvsel_last_error(void) { return g_last_error.c_str(); }
+
+KVSEL_API kvsel_status kvsel_plan(const kvsel_problem *p, size_t *workspace_bytes, int64_t *out_offsets_h) {
+  g_last_error.clear();
+  if (!workspace_bytes) return fail(KVSEL_EINVAL, "workspace_bytes is NULL");
+  Plan P;
+  kvsel_status s = make_plan(p, P);
+  if (s != KVSEL_OK) return s;
+  *workspace_bytes = P.ws_bytes;
+  if (out_offsets_h) std::memcpy(out_offsets_h, P.out_off.data(), P.out_off.size() * sizeof(int64_t));
+  return KVSEL_OK;
+}
+
+KVSEL_API kvsel_status kvsel_score(const kvsel_problem *p, const void *Q, const void *K, float *scores, void *ws,
+                                   size_t ws_bytes, kvsel_stream_t stream) {
+  g_last_error.clear();
+  Plan P;
+  kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = check_ptr(Q, "Q");
+  if (s == KVSEL_OK) s = check_ptr(K, "K");
+  if (s == KVSEL_OK) s = check_ptr(scores, "scores");
+  if (s == KVSEL_OK) s = check_ws(P, ws, ws_bytes);
+  if (s == KVSEL_OK) s = check_device();
+  if (s != KVSEL_OK) return s;
+  return run_score(P, Q, K, scores, static_cast<char *>(ws), reinterpret_cast<hipStream_t>(stream));
+}
+
+KVSEL_API kvsel_status kvsel_pool_topk(const kvsel_problem *p, const float *scores, float *pooled, int32_t *idx,
+                                       void *ws, size_t ws_bytes, kvsel_stream_t stream) {
+  g_last_error.clear();
+  Plan P;
+  kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = check_ptr(scores, "scores");
+  if (s == KVSEL_OK && pooled) s = check_ptr(pooled, "pooled");
+  if (s == KVSEL_OK && any_kept(P)) s = check_ptr(idx, "idx");
+  if (s == KVSEL_OK) s = check_ws(P, ws, ws_bytes);
+  if (s == KVSEL_OK) s = check_device();
+  if (s != KVSEL_OK) return s;
+  float *pool_buf = pooled ? pooled : reinterpret_cast<float *>(static_cast<char *>(ws) + P.off_pooled);
+  return run_select(P, scores, pool_buf, idx, reinterpret_cast<hipStream_t>(stream));
+}
+
+KVSEL_API kvsel_status kvsel_gather(const kvsel_problem *p, const int32_t *idx, const void *K, const void *V,
+                                    void *K_out, void *V_out, kvsel_stream_t stream) {
+  g_last_error.clear();
+  Plan P;
+  kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = check_ptr(K, "K");
+  if (s == KVSEL_OK) s = check_ptr(V, "V");
+  if (s == KVSEL_OK && any_kept(P)) s = check_ptr(idx, "idx");
+  if (s == KVSEL_OK && any_kept(P)) s = check_ptr(K_out, "K_out");
+  if (s == KVSEL_OK && any_kept(P)) s = check_ptr(V_out, "V_out");
+  if (s == KVSEL_OK) s = check_device();
+  if (s != KVSEL_OK) return s;
+  if (!any_kept(P)) return KVSEL_OK;
+  return run_gather(P, idx, K, V, K_out, V_out, reinterpret_cast<hipStream_t>(stream));
+}
+
+KVSEL_API kvsel_status kvsel_compress(const kvsel_problem *p, const void *Q, const void *K, const void *V,
+                                      int32_t *idx, void *K_out, void *V_out, float *pooled, void *ws,
+                                      size_t ws_bytes, kvsel_stream_t stream) {
+  g_last_error.clear();
+  Plan P;
+  kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = check_ptr(Q, "Q");
+  if (s == KVSEL_OK) s = check_ptr(K, "K");
+  if (s == KVSEL_OK) s = check_ptr(V, "V");
+  if (s == KVSEL_OK && any_kept(P)) s = check_ptr(idx, "idx");
+  if (s == KVSEL_OK && any_kept(P)) s = check_ptr(K_out, "K_out");
+  if (s == KVSEL_OK && any_kept(P)) s = check_ptr(V_out, "V_out");
+  if (s == KVSEL_OK && pooled) s = check_ptr(pooled, "pooled");
+  if (s == KVSEL_OK) s = check_ws(P, ws, ws_bytes);
+  if (s == KVSEL_OK) s = check_device();
+  if (s != KVSEL_OK) return s;
+  char *wsb = static_cast<char *>(ws);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float *scores = reinterpret_cast<float *>(wsb + P.off_scores);
+  float *pool_buf = pooled ? pooled : reinterpret_cast<float *>(wsb + P.off_pooled);
+  s = run_score(P, Q, K, scores, wsb, st);
+  if (s == KVSEL_OK) s = run_select(P, scores, pool_buf, idx, st);
+  if (s == KVSEL_OK && any_kept(P)) s = run_gather(P, idx, K, V, K_out, V_out, st);
+  return s;
+}

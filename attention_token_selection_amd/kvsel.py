@@ -1,0 +1,309 @@
+"""Thin ctypes binding of libkvsel (include/kvsel.h).
+
+The functions here only marshal arguments: they check that torch tensors
+have the device, dtype, contiguity and size the problem implies (so a
+mis-sized buffer is rejected on the host instead of faulting on the GPU),
+take their data pointers and the current HIP stream, and call the C entry
+point of the same name.  Every step of the computation runs in libkvsel's
+kernels.  There is no fallback: if the library is missing, importing this
+module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvsel.so")
+HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kvsel.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m attention_token_selection_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+KVSEL_OK, KVSEL_EINVAL, KVSEL_EUNSUPPORTED, KVSEL_EHIP = 0, 1, 2, 3
+POOLS = {"none": 0, "avg": 1, "max": 2}
+
+
+class KvselProblem(ctypes.Structure):
+    """Mirror of ``struct kvsel_problem``."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("Hq", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("L", ctypes.c_int64),
+        ("seq_offsets_h", ctypes.POINTER(ctypes.c_int64)),
+        ("w", ctypes.c_int32),
+        ("has_decode", ctypes.c_int32),
+        ("alpha", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("pool", ctypes.c_int32),
+        ("pool_kernel", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+        ("budgets_h", ctypes.POINTER(ctypes.c_int32)),
+        ("key_chunk", ctypes.c_int32),
+    ]
+
+
+_P = ctypes.POINTER(KvselProblem)
+_vp = ctypes.c_void_p
+_lib.kvsel_abi_version.restype = ctypes.c_int
+_lib.kvsel_status_string.restype = ctypes.c_char_p
+_lib.kvsel_status_string.argtypes = [ctypes.c_int]
+_lib.kvsel_last_error.restype = ctypes.c_char_p
+_lib.kvsel_plan.restype = ctypes.c_int
+_lib.kvsel_plan.argtypes = [_P, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_int64)]
+_lib.kvsel_score.restype = ctypes.c_int
+_lib.kvsel_score.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.kvsel_pool_topk.restype = ctypes.c_int
+_lib.kvsel_pool_topk.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.kvsel_gather.restype = ctypes.c_int
+_lib.kvsel_gather.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.kvsel_compress.restype = ctypes.c_int
+_lib.kvsel_compress.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+
+
+class KvselError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        detail = _lib.kvsel_last_error().decode()
+        name = _lib.kvsel_status_string(status).decode()
+        super().__init__(f"{where}: {name} ({status}): {detail}")
+
+
+def _check(status: int, where: str):
+    if status != KVSEL_OK:
+        raise KvselError(status, where)
+
+
+def exported_functions() -> list:
+    """Names of the functions include/kvsel.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(kvsel_[a-z_]+)\s*\(", text)))
+
+
+def abi_version() -> int:
+    return _lib.kvsel_abi_version()
+
+
+class Problem:
+    """A kvsel_problem plus the host arrays it points to.
+
+    ``seq_lens`` (list of prefix lengths) or ``L`` with ``batch``; a uniform
+    ``k`` or ``budgets`` [B][Hkv]; ``pool`` is "none", "avg" or "max".
+    """
+
+    def __init__(self, *, Hq: int, Hkv: int, w: int, d: int = 128, seq_lens: Optional[Sequence[int]] = None,
+                 L: int = 0, batch: int = 1, has_decode: bool = False, alpha: float = 0.0, causal: bool = True,
+                 scale: float = 0.0, pool: str = "none", pool_kernel: int = 1, k: int = 0,
+                 budgets=None, key_chunk: int = 0):
+        if seq_lens is None:
+            seq_lens = [int(L)] * int(batch)
+        self.seq_lens = [int(x) for x in seq_lens]
+        self.Hq, self.Hkv, self.d, self.w = int(Hq), int(Hkv), int(d), int(w)
+        self.has_decode = bool(has_decode)
+        self.budgets = None if budgets is None else [[int(x) for x in row] for row in budgets]
+        self.k = int(k)
+        offs = [0]
+        for x in self.seq_lens:
+            offs.append(offs[-1] + x)
+        self._offs = (ctypes.c_int64 * len(offs))(*offs)
+        self._budgets = None
+        if self.budgets is not None:
+            flat = [x for row in self.budgets for x in row]
+            self._budgets = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+        s = KvselProblem()
+        s.batch = len(self.seq_lens)
+        s.Hq, s.Hkv, s.d = self.Hq, self.Hkv, self.d
+        s.L = self.seq_lens[0] if self.seq_lens else 0
+        s.seq_offsets_h = ctypes.cast(self._offs, ctypes.POINTER(ctypes.c_int64))
+        s.w = self.w
+        s.has_decode = int(self.has_decode)
+        s.alpha = float(alpha)
+        s.causal = int(bool(causal))
+        s.scale = float(scale)
+        s.pool = POOLS[pool] if isinstance(pool, str) else int(pool)
+        s.pool_kernel = int(pool_kernel)
+        s.k = self.k
+        s.budgets_h = ctypes.cast(self._budgets, ctypes.POINTER(ctypes.c_int32)) if self._budgets else None
+        s.key_chunk = int(key_chunk)
+        self.struct = s
+
+    @property
+    def batch(self) -> int:
+        return len(self.seq_lens)
+
+    @property
+    def rows(self) -> int:
+        return self.w + int(self.has_decode)
+
+    @property
+    def total_keys(self) -> int:
+        return sum(self.seq_lens)
+
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def kvsel_plan(problem: Problem):
+    """(workspace bytes, out_offsets list of B*Hkv+1 ints)."""
+    ws = ctypes.c_size_t(0)
+    n = problem.batch * problem.Hkv + 1
+    offs = (ctypes.c_int64 * n)()
+    _check(_lib.kvsel_plan(problem.ref(), ctypes.byref(ws), offs), "kvsel_plan")
+    return int(ws.value), list(offs)
+
+
+# ---------------------------------------------------------------- torch marshalling
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t, name, dtype, numel, device=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _sizes(p: Problem):
+    ws, offs = kvsel_plan(p)
+    return {
+        "Q": p.batch * p.rows * p.Hq * p.d,
+        "K": p.total_keys * p.Hkv * p.d,
+        "scores": p.total_keys * p.Hkv,
+        "kept": offs[-1],
+        "ws": ws,
+        "offs": offs,
+    }
+
+
+def kvsel_score(problem: Problem, Q, K, scores, ws, stream=None):
+    torch = _torch()
+    n = _sizes(problem)
+    dev = K.device
+    args = (_ptr(Q, "Q", torch.bfloat16, n["Q"], dev), _ptr(K, "K", torch.bfloat16, n["K"], dev),
+            _ptr(scores, "scores", torch.float32, n["scores"], dev), _ptr(ws, "ws", torch.uint8, n["ws"], dev))
+    with torch.cuda.device(dev):
+        _check(_lib.kvsel_score(problem.ref(), *args, ctypes.c_size_t(ws.numel()), _stream(stream, dev)), "kvsel_score")
+
+
+def kvsel_pool_topk(problem: Problem, scores, pooled, idx, ws, stream=None):
+    torch = _torch()
+    n = _sizes(problem)
+    dev = scores.device
+    args = (_ptr(scores, "scores", torch.float32, n["scores"], dev),
+            _ptr(pooled, "pooled", torch.float32, n["scores"], dev),
+            _ptr(idx, "idx", torch.int32, n["kept"], dev) if n["kept"] else (idx.data_ptr() if idx is not None else None),
+            _ptr(ws, "ws", torch.uint8, n["ws"], dev))
+    with torch.cuda.device(dev):
+        _check(_lib.kvsel_pool_topk(problem.ref(), *args, ctypes.c_size_t(ws.numel()), _stream(stream, dev)),
+               "kvsel_pool_topk")
+
+
+def kvsel_gather(problem: Problem, idx, K, V, K_out, V_out, stream=None):
+    torch = _torch()
+    n = _sizes(problem)
+    dev = K.device
+    kept = n["kept"]
+    args = (_ptr(idx, "idx", torch.int32, kept, dev) if kept else None,
+            _ptr(K, "K", torch.bfloat16, n["K"], dev), _ptr(V, "V", torch.bfloat16, n["K"], dev),
+            _ptr(K_out, "K_out", torch.bfloat16, kept * problem.d, dev) if kept else None,
+            _ptr(V_out, "V_out", torch.bfloat16, kept * problem.d, dev) if kept else None)
+    with torch.cuda.device(dev):
+        _check(_lib.kvsel_gather(problem.ref(), *args, _stream(stream, dev)), "kvsel_gather")
+
+
+def kvsel_compress(problem: Problem, Q, K, V, idx, K_out, V_out, pooled, ws, stream=None):
+    torch = _torch()
+    n = _sizes(problem)
+    dev = K.device
+    kept = n["kept"]
+    args = (_ptr(Q, "Q", torch.bfloat16, n["Q"], dev), _ptr(K, "K", torch.bfloat16, n["K"], dev),
+            _ptr(V, "V", torch.bfloat16, n["K"], dev),
+            _ptr(idx, "idx", torch.int32, kept, dev) if kept else None,
+            _ptr(K_out, "K_out", torch.bfloat16, kept * problem.d, dev) if kept else None,
+            _ptr(V_out, "V_out", torch.bfloat16, kept * problem.d, dev) if kept else None,
+            _ptr(pooled, "pooled", torch.float32, n["scores"], dev),
+            _ptr(ws, "ws", torch.uint8, n["ws"], dev))
+    with torch.cuda.device(dev):
+        _check(_lib.kvsel_compress(problem.ref(), *args, ctypes.c_size_t(ws.numel()), _stream(stream, dev)),
+               "kvsel_compress")
+
+
+def alloc_outputs(problem: Problem, device, pooled: bool = True):
+    """Output tensors and workspace for kvsel_compress (torch.empty; the
+    workspace needs no initialisation)."""
+    torch = _torch()
+    n = _sizes(problem)
+    kept = n["kept"]
+    return {
+        "idx": torch.empty(max(kept, 1), dtype=torch.int32, device=device),
+        "K_out": torch.empty(max(kept, 1), problem.d, dtype=torch.bfloat16, device=device),
+        "V_out": torch.empty(max(kept, 1), problem.d, dtype=torch.bfloat16, device=device),
+        "pooled": torch.empty(max(n["scores"], 1), dtype=torch.float32, device=device) if pooled else None,
+        "ws": torch.empty(n["ws"], dtype=torch.uint8, device=device),
+        "out_offsets": n["offs"],
+    }
+
+
+def compress(problem: Problem, Q, K, V, pooled: bool = True, stream=None):
+    """Allocate outputs, run kvsel_compress, return them in a dict."""
+    out = alloc_outputs(problem, K.device, pooled=pooled)
+    kvsel_compress(problem, Q, K, V, out["idx"], out["K_out"], out["V_out"], out["pooled"], out["ws"], stream)
+    return out
+
+
+def bind_compress(problem: Problem, Q, K, V, idx, K_out, V_out, pooled, ws, stream=None):
+    """Check the arguments once and return a callable that only re-issues the
+    kvsel_compress C call with the same pointers (for tight loops and graph
+    capture, where per-call Python checks would dominate)."""
+    torch = _torch()
+    n = _sizes(problem)
+    dev = K.device
+    kept = n["kept"]
+    args = (problem.ref(), _ptr(Q, "Q", torch.bfloat16, n["Q"], dev), _ptr(K, "K", torch.bfloat16, n["K"], dev),
+            _ptr(V, "V", torch.bfloat16, n["K"], dev),
+            _ptr(idx, "idx", torch.int32, kept, dev) if kept else None,
+            _ptr(K_out, "K_out", torch.bfloat16, kept * problem.d, dev) if kept else None,
+            _ptr(V_out, "V_out", torch.bfloat16, kept * problem.d, dev) if kept else None,
+            _ptr(pooled, "pooled", torch.float32, n["scores"], dev),
+            _ptr(ws, "ws", torch.uint8, n["ws"], dev), ctypes.c_size_t(ws.numel()), _stream(stream, dev))
+    fn = _lib.kvsel_compress
+    keep = (problem, Q, K, V, idx, K_out, V_out, pooled, ws, stream)
+
+    def call():
+        _ = keep  # the tensors must outlive the bound call
+        st = fn(*args)
+        if st != KVSEL_OK:
+            raise KvselError(st, "kvsel_compress")
+
+    return call

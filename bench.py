@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Throughput of attention-score-based KV-cache selection on one MI355X.
+
+Workload: Llama-3.1-8B-shaped prefill compression, all 32 layers one after
+another, batch 1, L = 32768 prefix tokens, Hq = 32, Hkv = 8, d = 128, bf16,
+observation window w = 32, max pool 7, budget k = 2048 per KV head; keys
+N(0,1)/sqrt(d) with 1% planted positions in runs of 1-16 tokens (seeded
+synthetic inputs, generated on the GPU before timing).
+
+A step is one kvsel_compress per layer (scores -> pool -> top-k -> gather)
+for all 32 layers, with every input resident in HBM.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "prefix tokens scored+compressed/sec (all heads, 1 GPU); % of HBM peak"
+
+
+def algorithmic_bytes(spec, kept_rows: int):
+    """Bytes the path must move at least once per layer: K read once, Q read,
+    the kept K and V rows read and written, and the kept indices written."""
+    d = spec.d
+    keys = sum(spec.seq_lens)
+    k_bytes = keys * spec.Hkv * d * 2
+    q_bytes = spec.batch * spec.rows * spec.Hq * d * 2
+    gather = kept_rows * d * 2 * 2 * 2
+    idx = kept_rows * 4
+    return {"K": k_bytes, "Q": q_bytes, "scores_out": keys * spec.Hkv * 4,
+            "path": k_bytes + q_bytes + gather + idx}
+
+
+def cpu_baseline(spec, cases, layers):
+    """The fp64 oracle, untuned, on the host cores, over `layers` layers."""
+    import numpy as np
+
+    import oracle.kvsel_oracle as O
+    import workloads as W
+
+    try:
+        import threadpoolctl
+
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        threads = os.cpu_count() or 1
+    total = 0.0
+    tokens = 0
+    for layer in range(layers):
+        c = cases[layer]
+        Q = c["Q"].to("cpu").double().numpy()
+        K = c["K"].to("cpu").double().numpy()
+        V = c["V"].to("cpu").double().numpy()
+        t0 = time.perf_counter()
+        O.compress(Q, K, V, **W.oracle_kwargs(spec))
+        total += time.perf_counter() - t0
+        tokens += sum(spec.seq_lens)
+        del Q, K, V
+    return {"value": tokens / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"layers 0-{layers - 1} of {spec.layers} (all {spec.Hkv} KV heads, L={spec.seq_lens[0]}), "
+                      f"{total:.1f} s of numpy fp64 on the host"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--graph", type=int, default=1, help="replay each step from a captured HIP graph")
+    ap.add_argument("--cpu-layers", type=int, default=2, help="layers the CPU oracle baseline covers (0: skip)")
+    ap.add_argument("--stage-reps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this library runs on one GPU; multi-GPU runs are not part of it "
+              "(each GPU would take whole (sequence, KV head) segments independently).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_token_selection_amd as kv
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = W.config(2)
+    L = spec.seq_lens[0]
+    print(f"[bench] generating {spec.layers} layers of {spec.name} on {dev}", file=sys.stderr, flush=True)
+    cases = [W.make_case(spec, layer=l, device=dev) for l in range(spec.layers)]
+    p = kv.Problem(**W.problem_kwargs(spec))
+    ws_bytes, offs = kv.kvsel_plan(p)
+    kept = offs[-1]
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    outs = [kv.alloc_outputs(p, dev, pooled=False) for _ in range(spec.layers)]
+    for o in outs:
+        o["ws"] = ws  # one workspace: the layers run one after another on one stream
+
+    stream = torch.cuda.Stream(device=dev)
+    calls = [kv.bind_compress(p, c["Q"], c["K"], c["V"], o["idx"], o["K_out"], o["V_out"], None, ws, stream)
+             for c, o in zip(cases, outs)]
+
+    def step():
+        for call in calls:
+            call()
+
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+    else:
+        run = step
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            run()
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            run()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    wall = t1 - t0
+    gpu_s = ev0.elapsed_time(ev1) / 1e3
+    elapsed = max(wall, gpu_s)
+    tokens_per_step = L * spec.layers * spec.batch
+    value = tokens_per_step * args.steps / elapsed
+    ms_per_step = elapsed / args.steps * 1e3
+
+    ab = algorithmic_bytes(spec, kept)
+    path_gbs = ab["path"] * spec.layers * args.steps / elapsed / 1e9
+
+    # Dominant stage: the two-pass score (pass 1 + pass 2), timed with HIP
+    # events on the library's stream; then pool/top-k and gather for context.
+    scores = torch.empty(sum(spec.seq_lens) * spec.Hkv, dtype=torch.float32, device=dev)
+    stage = {}
+    for name in ("score", "pool_topk", "gather"):
+        evs = []
+        with torch.cuda.stream(stream):
+            for _ in range(args.stage_reps):
+                for c, o in zip(cases, outs):
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    if name == "score":
+                        kv.kvsel_score(p, c["Q"], c["K"], scores, ws, stream)
+                    elif name == "pool_topk":
+                        kv.kvsel_pool_topk(p, scores, None, o["idx"], ws, stream)
+                    else:
+                        kv.kvsel_gather(p, o["idx"], c["K"], c["V"], o["K_out"], o["V_out"], stream)
+                    b.record(stream)
+                    evs.append((a, b))
+        torch.cuda.synchronize()
+        stage[name] = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3  # microseconds
+    score_bytes = ab["K"] + ab["Q"] + ab["scores_out"]
+    achieved = score_bytes / (stage["score"] * 1e-6) / 1e9
+
+    cpu = None
+    if args.cpu_layers > 0:
+        print(f"[bench] cpu oracle baseline over {args.cpu_layers} layers", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(spec, cases, args.cpu_layers)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, generated on the GPU)",
+        "config": {
+            "workload": "llama3.1-8b-shaped prefill KV selection: 32 layers, batch 1, L=32768, Hq=32, Hkv=8, "
+                        "d=128, w=32, max pool 7, k=2048 per KV head",
+            "layers": spec.layers, "batch": spec.batch, "seq_len": L, "graph": bool(args.graph),
+        },
+        "hbm_frac_path": path_gbs / HBM_PEAK_GBS,
+        "path_GBps": path_gbs,
+        "stage_us": stage,
+        "roofline": {
+            "kernel": "score pass 1 + pass 2 (kvsel_score)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

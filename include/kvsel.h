@@ -1,0 +1,168 @@
+/*
+ * kvsel -- attention-score-based KV-cache selection on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of the library libkvsel.so.  All compute runs in hand-written HIP
+ * kernels; every call validates its arguments on the host, then enqueues work
+ * on the caller's stream and returns without synchronising.
+ *
+ * The operation, per sequence b and KV head h:
+ *   1. observation rows: the last w prompt queries (positions L_b-w .. L_b-1),
+ *      optionally followed by one decode-step query at position L_b
+ *      (TideKV, "Delayed KV Eviction via Layer-Wise Chunked Prefill", §4.2,
+ *      observation queries; DeferKV Guide, "Eviction Timing for KV Cache
+ *      Compression", Phase 2, decode-aware observation window);
+ *   2. logits s = scale * <q, k_i> for every prefix key i, causally masked for
+ *      window rows (TideKV §4.2, Eq. (4) and the masking rule beside it);
+ *   3. per-row softmax over the prefix, found with TideKV's two-pass blockwise
+ *      procedure (§4.2): pass 1 streams key blocks keeping a running max and a
+ *      rescaled sum of exponentials per row, pass 2 recomputes the logits;
+ *   4. S[i] = sum over the G = Hq/Hkv query heads of group h and over the rows
+ *      of c_r * p_r[i] (TideKV §4.2, grouped-query aggregation at KV-head
+ *      granularity); c_r = 1 without a decode row, else 1-alpha for prompt
+ *      rows and alpha for the decode row (DeferKV Guide, Phase 2 weighting);
+ *   5. a stride-1 1-D pool of odd width (avg: zero-padded sum / width; max:
+ *      over in-range positions) -- not defined on the pages;
+ *   6. top-k: the min(k_bh, L_b) positions with the largest pooled score,
+ *      lower position first among equal scores, reported ascending (TideKV
+ *      §5 keeps original positions; DeferKV Guide, Phase 3, sorts them);
+ *   7. gather of the kept K and V rows (TideKV §4.2 and §5, compact KV-head
+ *      layout with per-head offsets, §4.1).
+ * Query head g belongs to KV head g / G.
+ *
+ * Layouts (all packed, row-major, no padding):
+ *   Q       bf16 [B][w'][Hq][d], w' = w + has_decode, decode row last.
+ *   K, V    bf16 [sum_b L_b][Hkv][d]; sequence b occupies key rows
+ *           seq_offsets[b] .. seq_offsets[b+1]-1 (token-major).
+ *   scores, pooled
+ *           fp32, segment (b,h) is L_b contiguous floats starting at
+ *           Hkv*seq_offsets[b] + h*L_b.
+ *   idx     int32 positions relative to the start of sequence b, ascending
+ *           within each segment; segment (b,h) starts at out_offsets[b*Hkv+h]
+ *           (from kvsel_plan) and holds min(k_bh, L_b) entries.
+ *   K_out, V_out
+ *           bf16 [sum of kept][d], same segments as idx (head-major within a
+ *           sequence, i.e. the flattened variable-length layout).
+ *
+ * Ownership: the caller allocates and frees every buffer, including the
+ * workspace (size from kvsel_plan).  The library never allocates, frees or
+ * synchronises device memory.  Inputs are read-only.  The workspace needs no
+ * initialisation and may be reused by later calls on the same stream; two
+ * calls that overlap in time must not share a workspace.
+ *
+ * Errors: validation is synchronous and launches nothing when it fails.
+ *   KVSEL_EINVAL       bad argument (see each function);
+ *   KVSEL_EUNSUPPORTED valid but outside what this build implements
+ *                      (d != 128, more than 64 KV heads, more than 512
+ *                      observation rows per KV head, device is not gfx950);
+ *   KVSEL_EHIP         a HIP runtime call or kernel launch failed; the HIP
+ *                      error text is available from kvsel_last_error().
+ * No C++ exception crosses this interface.  NaN or Inf inputs give undefined
+ * (but memory-safe) results.
+ */
+#ifndef KVSEL_H
+#define KVSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVSEL_ABI_VERSION 1
+
+/* Same type as hipStream_t; NULL means the default stream. */
+typedef struct ihipStream_t *kvsel_stream_t;
+
+typedef enum kvsel_status {
+  KVSEL_OK = 0,
+  KVSEL_EINVAL = 1,
+  KVSEL_EUNSUPPORTED = 2,
+  KVSEL_EHIP = 3
+} kvsel_status;
+
+typedef enum kvsel_pool {
+  KVSEL_POOL_NONE = 0,
+  KVSEL_POOL_AVG = 1,
+  KVSEL_POOL_MAX = 2
+} kvsel_pool;
+
+/* Problem description, shared by every entry point.  Host memory. */
+typedef struct kvsel_problem {
+  int32_t batch;                 /* B >= 1 sequences */
+  int32_t Hq;                    /* query heads, multiple of Hkv */
+  int32_t Hkv;                   /* KV heads, 1..64 */
+  int32_t d;                     /* head dim; this build: 128 */
+  int64_t L;                     /* prefix length of every sequence when seq_offsets_h is NULL */
+  const int64_t *seq_offsets_h;  /* host, B+1 increasing offsets into the key axis (first 0), or NULL */
+  int32_t w;                     /* prompt observation rows, 1 <= w <= L_b for every b */
+  int32_t has_decode;            /* 0 or 1: one extra decode-step row at position L_b */
+  float alpha;                   /* decode weight in [0,1]; used only when has_decode */
+  int32_t causal;                /* 1: window row at position p sees keys <= p; 0: all keys */
+  float scale;                   /* logit scale; 0 selects 1/sqrt(d) */
+  int32_t pool;                  /* kvsel_pool */
+  int32_t pool_kernel;           /* odd, >= 1 (ignored for KVSEL_POOL_NONE) */
+  int32_t k;                     /* uniform budget >= 0 when budgets_h is NULL */
+  const int32_t *budgets_h;      /* host, B*Hkv budgets (>= 0, sequence-major), or NULL */
+  int32_t key_chunk;             /* keys per pass-1 statistics block (multiple of 16), 0 = library choice */
+} kvsel_problem;
+
+/* KVSEL_ABI_VERSION of the loaded library. */
+int kvsel_abi_version(void);
+
+/*
+ * Host-only planning.  Validates *p (pointer arguments are not needed) and
+ * returns the workspace size, in bytes, that kvsel_score, kvsel_pool_topk
+ * and kvsel_compress need for this problem (one size serves all three), and,
+ * if out_offsets_h is not NULL, the B*Hkv+1 output segment offsets
+ * (out_offsets_h[0] = 0, last = total kept rows).
+ * Errors: KVSEL_EINVAL for an invalid problem or NULL workspace_bytes.
+ */
+kvsel_status kvsel_plan(const kvsel_problem *p, size_t *workspace_bytes, int64_t *out_offsets_h);
+
+/*
+ * Steps 1-4: aggregated scores S (before pooling) into `scores`.
+ * Q, K: device bf16 inputs; scores: device fp32 output; ws: device workspace
+ * of at least kvsel_plan's size.  All device pointers 16-byte aligned.
+ * Errors: KVSEL_EINVAL (invalid problem, NULL pointer, misalignment,
+ * ws_bytes too small), KVSEL_EUNSUPPORTED, KVSEL_EHIP.
+ */
+kvsel_status kvsel_score(const kvsel_problem *p, const void *Q, const void *K, float *scores,
+                         void *ws, size_t ws_bytes, kvsel_stream_t stream);
+
+/*
+ * Steps 5-6: pool the given scores and select the top-k positions.
+ * scores: device fp32 input (layout above); pooled: device fp32 output or
+ * NULL (then it is kept in the workspace); idx: device int32 output.
+ * Errors as for kvsel_score.
+ */
+kvsel_status kvsel_pool_topk(const kvsel_problem *p, const float *scores, float *pooled, int32_t *idx,
+                             void *ws, size_t ws_bytes, kvsel_stream_t stream);
+
+/*
+ * Step 7: copy the rows named by idx (positions within each sequence) of K
+ * and V into K_out and V_out.  An index outside [0, L_b) yields a zero row.
+ * Needs no workspace.  Errors as for kvsel_score (no workspace checks).
+ */
+kvsel_status kvsel_gather(const kvsel_problem *p, const int32_t *idx, const void *K, const void *V,
+                          void *K_out, void *V_out, kvsel_stream_t stream);
+
+/*
+ * Steps 1-7 in one call: idx, K_out, V_out and (if not NULL) pooled; the
+ * unpooled scores stay in the workspace.
+ */
+kvsel_status kvsel_compress(const kvsel_problem *p, const void *Q, const void *K, const void *V,
+                            int32_t *idx, void *K_out, void *V_out, float *pooled,
+                            void *ws, size_t ws_bytes, kvsel_stream_t stream);
+
+/* Static text for a status code. */
+const char *kvsel_status_string(kvsel_status s);
+
+/* Thread-local detail of the last non-OK status returned on this thread ("" if none). */
+const char *kvsel_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSEL_H */

@@ -1,0 +1,288 @@
+"""HIP path vs the fp64 oracle, through the C ABI, on an MI355X.
+
+Small shapes are checked on every segment; the full-size workloads on
+sampled segments (the oracle computes one (sequence, KV head) at a time)
+plus properties that hold on every segment: exact top-k of the GPU's own
+pooled scores and bit-exact gathered rows.
+"""
+
+import json
+import math
+import zlib
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.kvsel_oracle as O
+import workloads as W
+from parity import check_against_oracle, check_scores, check_select_exact, segments, to_np64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+
+
+@pytest.fixture(scope="module")
+def kv():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    import attention_token_selection_amd as k
+
+    return k
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(kv, spec, case, with_scores=True):
+    p = kv.Problem(**W.problem_kwargs(spec))
+    Q, K, V = (case[x].to(DEV) for x in "QKV")
+    out = kv.compress(p, Q, K, V, pooled=True)
+    scores = None
+    if with_scores:
+        scores = torch.empty(sum(spec.seq_lens) * spec.Hkv, dtype=torch.float32, device=DEV)
+        kv.kvsel_score(p, Q, K, scores, out["ws"])
+    torch.cuda.synchronize()
+    return p, out, scores
+
+
+def _oracle(spec, case, heads=None):
+    return O.compress(to_np64(case["Q"]), to_np64(case["K"]), to_np64(case["V"]), heads=heads,
+                      **W.oracle_kwargs(spec))
+
+
+# ---------------------------------------------------------------- hand-worked examples
+def _hand_examples():
+    with open(GOLDEN) as f:
+        j = json.load(f)
+    return [(j["keys_c0"], ex) for ex in j["examples"]]
+
+
+@pytest.mark.parametrize("keys,ex", _hand_examples(), ids=lambda v: v["name"] if isinstance(v, dict) else "")
+def test_hand_examples(kv, keys, ex):
+    _say(f"hand example {ex['name']}")
+    case = W.hand_case(keys, ex["q_c0"], ex["Hq"], ex["Hkv"])
+    p = kv.Problem(Hq=ex["Hq"], Hkv=ex["Hkv"], w=ex["w"], L=len(keys), has_decode=ex["has_decode"],
+                   alpha=ex["alpha"], causal=ex["causal"], scale=1.0, pool=ex["pool"],
+                   pool_kernel=ex["pool_kernel"], k=ex["k"])
+    out = kv.compress(p, *(case[x].to(DEV) for x in "QKV"))
+    torch.cuda.synchronize()
+    assert out["idx"].cpu().tolist() == ex["expect_idx"]
+    ref = O.compress(to_np64(case["Q"]), to_np64(case["K"]), to_np64(case["V"]), seq_lens=[len(keys)],
+                     Hq=ex["Hq"], Hkv=ex["Hkv"], w=ex["w"], has_decode=ex["has_decode"], alpha=ex["alpha"],
+                     causal=ex["causal"], scale=1.0, pool=ex["pool"], pool_kernel=ex["pool_kernel"], k=ex["k"])
+    st = check_scores(out["pooled"].cpu().numpy(), ref[(0, 0)]["pooled"], rtol=1e-5)
+    assert st["max_rel"] < 1e-5
+
+
+# ---------------------------------------------------------------- small shapes, every segment
+@pytest.mark.parametrize("spec", W.small_cases(), ids=lambda s: s.name)
+def test_small_parity(kv, spec):
+    _say(f"small parity {spec.name} lens={spec.seq_lens[:4]} Hq={spec.Hq} Hkv={spec.Hkv} w={spec.w}")
+    case = W.make_case(spec)
+    _, out, scores = _run(kv, spec, case)
+    ref = _oracle(spec, case)
+    st = check_against_oracle(spec, case, out, ref, scores=scores)
+    assert st["segments"] == spec.batch * spec.Hkv
+    assert st["max_rel"] < 1e-4, st
+
+
+# ---------------------------------------------------------------- full-size workloads
+SAMPLED = {
+    1: [(0, 0), (0, 3), (0, 7)],
+    2: [(0, 0), (0, 7)],
+    3: [(0, 0), (0, 5)],
+    4: [(0, 1), (3, 6)],
+    5: [(0, 0), (4, 3), (7, 7)],
+}
+
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
+def test_config_parity(kv, i):
+    spec = W.config(i)
+    _say(f"config {i} {spec.name}: generating")
+    case = W.make_case(spec, layer=0, device=DEV)
+    _say(f"config {i}: running kvsel_compress")
+    _, out, scores = _run(kv, spec, case)
+    _say(f"config {i}: oracle on {SAMPLED[i]}")
+    case_cpu = {k: v.cpu() for k, v in case.items()}
+    ref = _oracle(spec, case_cpu, heads=SAMPLED[i])
+    st = check_against_oracle(spec, case_cpu, out, ref, heads=SAMPLED[i], scores=scores)
+    _say(f"config {i}: {st}")
+    assert st["segments"] == len(SAMPLED[i])
+
+
+def test_config2_last_layer(kv):
+    spec = W.config(2)
+    case = W.make_case(spec, layer=31, device=DEV)
+    _, out, _ = _run(kv, spec, case, with_scores=False)
+    case_cpu = {k: v.cpu() for k, v in case.items()}
+    ref = _oracle(spec, case_cpu, heads=[(0, 2)])
+    check_against_oracle(spec, case_cpu, out, ref, heads=[(0, 2)])
+
+
+# ---------------------------------------------------------------- entry points compose, determinism
+def test_entry_points_compose_and_repeat(kv):
+    spec = W.small_cases()[7]  # ragged, per-head budgets
+    case = W.make_case(spec)
+    p = kv.Problem(**W.problem_kwargs(spec))
+    Q, K, V = (case[x].to(DEV) for x in "QKV")
+    full = kv.compress(p, Q, K, V)
+    again = kv.compress(p, Q, K, V)
+    ws, offs = kv.kvsel_plan(p)
+    n = sum(spec.seq_lens) * spec.Hkv
+    scores = torch.empty(n, device=DEV)
+    pooled = torch.empty(n, device=DEV)
+    idx = torch.empty(max(1, offs[-1]), dtype=torch.int32, device=DEV)
+    Ko = torch.empty(max(1, offs[-1]), 128, dtype=torch.bfloat16, device=DEV)
+    Vo = torch.empty_like(Ko)
+    wsb = torch.full((ws,), 0xAB, dtype=torch.uint8, device=DEV)  # garbage workspace is fine
+    kv.kvsel_score(p, Q, K, scores, wsb)
+    kv.kvsel_pool_topk(p, scores, pooled, idx, wsb)
+    kv.kvsel_gather(p, idx, K, V, Ko, Vo)
+    torch.cuda.synchronize()
+    kept = offs[-1]
+    assert torch.equal(full["idx"][:kept], idx[:kept])
+    assert torch.equal(again["idx"][:kept], idx[:kept])
+    assert torch.equal(full["pooled"], pooled)
+    assert torch.equal(again["pooled"], pooled)
+    assert torch.equal(full["K_out"][:kept], Ko[:kept])
+    assert torch.equal(full["V_out"][:kept], Vo[:kept])
+
+
+def test_workspace_shared_across_problems(kv):
+    """One workspace serves several different problems in a row."""
+    cases = [W.small_cases()[i] for i in (6, 7, 11, 6)]
+    big = max(kv.kvsel_plan(kv.Problem(**W.problem_kwargs(s)))[0] for s in cases)
+    ws = torch.empty(big, dtype=torch.uint8, device=DEV)
+    for spec in cases:
+        case = W.make_case(spec)
+        p = kv.Problem(**W.problem_kwargs(spec))
+        out = kv.alloc_outputs(p, DEV)
+        kv.kvsel_compress(p, *(case[x].to(DEV) for x in "QKV"), out["idx"], out["K_out"], out["V_out"],
+                          out["pooled"], ws)
+        torch.cuda.synchronize()
+        ref = _oracle(spec, case)
+        check_against_oracle(spec, case, out, ref)
+
+
+# ---------------------------------------------------------------- selection on given scores (exact)
+def _adversarial_scores(kind, L, rng):
+    if kind == "integer":
+        return rng.integers(0, 50, L).astype(np.float32)
+    if kind == "all_equal":
+        return np.full(L, 0.25, dtype=np.float32)
+    if kind == "two_values":
+        return rng.choice(np.array([1.0, 2.0], dtype=np.float32), L)
+    if kind == "sorted":
+        return np.sort(rng.random(L).astype(np.float32))
+    if kind == "reverse":
+        return np.sort(rng.random(L).astype(np.float32))[::-1].copy()
+    if kind == "tiny_and_zero":
+        x = (rng.random(L) < 0.5).astype(np.float32) * np.float32(1e-30)
+        return x
+    return rng.random(L).astype(np.float32) * np.float32(10.0) ** rng.integers(-20, 2, L).astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["integer", "all_equal", "two_values", "sorted", "reverse", "tiny_and_zero", "spread"])
+@pytest.mark.parametrize("pool,kernel", [("none", 1), ("max", 7), ("avg", 5)])
+def test_select_exact_on_given_scores(kv, kind, pool, kernel):
+    rng = np.random.default_rng(zlib.crc32(f"{kind}/{pool}".encode()))
+    lens = [1, 7, 1000, 4099, 70000]
+    Hkv = 2
+    budgets = [[1, 0], [3, 7], [64, 999], [4099, 1500], [2048, 4096]]
+    p = kv.Problem(Hq=2, Hkv=Hkv, w=1, seq_lens=lens, pool=pool, pool_kernel=kernel, budgets=budgets)
+    ws, offs = kv.kvsel_plan(p)
+    S = np.concatenate([_adversarial_scores(kind, L, rng) for L in lens for _ in range(Hkv)])
+    scores = torch.from_numpy(S).to(DEV)
+    pooled = torch.empty_like(scores)
+    idx = torch.empty(offs[-1], dtype=torch.int32, device=DEV)
+    kv.kvsel_pool_topk(p, scores, pooled, idx, torch.empty(ws, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    P = pooled.cpu().numpy()
+    I = idx.cpu().numpy()
+    spec = W.Spec("given", lens, Hq=2, Hkv=Hkv, pool=pool, pool_kernel=kernel, budgets=budgets)
+    for (b, h, L, soff, ooff, keff) in segments(spec, offs):
+        seg = S[soff:soff + L]
+        if pool == "none":
+            np.testing.assert_array_equal(P[soff:soff + L], seg)
+        elif pool == "max":
+            np.testing.assert_array_equal(P[soff:soff + L], O.pool1d(seg.astype(np.float64), "max", kernel))
+        else:
+            check_scores(P[soff:soff + L], O.pool1d(seg.astype(np.float64), "avg", kernel), rtol=1e-6)
+        check_select_exact(I[ooff:ooff + keff], P[soff:soff + L], keff)
+
+
+# ---------------------------------------------------------------- gather on given indices
+def test_gather_given_indices(kv):
+    rng = np.random.default_rng(11)
+    lens = [33, 1000, 5]
+    Hkv = 4
+    budgets = [[5, 33, 0, 1], [100, 7, 999, 1000], [5, 2, 1, 3]]
+    p = kv.Problem(Hq=4, Hkv=Hkv, w=1, seq_lens=lens, budgets=budgets)
+    _, offs = kv.kvsel_plan(p)
+    K = torch.randn(sum(lens), Hkv, 128).to(torch.bfloat16)
+    V = torch.randn(sum(lens), Hkv, 128).to(torch.bfloat16)
+    idx = np.zeros(offs[-1], dtype=np.int32)
+    spec = W.Spec("given", lens, Hq=4, Hkv=Hkv, budgets=budgets)
+    for (b, h, L, soff, ooff, keff) in segments(spec, offs):
+        idx[ooff:ooff + keff] = rng.integers(-3, L + 3, keff)  # includes out-of-range entries
+    Ko = torch.full((offs[-1], 128), 7, dtype=torch.bfloat16, device=DEV)
+    Vo = torch.full_like(Ko, 7)
+    kv.kvsel_gather(p, torch.from_numpy(idx).to(DEV), K.to(DEV), V.to(DEV), Ko, Vo)
+    torch.cuda.synchronize()
+    Ko, Vo = Ko.cpu(), Vo.cpu()
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    for (b, h, L, soff, ooff, keff) in segments(spec, offs):
+        for j in range(keff):
+            pos = int(idx[ooff + j])
+            if 0 <= pos < L:
+                assert torch.equal(Ko[ooff + j], K[starts[b] + pos, h])
+                assert torch.equal(Vo[ooff + j], V[starts[b] + pos, h])
+            else:
+                assert not Ko[ooff + j].any() and not Vo[ooff + j].any()
+
+
+# ---------------------------------------------------------------- graph capture and replay
+def test_graph_replays_match_eager(kv):
+    """Capture kvsel_compress for two layers, replay several times with eager
+    library work and synchronisations in between; every replay must equal the
+    eager result bit for bit."""
+    spec = W.small_cases()[6]
+    p = kv.Problem(**W.problem_kwargs(spec))
+    cases = [{k: v.to(DEV) for k, v in W.make_case(spec, layer=l).items()} for l in range(3)]
+    eager = [kv.compress(p, c["Q"], c["K"], c["V"]) for c in cases[:2]]
+    torch.cuda.synchronize()
+    ws = torch.empty(kv.kvsel_plan(p)[0], dtype=torch.uint8, device=DEV)
+    outs = [kv.alloc_outputs(p, DEV) for _ in range(2)]
+    stream = torch.cuda.Stream(device=DEV)
+    calls = [kv.bind_compress(p, c["Q"], c["K"], c["V"], o["idx"], o["K_out"], o["V_out"], o["pooled"], ws, stream)
+             for c, o in zip(cases, outs)]
+    with torch.cuda.stream(stream):
+        for call in calls:
+            call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for call in calls:
+            call()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:  # poison the outputs
+            o["idx"].fill_(-7)
+            o["K_out"].fill_(3.0)
+            o["pooled"].fill_(-1.0)
+        kv.compress(p, cases[2]["Q"], cases[2]["K"], cases[2]["V"])  # eager work on the same library
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, o in zip(eager, outs):
+            assert torch.equal(e["idx"], o["idx"]), f"replay {rep}: idx"
+            assert torch.equal(e["K_out"], o["K_out"]), f"replay {rep}: K_out"
+            assert torch.equal(e["V_out"], o["V_out"]), f"replay {rep}: V_out"
+            assert torch.equal(e["pooled"], o["pooled"]), f"replay {rep}: pooled"

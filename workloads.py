@@ -230,5 +230,23 @@ def small_cases():
         Spec("s_chunked", [4100], Hq=32, Hkv=8, w=32, pool="avg", pool_kernel=7, k=300, key_chunk=512,
              recipe="zipf"),
         Spec("s_w_big", [300], Hq=32, Hkv=8, w=128, pool="max", pool_kernel=7, k=33, recipe="plant"),
+        Spec("s_many_seqs", [40 + 13 * i for i in range(10)], Hq=16, Hkv=8, w=4, pool="avg", pool_kernel=3,
+             k=9, recipe="plant", plant_frac=0.05),
+        Spec("s_hkv64", [70], Hq=64, Hkv=64, w=3, pool="max", pool_kernel=3, k=10, recipe="plain"),
     ]
     return cases
+
+
+def problem_kwargs(spec: Spec) -> dict:
+    """Keyword arguments describing ``spec`` to the library binding's Problem."""
+    return dict(Hq=spec.Hq, Hkv=spec.Hkv, d=spec.d, w=spec.w, seq_lens=list(spec.seq_lens),
+                has_decode=spec.has_decode, alpha=spec.alpha, causal=spec.causal, scale=spec.scale,
+                pool=spec.pool, pool_kernel=spec.pool_kernel, k=spec.k, budgets=spec.budgets,
+                key_chunk=spec.key_chunk)
+
+
+def oracle_kwargs(spec: Spec) -> dict:
+    """Keyword arguments describing ``spec`` to the oracle's ``compress``."""
+    return dict(seq_lens=list(spec.seq_lens), Hq=spec.Hq, Hkv=spec.Hkv, w=spec.w, has_decode=spec.has_decode,
+                alpha=spec.alpha, causal=spec.causal, scale=(spec.scale if spec.scale else None), pool=spec.pool,
+                pool_kernel=spec.pool_kernel, k=spec.k, budgets=spec.budgets)
