@@ -4,13 +4,11 @@
 #include "kvsel_internal.h"
 
 #include <atomic>
-#include <chrono>
 #include <cmath>
 #include <cstring>
 #include <string>
 #include <vector>
 
-#include <unistd.h>
 
 #define KVSEL_API extern "C" __attribute__((visibility("default")))
 
@@ -29,7 +27,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Everything the launches need, derived from a validated kvsel_problem.
 struct Plan {
-  int B, Hq, Hkv, G, w, wp, R, nrt, nrg, Rpad, ks;
+  int B, Hq, Hkv, G, w, wp, R, nrt, nrg, rt, Rpad, ks;
   int has_decode, causal, pool, pool_kernel;
   float alpha, cl2;
   std::vector<int64_t> seq_off;  // B + 1
@@ -65,6 +63,8 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   if (p->pool < KVSEL_POOL_NONE || p->pool > KVSEL_POOL_MAX) return fail(KVSEL_EINVAL, "unknown pool kind");
   if (p->pool != KVSEL_POOL_NONE && (p->pool_kernel < 1 || p->pool_kernel % 2 == 0))
     return fail(KVSEL_EINVAL, "pool_kernel must be odd and >= 1");
+  if (p->pool != KVSEL_POOL_NONE && p->pool_kernel > kMaxPoolKernel)
+    return fail(KVSEL_EUNSUPPORTED, "pool_kernel wider than 255");
   if (p->key_chunk < 0 || p->key_chunk % kTile != 0) return fail(KVSEL_EINVAL, "key_chunk must be 0 or a positive multiple of 16");
   if (!p->budgets_h && p->k < 0) return fail(KVSEL_EINVAL, "k must be >= 0");
 
@@ -119,7 +119,8 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
 
   P.nrt = (P.R + kTile - 1) / kTile;
   P.nrg = (P.nrt + kRowTilesPerWave - 1) / kRowTilesPerWave;
-  P.Rpad = P.nrg * kRowTilesPerWave * kTile;
+  P.rt = (P.nrt + P.nrg - 1) / P.nrg;  // spread the row tiles evenly over the row groups
+  P.Rpad = P.nrg * P.rt * kTile;
   P.ks = std::max(1, 4 / P.nrg);
   const int64_t head_keys = P.seq_off[P.B] * P.Hkv;
   const int waves = P.nrg * P.ks;
@@ -130,8 +131,8 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
 
   const size_t nseg = (size_t)P.B * P.Hkv;
   size_t off = 0;
-  P.off_tickets = off;
-  off = align_up(off + nseg * sizeof(unsigned long long), 256);
+  P.off_tickets = off;  // fixed: the same bytes for every problem, so tickets stay valid across problems
+  off = align_up(off + kTicketBytes, 256);
   P.off_partials = off;
   off = align_up(off + nseg * P.nblk1_max * P.Rpad * sizeof(float2), 256);
   P.off_bias = off;
@@ -144,22 +145,7 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   return KVSEL_OK;
 }
 
-std::atomic<uint32_t> g_epoch{0};
 std::atomic<int> g_device_ok[256];
-
-uint32_t next_epoch() {
-  static bool seeded = [] {
-    const uint64_t t = (uint64_t)std::chrono::high_resolution_clock::now().time_since_epoch().count();
-    g_epoch.store((uint32_t)(t ^ (t >> 32) ^ ((uint64_t)getpid() << 16)));
-    return true;
-  }();
-  (void)seeded;
-  uint32_t e;
-  do {
-    e = g_epoch.fetch_add(1) + 1;
-  } while (e == 0);
-  return e;
-}
 
 kvsel_status check_device() {
   int dev = 0;
@@ -245,6 +231,7 @@ ScoreParams score_params(const Plan &P, const void *Q, const void *K, float *sco
   sp.alpha = P.alpha;
   sp.nblk1_max = P.nblk1_max;
   sp.nrg = P.nrg;
+  sp.rt = P.rt;
   sp.ks = P.ks;
   return sp;
 }
@@ -253,7 +240,6 @@ kvsel_status run_score(const Plan &P, const void *Q, const void *K, float *score
   ScoreParams sp = score_params(P, Q, K, scores, ws);
   return for_each_group(P, [&](const SegTable &t, int64_t lmax) {
     sp.key_block = P.kb1;
-    sp.epoch = next_epoch();
     hipError_t e = launch_score_pass1(sp, t, (int)((lmax + P.kb1 - 1) / P.kb1), st);
     if (e != hipSuccess) return hip_fail(e, "score pass 1 launch");
     sp.key_block = P.kb2;

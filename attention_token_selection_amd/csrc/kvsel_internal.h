@@ -10,9 +10,11 @@ namespace kvsel {
 constexpr int kHeadDim = 128;        // d supported by this build
 constexpr int kMaxSeg = 64;          // (sequence, KV head) segments handled per launch
 constexpr int kTile = 16;            // keys per MFMA tile and rows per row tile
-constexpr int kRowTilesPerWave = 4;  // row tiles (of 16 rows) held by one wave
+constexpr int kRowTilesPerWave = 4;  // most row tiles (of 16 rows) held by one wave
 constexpr int kMaxRows = 512;        // observation rows per KV head (G * w')
 constexpr int kSelectThreads = 1024; // threads of the per-segment select workgroup
+constexpr int kTicketBytes = kMaxSeg * 8;  // ticket header at the start of every workspace
+constexpr int kMaxPoolKernel = 255;  // widest pool supported
 
 // Per-launch description of the sequences and segments a kernel works on.
 // Travels by value in the kernel arguments, so no device-side tables are
@@ -33,7 +35,7 @@ struct ScoreParams {
   float *scores;                // pass 2 output (layout of the public ABI)
   float2 *partials;             // pass 1 per-block (ref, Z), [nseg][nblk1_max][Rpad]
   float *bias;                  // pass 1 result per row, [nseg][Rpad]
-  unsigned long long *tickets;  // per-segment arrival tickets (epoch << 32 | count)
+  unsigned long long *tickets;  // arrival tickets of the launch's segments (fixed header of the workspace)
   int Hq, Hkv, G, w, wp, R, Rpad, nrt;
   int has_decode, causal;
   float cl2;                    // scale * log2(e)
@@ -41,7 +43,7 @@ struct ScoreParams {
   int key_block;                // keys per workgroup in this pass
   int nblk1_max;                // pass 1 blocks per segment of the longest sequence
   int nrg, ks;                  // row groups and key splits (waves = nrg * ks)
-  uint32_t epoch;               // unique per pass-1 launch (self-resetting tickets)
+  int rt;                       // row tiles per row group (1..4)
 };
 
 struct SelectParams {

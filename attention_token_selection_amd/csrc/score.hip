@@ -35,7 +35,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-constexpr int RT = kRowTilesPerWave;
 constexpr float kLazyThreshold = 16.0f;  // log2 units a logit may exceed its slot reference
 
 __device__ inline bf16x8 load_frag(const uint16_t *p) {
@@ -57,39 +56,56 @@ __device__ inline void lse_merge(float &r, float &z, float r2, float z2) {
   z = a + b;
 }
 
-// Arrival ticket of a (sequence, head): counts this pass-1 launch's blocks
-// without needing a zeroed workspace.  The ticket holds (epoch << 32 | n);
-// a ticket from another launch restarts at 1.  The last arriver resets it to
-// (epoch << 32 | 0) so a replay of the same launch counts from zero again.
-__device__ bool arrive_last(unsigned long long *ticket, uint32_t epoch, uint32_t n) {
-  unsigned long long old = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  unsigned long long want;
-  for (;;) {
-    want = ((uint32_t)(old >> 32) == epoch) ? old + 1ull : (((unsigned long long)epoch << 32) | 1ull);
-    if (__hip_atomic_compare_exchange_strong(ticket, &old, want, __ATOMIC_ACQ_REL, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT))
-      break;
+// Arrival ticket of a (sequence, head) for the last-arriver merge.  A ticket
+// is (kTicketTag << 32 | arrivals so far); the last arriver resets it to
+// (kTicketTag << 32 | 0), so between calls every ticket reads "tag, 0" and an
+// arrival is one fetch-add.  A ticket without the tag (a fresh workspace
+// holding arbitrary bytes) is claimed once with a compare-and-swap; arrivals
+// that raced onto the untagged value are discarded by that swap and redone.
+constexpr uint32_t kTicketTag = 0x6b76736cu;
+
+__device__ bool arrive_last(unsigned long long *ticket, uint32_t n) {
+  const unsigned long long tag = (unsigned long long)kTicketTag << 32;
+  unsigned long long old = __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t count;
+  if ((uint32_t)(old >> 32) == kTicketTag) {
+    count = (uint32_t)old + 1u;
+  } else {
+    unsigned long long cur = old + 1ull;
+    for (;;) {
+      if ((uint32_t)(cur >> 32) == kTicketTag) {
+        old = __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        count = (uint32_t)old + 1u;
+        break;
+      }
+      if (__hip_atomic_compare_exchange_strong(ticket, &cur, tag | 1ull, __ATOMIC_ACQ_REL, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)) {
+        count = 1u;
+        break;
+      }
+    }
   }
-  if ((uint32_t)want == n) {
-    __hip_atomic_store(ticket, (unsigned long long)epoch << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (count == n) {
+    __hip_atomic_store(ticket, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
   }
   return false;
 }
 
-__device__ inline void load_key_tile(bf16x8 (&kf)[4], const ScoreParams &p, int64_t key0, int L, int h,
-                                     int key, int lq) {
-  if (key < L) {
-    const uint16_t *src = p.K + ((key0 + key) * p.Hkv + h) * (int64_t)kHeadDim + lq * 8;
+// Key fragments of this lane's key.  The key index is clamped into the
+// sequence so every load is in bounds and branch-free; keys past the end are
+// masked in the epilogue.
+__device__ inline void load_key_tile(bf16x8 (&kf)[4], const uint16_t *kbase, int64_t key0, int L, int Hkv,
+                                     int key) {
+  const int kk = min(key, L - 1);
+  const uint16_t *src = kbase + (key0 + kk) * Hkv * (int64_t)kHeadDim;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kf[j] = load_frag(src + 32 * j);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kf[j] = zero_frag();
-  }
+  for (int j = 0; j < 4; ++j) kf[j] = load_frag(src + 32 * j);
 }
 
-template <int PASS>
+// RT: row tiles held per wave (the launch spreads the row tiles evenly over
+// the row groups; tiles past the last row hold zero queries).
+template <int PASS, int RT>
 __global__ __launch_bounds__(512) void score_kernel(ScoreParams p, SegTable t) {
   extern __shared__ float lds[];
   __shared__ int s_last;
@@ -105,13 +121,13 @@ __global__ __launch_bounds__(512) void score_kernel(ScoreParams p, SegTable t) {
   const int seg = t.seg0 + sb * p.Hkv + h;
   const int b = t.seq0 + sb;
 
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform indices (scalar registers, scalar branches)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int rg = wave % p.nrg;
   const int ks = wave / p.nrg;
   const int lq = lane >> 4;  // lane group: rows 4*lq.. of a D tile, chunk group of A/B
   const int lc = lane & 15;  // key column of a D tile, row of an A tile
-  const int nvalid = min(RT, p.nrt - rg * RT);
 
   // Query fragments of this wave's row tiles (rows = window row major,
   // query head of the group minor).
@@ -119,7 +135,7 @@ __global__ __launch_bounds__(512) void score_kernel(ScoreParams p, SegTable t) {
 #pragma unroll
   for (int tt = 0; tt < RT; ++tt) {
     const int row = (rg * RT + tt) * kTile + lc;
-    if (tt < nvalid && row < p.R) {
+    if (row < p.R) {
       const int r = row / p.G;
       const int gi = row - r * p.G;
       const uint16_t *src =
@@ -154,23 +170,19 @@ __global__ __launch_bounds__(512) void score_kernel(ScoreParams p, SegTable t) {
   const int ntile = (kb1 - kb0 + kTile - 1) / kTile;
   const int mask_from = p.causal ? (L - p.w) : L;
   const float cl2 = p.cl2;
+  const int step = p.ks;
+  const uint16_t *kbase = p.K + (int64_t)h * kHeadDim + lq * 8;
 
-  bf16x8 kf[4], kn[4];
-  if (ks < ntile) load_key_tile(kf, p, key0, L, h, kb0 + ks * kTile + lc, lq);
-
-  for (int ti = ks; ti < ntile; ti += p.ks) {
+  auto tile = [&](const bf16x8(&kf)[4], int ti) {
     const int i0 = kb0 + ti * kTile;
-    if (ti + p.ks < ntile) load_key_tile(kn, p, key0, L, h, i0 + p.ks * kTile + lc, lq);
-
     f32x4 acc[RT];
 #pragma unroll
-    for (int tt = 0; tt < RT; ++tt) {
-      acc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      if (tt < nvalid) {
+    for (int tt = 0; tt < RT; ++tt) acc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[tt][j], kf[j], acc[tt], 0, 0, 0);
-      }
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int tt = 0; tt < RT; ++tt)
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[tt][j], kf[j], acc[tt], 0, 0, 0);
     }
 
     const bool need_mask = (i0 + kTile) > mask_from;
@@ -186,7 +198,7 @@ __global__ __launch_bounds__(512) void score_kernel(ScoreParams p, SegTable t) {
           float v = fmaf(acc[tt][e], cl2, -ref[tt][e]);
           if (need_mask && key > lim[tt][e]) v = -INFINITY;
           tv[tt][e] = v;
-          if (tt < nvalid) mx = fmaxf(mx, v);
+          mx = fmaxf(mx, v);
         }
       }
       if (__ballot(mx > kLazyThreshold) != 0ull) {
@@ -207,33 +219,34 @@ __global__ __launch_bounds__(512) void score_kernel(ScoreParams p, SegTable t) {
       }
 #pragma unroll
       for (int tt = 0; tt < RT; ++tt) {
-        if (tt < nvalid) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) zs[tt][e] += fast_exp2(tv[tt][e]);
-        }
+        for (int e = 0; e < 4; ++e) zs[tt][e] += fast_exp2(tv[tt][e]);
       }
     } else {
       float sum = 0.0f;
 #pragma unroll
       for (int tt = 0; tt < RT; ++tt) {
-        if (tt < nvalid) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float v = fast_exp2(fmaf(acc[tt][e], cl2, -bias[tt][e]));
-            if (need_mask && key > lim[tt][e]) v = 0.0f;
-            sum += v;
-          }
+        for (int e = 0; e < 4; ++e) {
+          float v = fast_exp2(fmaf(acc[tt][e], cl2, -bias[tt][e]));
+          if (need_mask && key > lim[tt][e]) v = 0.0f;
+          sum += v;
         }
       }
       sum += __shfl_xor(sum, 16);
       sum += __shfl_xor(sum, 32);
       if (lq == 0) lds[rg * p.key_block + (i0 - kb0) + lc] = sum;
     }
+  };
 
-    if (ti + p.ks < ntile) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) kf[j] = kn[j];
-    }
+  // Two key tiles in flight per wave (ping-pong), every load unconditional.
+  bf16x8 ka[4], kb[4];
+  load_key_tile(ka, kbase, key0, L, p.Hkv, kb0 + ks * kTile + lc);
+  for (int ti = ks; ti < ntile; ti += 2 * step) {
+    load_key_tile(kb, kbase, key0, L, p.Hkv, kb0 + (ti + step) * kTile + lc);
+    tile(ka, ti);
+    load_key_tile(ka, kbase, key0, L, p.Hkv, kb0 + (ti + 2 * step) * kTile + lc);
+    if (ti + step < ntile) tile(kb, ti + step);
   }
 
   if constexpr (PASS == 2) {
@@ -284,7 +297,7 @@ __global__ __launch_bounds__(512) void score_kernel(ScoreParams p, SegTable t) {
     }
     __threadfence();
     __syncthreads();
-    if (threadIdx.x == 0) s_last = arrive_last(&p.tickets[seg], p.epoch, (uint32_t)nblk_seg) ? 1 : 0;
+    if (threadIdx.x == 0) s_last = arrive_last(&p.tickets[seg - t.seg0], (uint32_t)nblk_seg) ? 1 : 0;
     __syncthreads();
     if (!s_last) return;
     __threadfence();
@@ -305,22 +318,27 @@ __global__ __launch_bounds__(512) void score_kernel(ScoreParams p, SegTable t) {
   }
 }
 
-}  // namespace
-
-hipError_t launch_score_pass1(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
+template <int PASS>
+hipError_t launch_pass(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s, size_t lds) {
   const dim3 grid(nblk, p.Hkv, t.nseq);
   const dim3 block(64 * p.nrg * p.ks);
-  const size_t lds = (size_t)p.ks * p.Rpad * sizeof(float2);
-  hipLaunchKernelGGL(score_kernel<1>, grid, block, lds, s, p, t);
+  switch (p.rt) {
+    case 1: hipLaunchKernelGGL((score_kernel<PASS, 1>), grid, block, lds, s, p, t); break;
+    case 2: hipLaunchKernelGGL((score_kernel<PASS, 2>), grid, block, lds, s, p, t); break;
+    case 3: hipLaunchKernelGGL((score_kernel<PASS, 3>), grid, block, lds, s, p, t); break;
+    default: hipLaunchKernelGGL((score_kernel<PASS, 4>), grid, block, lds, s, p, t); break;
+  }
   return hipGetLastError();
 }
 
+}  // namespace
+
+hipError_t launch_score_pass1(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
+  return launch_pass<1>(p, t, nblk, s, (size_t)p.ks * p.Rpad * sizeof(float2));
+}
+
 hipError_t launch_score_pass2(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
-  const dim3 grid(nblk, p.Hkv, t.nseq);
-  const dim3 block(64 * p.nrg * p.ks);
-  const size_t lds = (size_t)p.nrg * p.key_block * sizeof(float);
-  hipLaunchKernelGGL(score_kernel<2>, grid, block, lds, s, p, t);
-  return hipGetLastError();
+  return launch_pass<2>(p, t, nblk, s, (size_t)p.nrg * p.key_block * sizeof(float));
 }
 
 }  // namespace kvsel

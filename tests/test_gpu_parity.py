@@ -141,7 +141,7 @@ def test_entry_points_compose_and_repeat(kv):
     idx = torch.empty(max(1, offs[-1]), dtype=torch.int32, device=DEV)
     Ko = torch.empty(max(1, offs[-1]), 128, dtype=torch.bfloat16, device=DEV)
     Vo = torch.empty_like(Ko)
-    wsb = torch.full((ws,), 0xAB, dtype=torch.uint8, device=DEV)  # garbage workspace is fine
+    wsb = torch.full((ws,), 0xAB, dtype=torch.uint8, device=DEV)  # arbitrary initial bytes are fine
     kv.kvsel_score(p, Q, K, scores, wsb)
     kv.kvsel_pool_topk(p, scores, pooled, idx, wsb)
     kv.kvsel_gather(p, idx, K, V, Ko, Vo)
