@@ -1,6 +1,6 @@
 """Compile libkvsel.so for gfx950 with hipcc (no GPU needed to build).
 
-Usage: ``python -m attention_token_selection_amd.build`` or ``build_library()``.
+Usage: ``python attention_token_selection_amd/build.py`` or ``build_library()``.
 """
 
 from __future__ import annotations

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvsel.so
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kvsel.h")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m attention_token_selection_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python attention_token_selection_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
