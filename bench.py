@@ -39,10 +39,9 @@ def algorithmic_bytes(spec, kept_rows: int):
             "path": k_bytes + q_bytes + gather + idx}
 
 
-def cpu_baseline(spec, cases, layers):
-    """The fp64 oracle, untuned, on the host cores, over `layers` layers."""
-    import numpy as np
-
+def cpu_baseline(spec, cases, budget_s):
+    """The fp64 oracle, untuned, on the host cores: whole layers (all KV
+    heads) until about ``budget_s`` seconds of oracle time have been spent."""
     import oracle.kvsel_oracle as O
     import workloads as W
 
@@ -51,10 +50,11 @@ def cpu_baseline(spec, cases, layers):
 
         threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
     except Exception:  # pragma: no cover - informational only
-        threads = os.cpu_count() or 1
+        threads = len(os.sched_getaffinity(0))
     total = 0.0
     tokens = 0
-    for layer in range(layers):
+    layers = 0
+    for layer in range(spec.layers):
         c = cases[layer]
         Q = c["Q"].to("cpu").double().numpy()
         K = c["K"].to("cpu").double().numpy()
@@ -63,10 +63,13 @@ def cpu_baseline(spec, cases, layers):
         O.compress(Q, K, V, **W.oracle_kwargs(spec))
         total += time.perf_counter() - t0
         tokens += sum(spec.seq_lens)
+        layers += 1
         del Q, K, V
+        if total >= budget_s:
+            break
     return {"value": tokens / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"layers 0-{layers - 1} of {spec.layers} (all {spec.Hkv} KV heads, L={spec.seq_lens[0]}), "
-                      f"{total:.1f} s of numpy fp64 on the host"}
+                      f"{total:.1f} s of numpy fp64 oracle time on the host"}
 
 
 def main():
@@ -75,7 +78,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--graph", type=int, default=1, help="replay each step from a captured HIP graph")
-    ap.add_argument("--cpu-layers", type=int, default=2, help="layers the CPU oracle baseline covers (0: skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle time the CPU baseline runs for, in whole layers (0: skip)")
     ap.add_argument("--stage-reps", type=int, default=3)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -175,9 +179,9 @@ def main():
     achieved = score_bytes / (stage["score"] * 1e-6) / 1e9
 
     cpu = None
-    if args.cpu_layers > 0:
-        print(f"[bench] cpu oracle baseline over {args.cpu_layers} layers", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(spec, cases, args.cpu_layers)
+    if args.cpu_seconds > 0:
+        print(f"[bench] cpu oracle baseline, about {args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(spec, cases, args.cpu_seconds)
 
     line = {
         "metric": METRIC,
