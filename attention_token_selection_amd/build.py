@@ -25,6 +25,9 @@ HIPCC_FLAGS = [
     "-fvisibility=hidden",
     # keep hipcc from forming packed fp32 arithmetic on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs (no copies out of AGPRs before the
+    # exp/sum epilogue)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

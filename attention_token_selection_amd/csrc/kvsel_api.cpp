@@ -27,7 +27,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Everything the launches need, derived from a validated kvsel_problem.
 struct Plan {
-  int B, Hq, Hkv, G, w, wp, R, nrt, nrg, rt, Rpad, ks;
+  int B, Hq, Hkv, G, w, wp, R, nrt, Rpad;
   int has_decode, causal, pool, pool_kernel;
   float alpha, cl2;
   std::vector<int64_t> seq_off;  // B + 1
@@ -35,16 +35,16 @@ struct Plan {
   std::vector<int64_t> out_off;  // B * Hkv + 1
   int64_t Lmax = 0;
   int kb1 = 0, kb2 = 0, nblk1_max = 0, nblk2_max = 0;
-  size_t off_tickets = 0, off_partials = 0, off_bias = 0, off_scores = 0, off_pooled = 0, ws_bytes = 0;
+  size_t off_partials = 0, off_bias = 0, off_scores = 0, off_pooled = 0, ws_bytes = 0;
 };
 
-int auto_key_block(int64_t head_keys, int waves_per_wg, int ks, int cap) {
-  // Aim for about 2048 waves over the launch (8 per compute unit).
-  const int64_t wgs = std::max<int64_t>(1, 2048 / waves_per_wg);
+int auto_key_block(int64_t head_keys, int64_t cap) {
+  // Aim for about 1024 workgroups (four per compute unit) over the launch,
+  // in whole 32-key tiles, at least two tiles per workgroup.
+  const int64_t wgs = 1024;
   int64_t kb = (head_keys + wgs - 1) / wgs;
-  const int64_t unit = (int64_t)kTile * ks;
-  kb = (kb + unit - 1) / unit * unit;
-  kb = std::max<int64_t>(kb, unit * 4);
+  kb = (kb + kKeyTile - 1) / kKeyTile * kKeyTile;
+  kb = std::max<int64_t>(kb, 2 * kKeyTile);
   kb = std::min<int64_t>(kb, cap);
   return (int)kb;
 }
@@ -65,7 +65,8 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
     return fail(KVSEL_EINVAL, "pool_kernel must be odd and >= 1");
   if (p->pool != KVSEL_POOL_NONE && p->pool_kernel > kMaxPoolKernel)
     return fail(KVSEL_EUNSUPPORTED, "pool_kernel wider than 255");
-  if (p->key_chunk < 0 || p->key_chunk % kTile != 0) return fail(KVSEL_EINVAL, "key_chunk must be 0 or a positive multiple of 16");
+  if (p->key_chunk < 0 || p->key_chunk % kKeyTile != 0)
+    return fail(KVSEL_EINVAL, "key_chunk must be 0 or a positive multiple of 32");
   if (!p->budgets_h && p->k < 0) return fail(KVSEL_EINVAL, "k must be >= 0");
 
   P.B = p->batch;
@@ -117,22 +118,16 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   const float scale = (p->scale == 0.0f) ? 1.0f / std::sqrt((float)p->d) : p->scale;
   P.cl2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
 
-  P.nrt = (P.R + kTile - 1) / kTile;
-  P.nrg = (P.nrt + kRowTilesPerWave - 1) / kRowTilesPerWave;
-  P.rt = (P.nrt + P.nrg - 1) / P.nrg;  // spread the row tiles evenly over the row groups
-  P.Rpad = P.nrg * P.rt * kTile;
-  P.ks = std::max(1, 4 / P.nrg);
+  P.nrt = (P.R + kRowTile - 1) / kRowTile;
+  P.Rpad = P.nrt * kRowTile;
   const int64_t head_keys = P.seq_off[P.B] * P.Hkv;
-  const int waves = P.nrg * P.ks;
-  P.kb1 = p->key_chunk > 0 ? p->key_chunk : auto_key_block(head_keys, waves, P.ks, 4096);
-  P.kb2 = auto_key_block(head_keys, waves, P.ks, std::min(4096, 16384 / P.nrg));
+  P.kb1 = p->key_chunk > 0 ? p->key_chunk : auto_key_block(head_keys, 4096);
+  P.kb2 = auto_key_block(head_keys, 2048);
   P.nblk1_max = (int)((P.Lmax + P.kb1 - 1) / P.kb1);
   P.nblk2_max = (int)((P.Lmax + P.kb2 - 1) / P.kb2);
 
   const size_t nseg = (size_t)P.B * P.Hkv;
   size_t off = 0;
-  P.off_tickets = off;  // fixed: the same bytes for every problem, so tickets stay valid across problems
-  off = align_up(off + kTicketBytes, 256);
   P.off_partials = off;
   off = align_up(off + nseg * P.nblk1_max * P.Rpad * sizeof(float2), 256);
   P.off_bias = off;
@@ -216,7 +211,6 @@ ScoreParams score_params(const Plan &P, const void *Q, const void *K, float *sco
   sp.scores = scores;
   sp.partials = reinterpret_cast<float2 *>(ws + P.off_partials);
   sp.bias = reinterpret_cast<float *>(ws + P.off_bias);
-  sp.tickets = reinterpret_cast<unsigned long long *>(ws + P.off_tickets);
   sp.Hq = P.Hq;
   sp.Hkv = P.Hkv;
   sp.G = P.G;
@@ -230,9 +224,6 @@ ScoreParams score_params(const Plan &P, const void *Q, const void *K, float *sco
   sp.cl2 = P.cl2;
   sp.alpha = P.alpha;
   sp.nblk1_max = P.nblk1_max;
-  sp.nrg = P.nrg;
-  sp.rt = P.rt;
-  sp.ks = P.ks;
   return sp;
 }
 

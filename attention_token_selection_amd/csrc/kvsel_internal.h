@@ -9,11 +9,11 @@ namespace kvsel {
 
 constexpr int kHeadDim = 128;        // d supported by this build
 constexpr int kMaxSeg = 64;          // (sequence, KV head) segments handled per launch
-constexpr int kTile = 16;            // keys per MFMA tile and rows per row tile
-constexpr int kRowTilesPerWave = 4;  // most row tiles (of 16 rows) held by one wave
-constexpr int kMaxRows = 512;        // observation rows per KV head (G * w')
+constexpr int kKeyTile = 32;         // keys per score tile (one 32x32 MFMA column block)
+constexpr int kRowTile = 32;         // observation rows per row tile
+constexpr int kScoreThreads = 256;   // threads (4 waves) of a score workgroup
+constexpr int kMaxRows = 512;        // observation rows per KV head (G * w'): 16 row tiles, 4 per wave
 constexpr int kSelectThreads = 1024; // threads of the per-segment select workgroup
-constexpr int kTicketBytes = kMaxSeg * 8;  // ticket header at the start of every workspace
 constexpr int kMaxPoolKernel = 255;  // widest pool supported
 
 // Per-launch description of the sequences and segments a kernel works on.
@@ -35,15 +35,14 @@ struct ScoreParams {
   float *scores;                // pass 2 output (layout of the public ABI)
   float2 *partials;             // pass 1 per-block (ref, Z), [nseg][nblk1_max][Rpad]
   float *bias;                  // pass 1 result per row, [nseg][Rpad]
-  unsigned long long *tickets;  // arrival tickets of the launch's segments (fixed header of the workspace)
-  int Hq, Hkv, G, w, wp, R, Rpad, nrt;
+  int Hq, Hkv, G, w, wp, R;
+  int nrt;                      // row tiles of 32 rows
+  int Rpad;                     // nrt * 32
   int has_decode, causal;
   float cl2;                    // scale * log2(e)
   float alpha;
-  int key_block;                // keys per workgroup in this pass
+  int key_block;                // keys per workgroup in this pass (multiple of 32)
   int nblk1_max;                // pass 1 blocks per segment of the longest sequence
-  int nrg, ks;                  // row groups and key splits (waves = nrg * ks)
-  int rt;                       // row tiles per row group (1..4)
 };
 
 struct SelectParams {

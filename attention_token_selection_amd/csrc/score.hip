@@ -1,47 +1,55 @@
 // Two-pass blockwise scoring of every prefix key against the observation rows
 // (TideKV, "Delayed KV Eviction via Layer-Wise Chunked Prefill", §4.2).
 //
-// Work unit: one workgroup per (key block, KV head, sequence).  Inside it,
-// waves are split into `nrg` row groups (4 row tiles = 64 observation rows
-// each) times `ks` key splits (interleaved 16-key tiles).  Every wave keeps
-// its rows' query fragments in registers for the whole block and streams its
-// key tiles from HBM straight into MFMA operands:
+// Work unit: one workgroup of four waves per (key block, KV head, sequence).
+// The block's keys are streamed in tiles of 32 keys (8 KiB of K).  Every
+// thread prefetches its share of the next PD tiles into registers with
+// coalesced 16-byte loads; a tile is then written to one of two LDS slots in
+// a swizzled layout (16-byte chunk c of key r lands in position c ^ (r & 15)
+// of the row, so the MFMA operand reads below are free of bank conflicts),
+// and after one barrier all four waves read it.  The observation rows
+// (R = G * w' per KV head, row = window row * G + query head of the group)
+// are split into row tiles of 32; wave v owns row tiles v, v+4, v+8, v+12
+// and keeps their query fragments in registers for the whole block.
 //
-//   D[16 rows x 16 keys] += Q[16 rows x 32 dims] * K^T[32 dims x 16 keys]
-//   (v_mfma_f32_16x16x32_bf16, four k-steps cover d = 128).
+// Contraction: v_mfma_f32_32x32x16_bf16 over d = 128 in 8 k-steps.  Lane l
+// supplies, at k-step j, the 16-byte chunk 2j + l/32 of row l%32 of each
+// operand; the same permutation of the contraction index is used for Q and
+// K, so the products are unchanged.
 //
-// The contraction index may be permuted freely as long as Q and K agree, so
-// lane group q = lane/16 of k-step j supplies the 16-byte chunk q + 4j of a
-// 256-byte row: one load instruction then reads 64 contiguous bytes from each
-// of 16 keys, and the four k-steps read every byte of the row once.
+// Pass 1 puts the keys in the MFMA's M dimension (A = K, B = Q), so each lane
+// holds 16 logits of one observation row.  The lane keeps a reference r and
+// Z = sum 2^(x - r) of its base-2 logits x = s * scale * log2(e); r is only
+// moved when Z would leave a safe range (checked once per tile for the whole
+// wave), so the common path costs one FMA, one exp2 and one add per logit.
+// The two lanes of a row are merged with the log-sum-exp rule and each
+// block's per-row state is stored; a small merge launch then combines the
+// blocks, in a fixed order, into per row bias = r + log2(Z) - log2(c_r).
 //
-// Pass 1 keeps, per accumulator slot (row, key lane), a reference r and
-// Z = sum 2^(x - r) of the base-2 logits x = s * scale * log2(e).  A slot's
-// reference only moves when a new logit exceeds it by more than 2^16, checked
-// once per tile for the whole wave, so the common path costs one FMA, one
-// exp2 and one add per logit.  Slots merge with the log-sum-exp rule, first
-// across lanes, then across key splits, then -- in the last workgroup of a
-// (sequence, head) to arrive -- across key blocks, in a fixed order, giving
-// per row bias = r + log2(Z) - log2(c_r).
-//
-// Pass 2 recomputes the logits and adds 2^(x - bias) over the wave's rows
-// in-lane, across lane groups with two butterflies, and across row groups in
-// LDS, in a fixed order (no floating-point atomics: results are
-// bit-reproducible).
+// Pass 2 puts the observation rows in M (A = Q, B = K), so each lane holds 16
+// rows of one key: it adds c_r * p = 2^(x - bias) over its rows in-lane, the
+// two lane halves are combined with one swap, the four waves in LDS, in a
+// fixed order (no floating-point atomics: results are bit-reproducible).
 #include "kvsel_internal.h"
 
 namespace kvsel {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-constexpr float kLazyThreshold = 16.0f;  // log2 units a logit may exceed its slot reference
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__device__ inline bf16x8 load_frag(const uint16_t *p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
-}
+constexpr int NT = kScoreThreads;        // 256 threads, 4 waves
+constexpr int NW = NT / 64;
+constexpr int KT = kKeyTile;             // 32 keys per tile
+constexpr int ROWB = kHeadDim * 2;       // 256 bytes per key row
+constexpr int TILE_BYTES = KT * ROWB;    // 8 KiB
+constexpr int TILE_CHUNKS = TILE_BYTES / 16;
+constexpr int LPT = TILE_CHUNKS / NT;    // 16-byte chunks each thread moves per tile
+static_assert(LPT == 2, "TileRegs holds two chunks");
+constexpr int PD = 4;                    // tiles in flight per workgroup (four named buffers below)
+constexpr float kZLimit = 0x1p100f;      // a lane's running sum stays below this
 
-__device__ inline bf16x8 zero_frag() { return __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u)); }
+__device__ inline bf16x8 as_frag(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -56,59 +64,63 @@ __device__ inline void lse_merge(float &r, float &z, float r2, float z2) {
   z = a + b;
 }
 
-// Arrival ticket of a (sequence, head) for the last-arriver merge.  A ticket
-// is (kTicketTag << 32 | arrivals so far); the last arriver resets it to
-// (kTicketTag << 32 | 0), so between calls every ticket reads "tag, 0" and an
-// arrival is one fetch-add.  A ticket without the tag (a fresh workspace
-// holding arbitrary bytes) is claimed once with a compare-and-swap; arrivals
-// that raced onto the untagged value are discarded by that swap and redone.
-constexpr uint32_t kTicketTag = 0x6b76736cu;
+// A thread's two 16-byte chunks of a tile (plain values, so they stay in
+// registers).  Chunk q of a tile (q = thread, thread + 256) holds 16-byte
+// chunk (q & 15) ^ (row & 15) of key row = q >> 4: the swizzled LDS layout.
+struct TileRegs {
+  uint4 a, b;
+};
 
-__device__ bool arrive_last(unsigned long long *ticket, uint32_t n) {
-  const unsigned long long tag = (unsigned long long)kTicketTag << 32;
-  unsigned long long old = __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  uint32_t count;
-  if ((uint32_t)(old >> 32) == kTicketTag) {
-    count = (uint32_t)old + 1u;
-  } else {
-    unsigned long long cur = old + 1ull;
-    for (;;) {
-      if ((uint32_t)(cur >> 32) == kTicketTag) {
-        old = __hip_atomic_fetch_add(ticket, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        count = (uint32_t)old + 1u;
-        break;
-      }
-      if (__hip_atomic_compare_exchange_strong(ticket, &cur, tag | 1ull, __ATOMIC_ACQ_REL, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT)) {
-        count = 1u;
-        break;
-      }
-    }
-  }
-  if (count == n) {
-    __hip_atomic_store(ticket, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return true;
-  }
-  return false;
+// Loads of key tile i0 .. i0+31 from `kt` = the tile's first key row of this
+// head.  Rows past `rmax` (last key of the block minus i0, wave-uniform) are
+// clamped to it, so every load is in bounds and a tile past the end of the
+// block re-reads one cached row; such keys are masked or never consumed.
+__device__ inline TileRegs load_tile(const uint16_t *kt, int rmax, int rowstride, int ra, int ca, int cb) {
+  TileRegs t;
+  t.a = *reinterpret_cast<const uint4 *>(kt + (min(ra, rmax) * rowstride + ca));
+  t.b = *reinterpret_cast<const uint4 *>(kt + (min(ra + 16, rmax) * rowstride + cb));
+  return t;
 }
 
-// Key fragments of this lane's key.  The key index is clamped into the
-// sequence so every load is in bounds and branch-free; keys past the end are
-// masked in the epilogue.
-__device__ inline void load_key_tile(bf16x8 (&kf)[4], const uint16_t *kbase, int64_t key0, int L, int Hkv,
-                                     int key) {
-  const int kk = min(key, L - 1);
-  const uint16_t *src = kbase + (key0 + kk) * Hkv * (int64_t)kHeadDim;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) kf[j] = load_frag(src + 32 * j);
+__device__ inline void store_tile(char *slot, const TileRegs &v) {
+  *reinterpret_cast<uint4 *>(slot + threadIdx.x * 16) = v.a;
+  *reinterpret_cast<uint4 *>(slot + (threadIdx.x + NT) * 16) = v.b;
 }
 
-// RT: row tiles held per wave (the launch spreads the row tiles evenly over
-// the row groups; tiles past the last row hold zero queries).
+// Row bookkeeping: observation row index -> causal limit (last visible key).
+__device__ inline int row_limit(int row, const ScoreParams &p, int L) {
+  const int r = row / p.G;
+  if (!p.causal || r >= p.w) return L - 1;
+  return L - p.w + r;  // <= L - 1
+}
+
+// x + (the same register of the other lane half), identical in both halves.
+__device__ inline float sum_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// The value of x held by lane l ^ 32.
+__device__ inline float other_half(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return (threadIdx.x & 32) ? __uint_as_float(sw[0]) : __uint_as_float(sw[1]);
+}
+
+// Sum of 16 values as four interleaved chains (shorter dependency chains; the
+// order is fixed, so results stay reproducible).
+__device__ inline float sum16(const float (&e)[16]) {
+  const float a = (e[0] + e[4]) + (e[8] + e[12]);
+  const float b = (e[1] + e[5]) + (e[9] + e[13]);
+  const float c = (e[2] + e[6]) + (e[10] + e[14]);
+  const float d = (e[3] + e[7]) + (e[11] + e[15]);
+  return (a + b) + (c + d);
+}
+
+// RT: row tiles (of 32 rows) per wave.
 template <int PASS, int RT>
-__global__ __launch_bounds__(512) void score_kernel(ScoreParams p, SegTable t) {
-  extern __shared__ float lds[];
-  __shared__ int s_last;
+__global__ __launch_bounds__(NT) void score_kernel(ScoreParams p, SegTable t) {
+  __shared__ __attribute__((aligned(16))) char tiles[2][TILE_BYTES];
+  extern __shared__ float red[];  // pass 2: [NW][key_block] partial sums
 
   const int blk = blockIdx.x;
   const int h = blockIdx.y;
@@ -121,208 +133,285 @@ __global__ __launch_bounds__(512) void score_kernel(ScoreParams p, SegTable t) {
   const int seg = t.seg0 + sb * p.Hkv + h;
   const int b = t.seq0 + sb;
 
-  // wave-uniform indices (scalar registers, scalar branches)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int rg = wave % p.nrg;
-  const int ks = wave / p.nrg;
-  const int lq = lane >> 4;  // lane group: rows 4*lq.. of a D tile, chunk group of A/B
-  const int lc = lane & 15;  // key column of a D tile, row of an A tile
-
-  // Query fragments of this wave's row tiles (rows = window row major,
-  // query head of the group minor).
-  bf16x8 qf[RT][4];
+  const int lr = lane & 31;  // row (pass 1: observation row; pass 2: key) within a 32-tile
+  const int hf = lane >> 5;  // lane half: chunk parity, and rows 4*hf.. of the output
+  const int nrt = p.nrt;     // row tiles of 32 over all waves
+  int my_rt = 0;             // row tiles this wave owns (wave-uniform)
 #pragma unroll
-  for (int tt = 0; tt < RT; ++tt) {
-    const int row = (rg * RT + tt) * kTile + lc;
-    if (row < p.R) {
+  for (int k = 0; k < RT; ++k) my_rt += (wave + NW * k < nrt) ? 1 : 0;
+
+  // Query fragments of this wave's row tiles: lane supplies row lr of the
+  // tile, chunks 2j + hf.
+  bf16x8 qf[RT][8];
+#pragma unroll
+  for (int k = 0; k < RT; ++k) {
+    const int row = (wave + NW * k) * 32 + lr;
+    if (k < my_rt && row < p.R) {
       const int r = row / p.G;
       const int gi = row - r * p.G;
-      const uint16_t *src =
-          p.Q + ((int64_t)(b * p.wp + r) * p.Hq + h * p.G + gi) * (int64_t)kHeadDim + lq * 8;
+      const uint16_t *src = p.Q + ((int64_t)(b * p.wp + r) * p.Hq + h * p.G + gi) * (int64_t)kHeadDim + hf * 8;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) qf[tt][j] = load_frag(src + 32 * j);
+      for (int j = 0; j < 8; ++j) qf[k][j] = as_frag(*reinterpret_cast<const uint4 *>(src + 16 * j));
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) qf[tt][j] = zero_frag();
+      for (int j = 0; j < 8; ++j) qf[k][j] = as_frag(make_uint4(0u, 0u, 0u, 0u));
     }
   }
 
-  // Last visible key of each accumulator slot's row (causal limit, and the
-  // end of the sequence for every row).
-  int lim[RT][4];
-  float bias[RT][4];
-  float ref[RT][4], zs[RT][4];
+  // Per-lane state.  Pass 1: reference, sum and causal limit of the lane's
+  // row in each row tile.  Pass 2: bias of the lane's 16 rows per row tile.
+  float ref[RT], zs[RT];
+  int lim[RT];
+  float bias[RT][16];
 #pragma unroll
-  for (int tt = 0; tt < RT; ++tt) {
+  for (int k = 0; k < RT; ++k) {
+    ref[k] = -INFINITY;
+    zs[k] = 0.0f;
+    lim[k] = row_limit((wave + NW * k) * 32 + lr, p, L);
+    if constexpr (PASS == 2) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = (rg * RT + tt) * kTile + 4 * lq + e;
-      const int r = row / p.G;
-      const int pos = (r < p.w) ? (L - p.w + r) : L;
-      lim[tt][e] = p.causal ? min(pos, L - 1) : (L - 1);
-      ref[tt][e] = -INFINITY;
-      zs[tt][e] = 0.0f;
-      bias[tt][e] = (PASS == 2) ? p.bias[(int64_t)seg * p.Rpad + row] : 0.0f;
+      for (int i = 0; i < 16; ++i) {
+        const int row = (wave + NW * k) * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+        bias[k][i] = (k < my_rt) ? p.bias[(int64_t)seg * p.Rpad + row] : INFINITY;
+      }
     }
   }
 
-  const int ntile = (kb1 - kb0 + kTile - 1) / kTile;
-  const int mask_from = p.causal ? (L - p.w) : L;
   const float cl2 = p.cl2;
-  const int step = p.ks;
-  const uint16_t *kbase = p.K + (int64_t)h * kHeadDim + lq * 8;
+  const int minlim = p.causal ? (L - p.w) : (L - 1);  // keys up to here are visible to every row
+  const int ntile = (kb1 - kb0 + KT - 1) / KT;
+  const int rowstride = p.Hkv * kHeadDim;  // elements between consecutive keys of one head
+  const uint16_t *kblk = p.K + (key0 + kb0) * (int64_t)rowstride + (int64_t)h * kHeadDim;
+  const int last = kb1 - 1 - kb0;  // block-relative index of the block's last key
+  // This thread's load slots: rows ra and ra + 16, chunk offsets (elements).
+  const int ra = threadIdx.x >> 4;
+  const int ca = (((threadIdx.x & 15) ^ (ra & 15)) * 8);
+  const int cb = ca;  // row ra + 16 has the same low four bits
+  // LDS byte offset of this lane's operand chunk for k-step j: row lr, chunk 2j + hf, swizzled.
+  const int rd_base = lr * ROWB;
+  const int sw = lr & 15;
 
-  auto tile = [&](const bf16x8(&kf)[4], int ti) {
-    const int i0 = kb0 + ti * kTile;
-    f32x4 acc[RT];
-#pragma unroll
-    for (int tt = 0; tt < RT; ++tt) acc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int tt = 0; tt < RT; ++tt)
-        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[tt][j], kf[j], acc[tt], 0, 0, 0);
+  // Loads are issued unconditionally (past the block they re-read its last
+  // row), so every wait below is for exactly the buffer about to be used.
+  // The scheduling barriers keep the four prologue loads in tile order, the
+  // order in which the loop consumes them.
+  auto tile_src = [&](int ti) { return kblk + (int64_t)(ti * KT) * rowstride; };
+  TileRegs pf0 = load_tile(tile_src(0), last - 0 * KT, rowstride, ra, ca, cb);
+  __builtin_amdgcn_sched_barrier(0);
+  TileRegs pf1 = load_tile(tile_src(1), last - 1 * KT, rowstride, ra, ca, cb);
+  __builtin_amdgcn_sched_barrier(0);
+  TileRegs pf2 = load_tile(tile_src(2), last - 2 * KT, rowstride, ra, ca, cb);
+  __builtin_amdgcn_sched_barrier(0);
+  TileRegs pf3 = load_tile(tile_src(3), last - 3 * KT, rowstride, ra, ca, cb);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Consumes tile ti from `buf` and returns the registers refilled with
+  // tile ti + PD.
+  auto step = [&](TileRegs buf, const int ti) -> TileRegs {
+    char *slot = tiles[ti & 1];
+    store_tile(slot, buf);
+    buf = load_tile(tile_src(ti + PD), last - (ti + PD) * KT, rowstride, ra, ca, cb);
+    __syncthreads();
+    if (ti >= ntile) return buf;  // padding step of the last group of four
+    const int i0 = kb0 + ti * KT;
+    if (my_rt == 0) {  // this wave owns no rows (fewer than four row tiles in all)
+      if constexpr (PASS == 2)
+        if (hf == 0) red[wave * p.key_block + ti * KT + lr] = 0.0f;
+      return buf;
     }
 
-    const bool need_mask = (i0 + kTile) > mask_from;
-    const int key = i0 + lc;
+    // All eight K fragments of the tile go to distinct registers before the
+    // first MFMA: no LDS read may land in a register that a queued MFMA has
+    // yet to read (a later fragment would otherwise reuse the registers of
+    // an earlier one while the matrix pipe still holds that MFMA).
+    bf16x8 kf[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      kf[j] = as_frag(*reinterpret_cast<const uint4 *>(slot + rd_base + (((2 * j + hf) ^ sw) << 4)));
+    f32x16 acc[RT];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int k = 0; k < RT; ++k) {
+        if (k < my_rt) {
+          const f32x16 c = (j == 0) ? f32x16{} : acc[k];
+          if constexpr (PASS == 1)
+            acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[k][j], c, 0, 0, 0);
+          else
+            acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[k][j], kf[j], c, 0, 0, 0);
+        }
+      }
+    }
+    const bool need_mask = (i0 + KT - 1) > minlim;
 
     if constexpr (PASS == 1) {
-      float tv[RT][4];
-      float mx = -INFINITY;
+      // acc[k][i]: key i0 + 8*(i/4) + 4*hf + i%4, row of this lane.
+      bool bad = false;
+      float znew[RT];
 #pragma unroll
-      for (int tt = 0; tt < RT; ++tt) {
+      for (int k = 0; k < RT; ++k) {
+        float e[16];
+        if (!need_mask) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float v = fmaf(acc[tt][e], cl2, -ref[tt][e]);
-          if (need_mask && key > lim[tt][e]) v = -INFINITY;
-          tv[tt][e] = v;
-          mx = fmaxf(mx, v);
-        }
-      }
-      if (__ballot(mx > kLazyThreshold) != 0ull) {
-        // Rare: some logit outgrew its slot's reference; move references up.
+          for (int i = 0; i < 16; ++i) e[i] = fast_exp2(fmaf(acc[k][i], cl2, -ref[k]));
+        } else {
 #pragma unroll
-        for (int tt = 0; tt < RT; ++tt) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (need_mask && key > lim[tt][e]) continue;
-            const float x = acc[tt][e] * cl2;
-            if (x > ref[tt][e]) {
-              zs[tt][e] = (ref[tt][e] == -INFINITY) ? 0.0f : zs[tt][e] * fast_exp2(ref[tt][e] - x);
-              ref[tt][e] = x;
-            }
-            tv[tt][e] = x - ref[tt][e];
+          for (int i = 0; i < 16; ++i) {
+            const float v = fast_exp2(fmaf(acc[k][i], cl2, -ref[k]));
+            e[i] = ((i0 + 8 * (i >> 2) + 4 * hf + (i & 3)) > lim[k]) ? 0.0f : v;
           }
         }
+        // Row tiles this wave does not own skipped their MFMAs: their
+        // accumulators hold stale register contents and must not be summed.
+        znew[k] = (k < my_rt) ? zs[k] + sum16(e) : 0.0f;
+        bad |= (k < my_rt) && !(znew[k] <= kZLimit);
       }
+      if (__builtin_expect(__ballot(bad) != 0ull, 0)) {
+        // Rare (always on a wave's first tile): move each reference up to
+        // the largest logit seen so far and redo this tile's sum.
 #pragma unroll
-      for (int tt = 0; tt < RT; ++tt) {
+        for (int k = 0; k < RT; ++k) {
+          if (k >= my_rt) continue;
+          float m = ref[k];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) zs[tt][e] += fast_exp2(tv[tt][e]);
+          for (int i = 0; i < 16; ++i) {
+            const bool vis = !need_mask || (i0 + 8 * (i >> 2) + 4 * hf + (i & 3)) <= lim[k];
+            if (vis) m = fmaxf(m, acc[k][i] * cl2);
+          }
+          float z = (ref[k] == -INFINITY || m == -INFINITY) ? 0.0f : zs[k] * fast_exp2(ref[k] - m);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const bool vis = !need_mask || (i0 + 8 * (i >> 2) + 4 * hf + (i & 3)) <= lim[k];
+            if (vis) z += fast_exp2(fmaf(acc[k][i], cl2, -m));
+          }
+          ref[k] = m;
+          zs[k] = z;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < RT; ++k) zs[k] = znew[k];
       }
     } else {
-      float sum = 0.0f;
+      // acc[k][i]: row 8*(i/4) + 4*hf + i%4 of row tile k, key i0 + lr.
+      float part[RT];
 #pragma unroll
-      for (int tt = 0; tt < RT; ++tt) {
+      for (int k = 0; k < RT; ++k) {
+        float e[16];
+        if (!need_mask) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float v = fast_exp2(fmaf(acc[tt][e], cl2, -bias[tt][e]));
-          if (need_mask && key > lim[tt][e]) v = 0.0f;
-          sum += v;
+          for (int i = 0; i < 16; ++i) e[i] = fast_exp2(fmaf(acc[k][i], cl2, -bias[k][i]));
+        } else {
+          const int key = i0 + lr;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = (wave + NW * k) * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+            const float v = fast_exp2(fmaf(acc[k][i], cl2, -bias[k][i]));
+            e[i] = (key > row_limit(row, p, L)) ? 0.0f : v;
+          }
         }
+        part[k] = (k < my_rt) ? sum16(e) : 0.0f;  // unowned tiles: stale accumulators
       }
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
-      if (lq == 0) lds[rg * p.key_block + (i0 - kb0) + lc] = sum;
+      float s = part[0];
+#pragma unroll
+      for (int k = 1; k < RT; ++k) s += part[k];
+      s = sum_halves(s);
+      if (hf == 0) red[wave * p.key_block + ti * KT + lr] = s;
     }
+    return buf;
   };
 
-  // Two key tiles in flight per wave (ping-pong), every load unconditional.
-  bf16x8 ka[4], kb[4];
-  load_key_tile(ka, kbase, key0, L, p.Hkv, kb0 + ks * kTile + lc);
-  for (int ti = ks; ti < ntile; ti += 2 * step) {
-    load_key_tile(kb, kbase, key0, L, p.Hkv, kb0 + (ti + step) * kTile + lc);
-    tile(ka, ti);
-    load_key_tile(ka, kbase, key0, L, p.Hkv, kb0 + (ti + 2 * step) * kTile + lc);
-    if (ti + step < ntile) tile(kb, ti + step);
+  // Whole groups of four steps, no early exit: every path into the loop
+  // head has issued the same loads in the same order, so each wait is exact.
+  for (int t0 = 0; t0 < ntile; t0 += PD) {
+    pf0 = step(pf0, t0);
+    pf1 = step(pf1, t0 + 1);
+    pf2 = step(pf2, t0 + 2);
+    pf3 = step(pf3, t0 + 3);
   }
+  // The last group issued loads for tiles past the block that nobody
+  // consumes; drain them so no load is still in flight when the wave ends.
+  __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
   if constexpr (PASS == 2) {
     __syncthreads();
     const int n = kb1 - kb0;
     float *out = p.scores + (int64_t)p.Hkv * key0 + (int64_t)h * L + kb0;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      float v = 0.0f;
-      for (int g = 0; g < p.nrg; ++g) v += lds[g * p.key_block + i];
+    for (int i = threadIdx.x; i < n; i += NT) {
+      float v = red[i];
+#pragma unroll
+      for (int w2 = 1; w2 < NW; ++w2) v += red[w2 * p.key_block + i];
       out[i] = v;
     }
-    return;
   } else {
-    // Merge the 16 key lanes that share each row (butterfly, symmetric).
-#pragma unroll
-    for (int tt = 0; tt < RT; ++tt) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-          const float r2 = __shfl_xor(ref[tt][e], off);
-          const float z2 = __shfl_xor(zs[tt][e], off);
-          lse_merge(ref[tt][e], zs[tt][e], r2, z2);
-        }
-      }
-    }
-    float2 *st = reinterpret_cast<float2 *>(lds);  // [ks][Rpad]
-    if (lc == 0) {
-#pragma unroll
-      for (int tt = 0; tt < RT; ++tt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = (rg * RT + tt) * kTile + 4 * lq + e;
-          st[ks * p.Rpad + row] = make_float2(ref[tt][e], zs[tt][e]);
-        }
-      }
-    }
-    __syncthreads();
-    const int nblk_seg = (L + p.key_block - 1) / p.key_block;
+    // Merge the two lane halves that share each row and publish this
+    // block's per-row state; the blocks are merged by merge_kernel.
     float2 *part = p.partials + ((int64_t)seg * p.nblk1_max + blk) * p.Rpad;
-    for (int row = threadIdx.x; row < p.Rpad; row += blockDim.x) {
-      float r = -INFINITY, z = 0.0f;
-      for (int k2 = 0; k2 < p.ks; ++k2) {
-        const float2 v = st[k2 * p.Rpad + row];
-        lse_merge(r, z, v.x, v.y);
-      }
-      part[row] = make_float2(r, z);
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = arrive_last(&p.tickets[seg - t.seg0], (uint32_t)nblk_seg) ? 1 : 0;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const float2 *all = p.partials + (int64_t)seg * p.nblk1_max * p.Rpad;
-    for (int row = threadIdx.x; row < p.Rpad; row += blockDim.x) {
-      float r = -INFINITY, z = 0.0f;
-      for (int bb = 0; bb < nblk_seg; ++bb) {
-        const float2 v = all[(int64_t)bb * p.Rpad + row];
-        lse_merge(r, z, v.x, v.y);
-      }
-      const int wr = row / p.G;
-      float c = 1.0f;
-      if (p.has_decode) c = (wr < p.w) ? (1.0f - p.alpha) : p.alpha;
-      float out = INFINITY;
-      if (row < p.R && c > 0.0f && z > 0.0f) out = r + log2f(z) - log2f(c);
-      p.bias[(int64_t)seg * p.Rpad + row] = out;
+#pragma unroll
+    for (int k = 0; k < RT; ++k) {
+      const float r2 = other_half(ref[k]);
+      const float z2 = other_half(zs[k]);
+      lse_merge(ref[k], zs[k], r2, z2);
+      const int row = (wave + NW * k) * 32 + lr;
+      if (hf == 0 && k < my_rt) part[row] = make_float2(ref[k], zs[k]);
     }
   }
+}
+
+// Merge of the pass-1 block states of every (sequence, head) into the
+// per-row bias = r + log2(Z) - log2(c_r) that pass 2 subtracts.  A separate
+// launch: the kernel boundary makes every block's partials visible, with no
+// per-workgroup cache write-backs.  Workgroup (row group of 64, segment):
+// four threads share a row, each merging every fourth block with 16 loads
+// in flight; the four shares are combined in a fixed order through LDS.
+constexpr int MERGE_ROWS = 64;
+constexpr int MERGE_SPLIT = NT / MERGE_ROWS;
+
+__global__ __launch_bounds__(NT) void merge_kernel(ScoreParams p, SegTable t) {
+  __shared__ float2 shares[MERGE_SPLIT][MERGE_ROWS];
+  const int sl = blockIdx.y;  // local segment: sequence-major, head-minor
+  const int sb = sl / p.Hkv;
+  const int seg = t.seg0 + sl;
+  const int L = (int)(t.key_off[sb + 1] - t.key_off[sb]);
+  const int nblk = (L + p.key_block - 1) / p.key_block;
+  const int lrow = threadIdx.x % MERGE_ROWS;
+  const int sh = threadIdx.x / MERGE_ROWS;
+  const int row = blockIdx.x * MERGE_ROWS + lrow;
+  const float2 *all = p.partials + (int64_t)seg * p.nblk1_max * p.Rpad;
+  float r = -INFINITY, z = 0.0f;
+  if (row < p.R) {
+    for (int bb0 = sh; bb0 < nblk; bb0 += 16 * MERGE_SPLIT) {
+      float2 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int bb = bb0 + u * MERGE_SPLIT;
+        v[u] = (bb < nblk) ? all[(int64_t)bb * p.Rpad + row] : make_float2(-INFINITY, 0.0f);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) lse_merge(r, z, v[u].x, v[u].y);
+    }
+  }
+  shares[sh][lrow] = make_float2(r, z);
+  __syncthreads();
+  if (sh != 0 || row >= p.Rpad) return;
+#pragma unroll
+  for (int k = 1; k < MERGE_SPLIT; ++k) lse_merge(r, z, shares[k][lrow].x, shares[k][lrow].y);
+  const int wr = row / p.G;
+  float c = 1.0f;
+  if (p.has_decode) c = (wr < p.w) ? (1.0f - p.alpha) : p.alpha;
+  float out = INFINITY;
+  if (row < p.R && c > 0.0f && z > 0.0f) out = r + log2f(z) - log2f(c);
+  p.bias[(int64_t)seg * p.Rpad + row] = out;
 }
 
 template <int PASS>
 hipError_t launch_pass(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s, size_t lds) {
   const dim3 grid(nblk, p.Hkv, t.nseq);
-  const dim3 block(64 * p.nrg * p.ks);
-  switch (p.rt) {
+  const dim3 block(NT);
+  const int rt = (p.nrt + NW - 1) / NW;
+  switch (rt) {
     case 1: hipLaunchKernelGGL((score_kernel<PASS, 1>), grid, block, lds, s, p, t); break;
     case 2: hipLaunchKernelGGL((score_kernel<PASS, 2>), grid, block, lds, s, p, t); break;
     case 3: hipLaunchKernelGGL((score_kernel<PASS, 3>), grid, block, lds, s, p, t); break;
@@ -334,11 +423,15 @@ hipError_t launch_pass(const ScoreParams &p, const SegTable &t, int nblk, hipStr
 }  // namespace
 
 hipError_t launch_score_pass1(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
-  return launch_pass<1>(p, t, nblk, s, (size_t)p.ks * p.Rpad * sizeof(float2));
+  hipError_t e = launch_pass<1>(p, t, nblk, s, 0);
+  if (e != hipSuccess) return e;
+  const dim3 grid((p.Rpad + MERGE_ROWS - 1) / MERGE_ROWS, t.nseq * p.Hkv);
+  hipLaunchKernelGGL(merge_kernel, grid, dim3(NT), 0, s, p, t);
+  return hipGetLastError();
 }
 
 hipError_t launch_score_pass2(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
-  return launch_pass<2>(p, t, nblk, s, (size_t)p.nrg * p.key_block * sizeof(float));
+  return launch_pass<2>(p, t, nblk, s, (size_t)NW * p.key_block * sizeof(float));
 }
 
 }  // namespace kvsel

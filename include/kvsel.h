@@ -104,7 +104,7 @@ typedef struct kvsel_problem {
   int32_t pool_kernel;           /* odd, >= 1 (ignored for KVSEL_POOL_NONE) */
   int32_t k;                     /* uniform budget >= 0 when budgets_h is NULL */
   const int32_t *budgets_h;      /* host, B*Hkv budgets (>= 0, sequence-major), or NULL */
-  int32_t key_chunk;             /* keys per pass-1 statistics block (multiple of 16), 0 = library choice */
+  int32_t key_chunk;             /* keys per pass-1 statistics block (multiple of 32), 0 = library choice */
 } kvsel_problem;
 
 /* KVSEL_ABI_VERSION of the loaded library. */

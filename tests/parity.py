@@ -63,12 +63,38 @@ def check_selection(gpu_idx, ref_idx, P_ref, keff, L, rtol=RTOL):
     return len(diff)
 
 
-def check_select_exact(gpu_idx, gpu_pooled32, keff):
+def _runs(mask, limit=6):
+    """(first, last) index of the first few runs of True in a boolean array."""
+    idx = np.nonzero(mask)[0]
+    if not len(idx):
+        return []
+    br = np.nonzero(np.diff(idx) > 1)[0]
+    starts = np.concatenate([[idx[0]], idx[br + 1]])
+    ends = np.concatenate([idx[br], [idx[-1]]])
+    return list(zip(starts.tolist(), ends.tolist()))[:limit]
+
+
+def check_finite(x, what):
+    x = np.asarray(x)
+    bad = ~np.isfinite(x)
+    assert not bad.any(), f"{what}: {int(bad.sum())} non-finite values, runs {_runs(bad)}"
+
+
+def check_select_exact(gpu_idx, gpu_pooled32, keff, where=""):
     """Top-k of the GPU's own fp32 pooled scores, from a CPU stable sort."""
     P = np.asarray(gpu_pooled32, dtype=np.float32)
+    check_finite(P, f"{where} pooled")
     order = np.argsort(-P, kind="stable")
     expect = np.sort(order[:keff])
-    np.testing.assert_array_equal(np.asarray(gpu_idx, dtype=np.int64), expect)
+    got = np.asarray(gpu_idx, dtype=np.int64)
+    if not np.array_equal(got, expect):
+        only_gpu = np.setdiff1d(got, expect)[:5]
+        only_cpu = np.setdiff1d(expect, got)[:5]
+        tau = P[order[keff - 1]] if keff else None
+        raise AssertionError(f"{where}: selection differs from a stable sort of the GPU's pooled scores; "
+                             f"k-th value {tau!r}; GPU-only {only_gpu.tolist()} -> {P[only_gpu].tolist() if len(only_gpu) and only_gpu.max() < len(P) else []}; "
+                             f"CPU-only {only_cpu.tolist()} -> {P[only_cpu].tolist()}; "
+                             f"GPU idx ascending: {bool(np.all(np.diff(got) > 0))}, in range: {bool(got.min() >= 0 and got.max() < len(P)) if len(got) else True}")
 
 
 def segments(spec, out_offsets):
@@ -107,8 +133,10 @@ def check_against_oracle(spec, case, out, ref, heads=None, scores=None):
             rows = torch.from_numpy(starts[b] + gidx.astype(np.int64))
             assert torch.equal(Ko[ooff:ooff + keff], Kc[rows, h]), f"K_out mismatch in segment {(b, h)}"
             assert torch.equal(Vo[ooff:ooff + keff], Vc[rows, h]), f"V_out mismatch in segment {(b, h)}"
+        if sc is not None:
+            check_finite(sc[soff:soff + L], f"segment {(b, h)} scores")
         if pooled is not None:
-            check_select_exact(gidx, pooled[soff:soff + L], keff)
+            check_select_exact(gidx, pooled[soff:soff + L], keff, where=f"segment {(b, h)}")
         if heads is not None and (b, h) not in heads:
             continue
         r = ref[(b, h)]

@@ -64,7 +64,7 @@ BAD = {
     "alpha_big": dict(has_decode=True, alpha=1.5),
     "alpha_nan": dict(has_decode=True, alpha=float("nan")),
     "k_negative": dict(k=-1),
-    "chunk_not_16": dict(key_chunk=100),
+    "chunk_not_32": dict(key_chunk=48),
     "decode_flag": dict(has_decode=2),
     "scale_inf": dict(scale=float("inf")),
     "budget_negative": dict(budgets=[[1, -1]]),
