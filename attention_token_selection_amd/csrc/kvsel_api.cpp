@@ -35,7 +35,9 @@ struct Plan {
   std::vector<int64_t> out_off;  // B * Hkv + 1
   int64_t Lmax = 0;
   int kb1 = 0, kb2 = 0, nblk1_max = 0, nblk2_max = 0;
+  int nchunk_max = 0;
   size_t off_partials = 0, off_bias = 0, off_scores = 0, off_pooled = 0, ws_bytes = 0;
+  size_t off_tfine = 0, off_tcoarse = 0, off_bucket = 0;
 };
 
 int auto_key_block(int64_t head_keys, int64_t cap) {
@@ -89,7 +91,7 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   }
   for (int b = 0; b < P.B; ++b) {
     const int64_t Lb = P.seq_off[b + 1] - P.seq_off[b];
-    if (Lb > (int64_t)INT32_MAX / 2) return fail(KVSEL_EUNSUPPORTED, "sequence longer than 2^30 keys");
+    if (Lb > (int64_t)kMaxChunks * kSelectChunk) return fail(KVSEL_EUNSUPPORTED, "sequence longer than 2^20 keys");
     if (p->w > Lb) return fail(KVSEL_EINVAL, "w must not exceed any sequence length");
     P.Lmax = std::max(P.Lmax, Lb);
   }
@@ -136,6 +138,14 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   off = align_up(off + (size_t)head_keys * sizeof(float), 256);
   P.off_pooled = off;
   off = align_up(off + (size_t)head_keys * sizeof(float), 256);
+  P.nchunk_max = (int)((P.Lmax + kSelectChunk - 1) / kSelectChunk);
+  const size_t nchunks = nseg * (size_t)P.nchunk_max;
+  P.off_tfine = off;
+  off = align_up(off + nchunks * kSelectBins * sizeof(uint16_t), 256);
+  P.off_tcoarse = off;
+  off = align_up(off + nchunks * (kSelectBins / 32) * sizeof(uint16_t), 256);
+  P.off_bucket = off;
+  off = align_up(off + nchunks * kSelectChunk * sizeof(uint32_t), 256);
   P.ws_bytes = off;
   return KVSEL_OK;
 }
@@ -240,11 +250,22 @@ kvsel_status run_score(const Plan &P, const void *Q, const void *K, float *score
   });
 }
 
-kvsel_status run_select(const Plan &P, const float *scores, float *pooled, int32_t *idx, hipStream_t st) {
+// Pool + top-k; with K_out given, also the K/V compaction (fused).
+kvsel_status run_select(const Plan &P, const float *scores, float *pooled, int32_t *idx, char *ws, hipStream_t st,
+                        const void *K = nullptr, const void *V = nullptr, void *K_out = nullptr,
+                        void *V_out = nullptr) {
   SelectParams sp;
   sp.scores = scores;
   sp.pooled = pooled;
   sp.idx = idx;
+  sp.tab_fine = reinterpret_cast<uint16_t *>(ws + P.off_tfine);
+  sp.tab_coarse = reinterpret_cast<uint16_t *>(ws + P.off_tcoarse);
+  sp.bucket = reinterpret_cast<uint32_t *>(ws + P.off_bucket);
+  sp.nchunk_max = P.nchunk_max;
+  sp.K = static_cast<const uint4 *>(K);
+  sp.V = static_cast<const uint4 *>(V);
+  sp.K_out = static_cast<uint4 *>(K_out);
+  sp.V_out = static_cast<uint4 *>(V_out);
   sp.Hkv = P.Hkv;
   sp.pool = P.pool;
   sp.pool_kernel = P.pool_kernel;
@@ -326,7 +347,7 @@ KVSEL_API kvsel_status kvsel_pool_topk(const kvsel_problem *p, const float *scor
   if (s == KVSEL_OK) s = check_device();
   if (s != KVSEL_OK) return s;
   float *pool_buf = pooled ? pooled : reinterpret_cast<float *>(static_cast<char *>(ws) + P.off_pooled);
-  return run_select(P, scores, pool_buf, idx, reinterpret_cast<hipStream_t>(stream));
+  return run_select(P, scores, pool_buf, idx, static_cast<char *>(ws), reinterpret_cast<hipStream_t>(stream));
 }
 
 KVSEL_API kvsel_status kvsel_gather(const kvsel_problem *p, const int32_t *idx, const void *K, const void *V,
@@ -366,7 +387,7 @@ KVSEL_API kvsel_status kvsel_compress(const kvsel_problem *p, const void *Q, con
   float *scores = reinterpret_cast<float *>(wsb + P.off_scores);
   float *pool_buf = pooled ? pooled : reinterpret_cast<float *>(wsb + P.off_pooled);
   s = run_score(P, Q, K, scores, wsb, st);
-  if (s == KVSEL_OK) s = run_select(P, scores, pool_buf, idx, st);
-  if (s == KVSEL_OK && any_kept(P)) s = run_gather(P, idx, K, V, K_out, V_out, st);
-  return s;
+  if (s != KVSEL_OK) return s;
+  if (any_kept(P)) return run_select(P, scores, pool_buf, idx, wsb, st, K, V, K_out, V_out);
+  return run_select(P, scores, pool_buf, idx, wsb, st);
 }

@@ -13,8 +13,10 @@ constexpr int kKeyTile = 32;         // keys per score tile (one 32x32 MFMA colu
 constexpr int kRowTile = 32;         // observation rows per row tile
 constexpr int kScoreThreads = 256;   // threads (4 waves) of a score workgroup
 constexpr int kMaxRows = 512;        // observation rows per KV head (G * w'): 16 row tiles, 4 per wave
-constexpr int kSelectThreads = 1024; // threads of the per-segment select workgroup
 constexpr int kMaxPoolKernel = 255;  // widest pool supported
+constexpr int kSelectChunk = 2048;   // positions per pool / select workgroup
+constexpr int kSelectBins = 8192;    // bins of the first radix digit (top 13 bits of an order key)
+constexpr int kMaxChunks = 512;      // chunks per sequence, so L_b <= 2^20
 
 // Per-launch description of the sequences and segments a kernel works on.
 // Travels by value in the kernel arguments, so no device-side tables are
@@ -49,9 +51,18 @@ struct SelectParams {
   const float *scores;
   float *pooled;
   int32_t *idx;
+  uint16_t *tab_fine;    // [nseg][nchunk_max][kSelectBins]: exclusive prefix of each chunk's first-digit histogram
+  uint16_t *tab_coarse;  // [nseg][nchunk_max][kSelectBins / 32]: every 32nd entry of tab_fine
+  uint32_t *bucket;      // [nseg][nchunk_max][kSelectChunk]: each chunk's order keys grouped by first digit
+  int nchunk_max;        // chunks of kSelectChunk positions in the longest sequence
   int Hkv;
-  int pool;         // 0 none, 1 avg, 2 max
-  int pool_kernel;  // odd
+  int pool;              // 0 none, 1 avg, 2 max
+  int pool_kernel;       // odd
+  // Optional K/V compaction fused into the selection (K_out == nullptr: off).
+  const uint4 *K;        // rows of d bf16 = 16 x uint4
+  const uint4 *V;
+  uint4 *K_out;
+  uint4 *V_out;
 };
 
 struct GatherParams {

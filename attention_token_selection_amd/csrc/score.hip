@@ -363,10 +363,10 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreParams p, SegTable t) {
 // Merge of the pass-1 block states of every (sequence, head) into the
 // per-row bias = r + log2(Z) - log2(c_r) that pass 2 subtracts.  A separate
 // launch: the kernel boundary makes every block's partials visible, with no
-// per-workgroup cache write-backs.  Workgroup (row group of 64, segment):
-// four threads share a row, each merging every fourth block with 16 loads
-// in flight; the four shares are combined in a fixed order through LDS.
-constexpr int MERGE_ROWS = 64;
+// per-workgroup cache write-backs.  Workgroup (row group of 16, segment):
+// sixteen threads share a row, each merging every sixteenth block with 16
+// loads in flight; the shares are combined in a fixed order through LDS.
+constexpr int MERGE_ROWS = 16;
 constexpr int MERGE_SPLIT = NT / MERGE_ROWS;
 
 __global__ __launch_bounds__(NT) void merge_kernel(ScoreParams p, SegTable t) {

@@ -1,39 +1,95 @@
-// Pool + top-k of one (sequence, KV head) segment per workgroup.
+// Pool + top-k (+ optionally the K/V compaction) of every (sequence, KV
+// head) segment, in two launches whose workgroups each own one chunk of
+// 2048 positions of one segment, so that every per-position step runs
+// spread over the chip even when a launch holds only a few segments.
 //
-// The segment is processed in pieces of 8192 positions (8 consecutive
-// positions per thread).  For each piece the scores plus a halo of
-// (width-1)/2 on each side are staged into LDS with coalesced loads, and the
-// 1-D pool (odd width, stride 1; avg = zero-padded sum / width, max over
-// in-range positions) is evaluated from LDS.  Pooled values are written out
-// and, for segments up to 8 pieces long, kept in registers for the selection
-// passes; longer segments re-read them from memory.
+// 1. pool_bucket_kernel.  Pools the chunk (odd width, stride 1; avg =
+//    zero-padded window sum / width, max over the in-range positions;
+//    positions outside the sequence read as the pool's neutral value, 0 for
+//    avg and -inf for max, so windows need no bounds logic) and writes it.
+//    Then a counting sort of the chunk by the first radix digit of each
+//    pooled value's order key (its top 13 bits): the exclusive prefix of the
+//    chunk's digit histogram is written out (tab_fine, plus every 32nd entry
+//    in tab_coarse) together with the chunk's keys grouped by digit
+//    (bucket).  No global atomics; nothing needs clearing beforehand.
 //
-// Selection is a three-digit radix select (11 + 11 + 10 bits) on order keys
-// of the fp32 values (monotone: larger value, larger key; -0 ranks as +0).
-// It finds the k-th largest key tau and how many of the keys equal to tau
-// are needed.  Compaction walks the pieces in order; inside a piece each
-// thread owns 8 consecutive positions, and a block-wide exclusive scan of the
-// packed (greater, equal) counts gives each thread its first output slot.  A
-// position is kept if its key is greater than tau, or equal to tau and among
-// the first needed equal ones -- so the lower position wins among equal
-// scores and positions come out ascending (TideKV §5 keeps original
-// positions; the DeferKV guide, Phase 3, sorts the kept indices), without a
-// sort.
+// 2. select_chunk_kernel.  Every workgroup of a segment first finds, from
+//    the tables of all the segment's chunks, the digit b1 whose bin holds
+//    the k-th largest key (a 256-way search over tab_coarse, then over 32
+//    entries of tab_fine).  It loads the keys of bin b1 from every chunk's
+//    bucket (usually a few hundred candidates) and resolves the remaining 19
+//    bits with radix rounds over those candidates alone.  This gives tau,
+//    the k-th largest key, and take_eq, how many keys equal to tau are kept:
+//    the lowest-positioned ones.  Per-chunk counts of kept keys then give
+//    each chunk's first output slot, and the workgroup writes the kept
+//    positions of its own chunk in ascending order (a scan of packed
+//    (greater, equal) counts), so positions come out sorted and the lower
+//    position wins among equal scores (TideKV §5 keeps original positions;
+//    the DeferKV guide, Phase 3, sorts the kept indices).  When K_out is
+//    given it also copies the kept K and V rows to the compact layout
+//    (TideKV §4.1 and §5).
+//
+// Order keys: the fp32 bits mapped so that a larger value has a larger
+// unsigned key (-0 ranks as +0).
 #include "kvsel_internal.h"
 
 namespace kvsel {
 namespace {
 
-constexpr int NT = kSelectThreads;
+constexpr int NT = 256;                  // threads of both kernels
 constexpr int NWAVE = NT / 64;
-constexpr int PER = 8;              // positions per thread per piece
-constexpr int PIECE = NT * PER;     // positions per piece
+constexpr int CH = kSelectChunk;         // positions per chunk (workgroup)
+constexpr int PER = CH / NT;             // positions per thread
+constexpr int NBIN = kSelectBins;        // first-digit bins
+constexpr int DSHIFT = 19;               // first digit = key >> DSHIFT
+constexpr int CSTEP = 32;                // tab_coarse keeps every CSTEP-th prefix entry
+constexpr int NCOARSE = NBIN / CSTEP;    // = NT: one coarse entry per thread
+constexpr int WIN = CSTEP + 1;           // staged prefix entries per chunk in the second search level
+constexpr int MAXC = 4096;               // candidates held in LDS (more: re-read from memory)
+constexpr int MAXCH = kMaxChunks;
 constexpr int HALO = (kMaxPoolKernel - 1) / 2;
+constexpr int HOFF = 128;                // stage index of a chunk's first position (>= HALO, multiple of 4)
+constexpr int FASTR = 4;                 // pools of radius <= FASTR run from a register window
+static_assert(PER == 8, "two 16-byte runs per thread");
+static_assert(NBIN == 1 << (32 - DSHIFT), "first digit width");
+static_assert(NCOARSE == NT, "one coarse entry per thread");
+static_assert(HOFF >= HALO && HOFF % 4 == 0, "stage layout");
+static_assert(MAXCH <= 2 * NT, "chunk scans hold two chunks per thread");
 
 __device__ inline uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// N consecutive values of X from position `first` on (first may be
+// negative), `fill` outside [0, L); 16-byte loads where the run is in range
+// and aligned.
+template <int N>
+__device__ inline void load_run(const float *X, int L, int first, bool vec, float fill, float (&v)[N]) {
+  if (vec && first >= 0 && first + N <= L) {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      const float4 a = *reinterpret_cast<const float4 *>(X + first + 4 * q);
+      v[4 * q] = a.x; v[4 * q + 1] = a.y; v[4 * q + 2] = a.z; v[4 * q + 3] = a.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; ++e) v[e] = (first + e >= 0 && first + e < L) ? X[first + e] : fill;
+  }
+}
+
+template <int N>
+__device__ inline void store_run(float *X, int L, int first, bool vec, const float (&v)[N]) {
+  if (vec && first + N <= L) {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q)
+      *reinterpret_cast<float4 *>(X + first + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+      if (first + e < L) X[first + e] = v[e];
+  }
 }
 
 // Exclusive prefix sum over the workgroup; also returns the total.
@@ -59,212 +115,446 @@ __device__ int block_exscan(int v, int *tmp, int &total) {
   return before + x - v;
 }
 
-// Bin holding the need-th largest element of the histogram, and the number
-// of elements in higher bins.
-__device__ void find_bin(const uint32_t *hist, int nbins, int need, int *tmp, int *s_bin, int *s_above,
-                         int &bin, int &above) {
-  const int per = nbins / NT;
-  const int first = threadIdx.x * per;
-  int c = 0;
-  for (int j = 0; j < per; ++j) c += (int)hist[first + j];
-  int total;
-  const int pre = block_exscan(c, tmp, total);
-  int ab = total - pre - c;
-  for (int j = per - 1; j >= 0; --j) {
-    const int hb = (int)hist[first + j];
-    if (ab < need && ab + hb >= need) {
-      *s_bin = first + j;
-      *s_above = ab;
-    }
-    ab += hb;
-  }
+// Number of threads of the workgroup for which `pred` holds.
+__device__ int block_count(bool pred, int *tmp) {
+  const int n = __popcll(__ballot(pred));
+  if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = n;
   __syncthreads();
-  bin = *s_bin;
-  above = *s_above;
+  int tot = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; ++i) tot += tmp[i];
   __syncthreads();
+  return tot;
 }
 
-// NP > 0: at most NP pieces, pooled values kept in registers.
-// NP == 0: any length, pooled values re-read from memory on each pass.
-template <int NP>
-__global__ __launch_bounds__(NT) void pool_topk_kernel(SelectParams p, SegTable t) {
-  __shared__ float stage[PIECE + 2 * HALO];
-  __shared__ uint32_t hist[2048];
-  __shared__ int tmp[NWAVE];
-  __shared__ int s_bin, s_above;
+struct Segment {
+  const float *S;
+  float *P;
+  int32_t *out;
+  int64_t key0;   // first key row of the sequence
+  int64_t out0;   // first output row of the segment
+  int seg;        // global segment index
+  int h;
+  int L, keff, r;
+  bool is_max, vec_in, vec_out;
+  float fill, width;
+};
 
-  const int h = blockIdx.x;
-  const int sb = blockIdx.y;
+__device__ inline Segment segment_of(const SelectParams &p, const SegTable &t, int h, int sb) {
+  Segment g;
   const int segl = sb * p.Hkv + h;
-  const int64_t key0 = t.key_off[sb];
-  const int L = (int)(t.key_off[sb + 1] - key0);
-  const int64_t base = (int64_t)p.Hkv * key0 + (int64_t)h * L;
-  const float *S = p.scores + base;
-  float *P = p.pooled + base;
-  int32_t *out = p.idx + t.out_off[segl];
-  const int keff = t.keff[segl];
-  const int r = (p.pool == 0) ? 0 : (p.pool_kernel - 1) / 2;
-  const float width = (float)p.pool_kernel;
+  g.key0 = t.key_off[sb];
+  g.seg = t.seg0 + segl;
+  g.h = h;
+  g.L = (int)(t.key_off[sb + 1] - g.key0);
+  const int64_t base = (int64_t)p.Hkv * g.key0 + (int64_t)h * g.L;
+  g.S = p.scores + base;
+  g.P = p.pooled + base;
+  g.out0 = t.out_off[segl];
+  g.out = p.idx + g.out0;
+  g.keff = t.keff[segl];
+  g.r = (p.pool == 0) ? 0 : (p.pool_kernel - 1) / 2;
+  g.is_max = p.pool == 2;
+  // Positions outside the sequence: 0 for the zero-padded average, -inf
+  // (never the maximum: a window always holds its own in-range centre) for max.
+  g.fill = g.is_max ? -INFINITY : 0.0f;
+  g.width = (float)p.pool_kernel;
+  g.vec_in = (reinterpret_cast<uintptr_t>(g.S) & 15u) == 0;
+  g.vec_out = (reinterpret_cast<uintptr_t>(g.P) & 15u) == 0;
+  return g;
+}
+
+__device__ inline int chunk_len(int L, int c) { return min(CH, L - c * CH); }
+
+// ---------------------------------------------------------------- 1. pool + counting sort by first digit
+__global__ __launch_bounds__(NT) void pool_bucket_kernel(SelectParams p, SegTable t) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[NBIN];  // counts, then exclusive prefix
+  __shared__ __attribute__((aligned(16))) float stage[HOFF + CH + HOFF];  // pools wider than 9 only
+  __shared__ int tmp[NWAVE];
+
+  const Segment g = segment_of(p, t, blockIdx.y, blockIdx.z);
+  const int c = blockIdx.x;
+  const int p0 = c * CH;
+  if (p0 >= g.L) return;  // the whole workgroup leaves together
   const int tid = threadIdx.x;
-  const int npieces = (L + PIECE - 1) / PIECE;
+  const int first = p0 + tid * PER;
 
-  constexpr int NR = NP > 0 ? NP : 1;
-  float reg[NR][PER];
+  uint4 *h4 = reinterpret_cast<uint4 *>(hist);
+  for (int i = tid; i < NBIN / 4; i += NT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
 
-  for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
-
-  // ---- pool every piece, write it out, histogram of the top 11 key bits
-  auto pool_piece = [&](int pc, float (&v)[PER]) {
-    const int plo = pc * PIECE;
-    const int span = PIECE + 2 * r;
-    __syncthreads();  // previous piece's stage reads are done
+  float v[PER];
+  if (g.r == 0) {
+    load_run<PER>(g.S, g.L, first, g.vec_in, g.fill, v);
+  } else if (g.r <= FASTR) {
+    float wv[PER + 2 * FASTR];
+    load_run<PER + 2 * FASTR>(g.S, g.L, first - FASTR, g.vec_in, g.fill, wv);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      if (g.is_max) {
+        float m = wv[FASTR + e];
+#pragma unroll
+        for (int j = -FASTR; j <= FASTR; ++j)
+          if (j != 0 && j >= -g.r && j <= g.r) m = fmaxf(m, wv[FASTR + e + j]);
+        v[e] = m;
+      } else {
+        float sum = 0.0f;
+#pragma unroll
+        for (int j = -FASTR; j <= FASTR; ++j)
+          if (j >= -g.r && j <= g.r) sum += wv[FASTR + e + j];
+        v[e] = sum / g.width;
+      }
+    }
+  } else {
+    const int span = CH + 2 * g.r;
     for (int j = tid; j < span; j += NT) {
-      const int gi = plo - r + j;
-      stage[j] = (gi >= 0 && gi < L) ? S[gi] : 0.0f;
+      const int pos = p0 - g.r + j;
+      stage[HOFF - g.r + j] = (pos >= 0 && pos < g.L) ? g.S[pos] : g.fill;
     }
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const int li = tid * PER + e;  // position within the piece
-      const int i = plo + li;
-      float x = 0.0f;
-      if (i < L) {
-        if (r == 0) {
-          x = stage[li];
-        } else if (p.pool == 1) {
-          float s = 0.0f;
-          for (int j = -r; j <= r; ++j) s += stage[li + r + j];  // outside positions are staged as 0
-          x = s / width;
-        } else {
-          const int lo = max(-r, -i), hi = min(r, L - 1 - i);
-          x = stage[li + r + lo];
-          for (int j = lo + 1; j <= hi; ++j) x = fmaxf(x, stage[li + r + j]);
-        }
-        P[i] = x;
-        atomicAdd(&hist[order_key(x) >> 21], 1u);
+      const float *cc = stage + HOFF + tid * PER + e;
+      if (g.is_max) {
+        float m = cc[0];
+        for (int j = -g.r; j <= g.r; ++j) m = fmaxf(m, cc[j]);
+        v[e] = m;
+      } else {
+        float sum = 0.0f;
+        for (int j = -g.r; j <= g.r; ++j) sum += cc[j];
+        v[e] = sum / g.width;
       }
-      v[e] = x;
     }
-  };
+  }
+  store_run<PER>(g.P, g.L, first, g.vec_out, v);
 
-  if constexpr (NP > 0) {
+  // Histogram; the value an atomic returns is the position's rank in its bin.
+  __syncthreads();  // the histogram is cleared
+  uint32_t bin[PER], rank[PER];
 #pragma unroll
-    for (int pc = 0; pc < NP; ++pc)
-      if (pc < npieces) pool_piece(pc, reg[pc]);
-  } else {
-    for (int pc = 0; pc < npieces; ++pc) pool_piece(pc, reg[0]);
+  for (int e = 0; e < PER; ++e) {
+    bin[e] = order_key(v[e]) >> DSHIFT;
+    rank[e] = (first + e < g.L) ? atomicAdd(&hist[bin[e]], 1u) : 0u;
   }
   __syncthreads();
-  if (keff <= 0) return;
-  if (keff >= L) {
-    for (int i = tid; i < L; i += NT) out[i] = i;
-    return;
-  }
 
-  // Visit every valid (position, pooled value) of this thread in piece order.
-  auto for_each = [&](auto &&fn) {
-    if constexpr (NP > 0) {
+  // Exclusive prefix over the bins: thread tid owns bins [32 tid, 32 tid + 32).
+  uint32_t cnt[CSTEP];
 #pragma unroll
-      for (int pc = 0; pc < NP; ++pc) {
-        if (pc < npieces) {
+  for (int q = 0; q < CSTEP / 4; ++q) {
+    const uint4 a = h4[tid * (CSTEP / 4) + q];
+    cnt[4 * q] = a.x; cnt[4 * q + 1] = a.y; cnt[4 * q + 2] = a.z; cnt[4 * q + 3] = a.w;
+  }
+  int own = 0;
 #pragma unroll
-          for (int e = 0; e < PER; ++e) {
-            const int i = pc * PIECE + tid * PER + e;
-            if (i < L) fn(reg[pc][e]);
+  for (int j = 0; j < CSTEP; ++j) own += (int)cnt[j];
+  int total;
+  uint32_t run = (uint32_t)block_exscan(own, tmp, total);  // its barriers also end the reads above
+  uint32_t pre[CSTEP];
+#pragma unroll
+  for (int j = 0; j < CSTEP; ++j) {
+    pre[j] = run;
+    run += cnt[j];
+  }
+#pragma unroll
+  for (int q = 0; q < CSTEP / 4; ++q)
+    h4[tid * (CSTEP / 4) + q] = make_uint4(pre[4 * q], pre[4 * q + 1], pre[4 * q + 2], pre[4 * q + 3]);
+  // Prefixes are at most CH = 2048: 16 bits hold them.
+  const int64_t tab = (int64_t)g.seg * p.nchunk_max + c;
+  uint4 *tf = reinterpret_cast<uint4 *>(p.tab_fine + tab * NBIN + tid * CSTEP);
+#pragma unroll
+  for (int q = 0; q < CSTEP / 8; ++q)
+    tf[q] = make_uint4(pre[8 * q] | (pre[8 * q + 1] << 16), pre[8 * q + 2] | (pre[8 * q + 3] << 16),
+                       pre[8 * q + 4] | (pre[8 * q + 5] << 16), pre[8 * q + 6] | (pre[8 * q + 7] << 16));
+  p.tab_coarse[tab * NCOARSE + tid] = (uint16_t)pre[0];
+  __syncthreads();
+
+  uint32_t *bk = p.bucket + tab * CH;
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    if (first + e < g.L) bk[hist[bin[e]] + rank[e]] = order_key(v[e]);
+}
+
+// ---------------------------------------------------------------- 2. select + compaction per chunk
+template <bool GATHER>
+__global__ __launch_bounds__(NT) void select_chunk_kernel(SelectParams p, SegTable t) {
+  __shared__ uint32_t candk[MAXC];       // keys of bin b1
+  __shared__ uint16_t candc[MAXC];       // their chunks
+  __shared__ uint32_t hist[2048];
+  __shared__ uint16_t win[MAXCH][WIN];   // per chunk: prefix entries 32 t0 .. 32 t0 + 32
+  __shared__ int ch_lo[MAXCH];           // per chunk: start of bin b1 in its bucket
+  __shared__ int ch_cb[MAXCH + 1];       // per chunk: first candidate index
+  __shared__ int ch_above[MAXCH];        // per chunk: keys in bins above b1
+  __shared__ int ch_gt[MAXCH];           // per chunk: candidates above tau
+  __shared__ int ch_eq[MAXCH];           // per chunk: candidates equal to tau
+  __shared__ int ge32[CSTEP];
+  __shared__ uint16_t kept[CH];          // kept chunk-local positions, in output order
+  __shared__ int tmp[NWAVE];
+  __shared__ int sh[4];
+
+  const Segment g = segment_of(p, t, blockIdx.y, blockIdx.z);
+  const int c = blockIdx.x;
+  const int p0 = c * CH;
+  if (p0 >= g.L) return;  // the whole workgroup leaves together
+  if (g.keff <= 0) return;
+  const int tid = threadIdx.x;
+  const int nch = (g.L + CH - 1) / CH;
+  const int n_me = chunk_len(g.L, c);
+  const int first = p0 + tid * PER;
+
+  int base = 0;   // first output slot of this chunk
+  int nkept = 0;  // kept positions of this chunk
+  if (g.keff >= g.L) {
+    base = p0;
+    nkept = n_me;
+    for (int i = tid; i < n_me; i += NT) {
+      g.out[p0 + i] = p0 + i;
+      kept[i] = (uint16_t)i;
+    }
+  } else {
+    // This chunk's pooled values, for the compaction at the end (issued now,
+    // used last).
+    float v[PER];
+    load_run<PER>(g.P, g.L, first, g.vec_out, 0.0f, v);
+
+    const int64_t tab0 = (int64_t)g.seg * p.nchunk_max;
+    const uint16_t *TC = p.tab_coarse + tab0 * NCOARSE;
+    const uint16_t *TF = p.tab_fine + tab0 * NBIN;
+    const uint32_t *BK = p.bucket + tab0 * CH;
+
+    // ---- b1: the largest digit b with ge(b) >= keff, where ge(b) counts
+    // the segment's keys whose digit is >= b (over chunks: length - prefix).
+    int ge1 = 0;  // ge(32 tid)
+    for (int c0 = 0; c0 < nch; c0 += 16) {
+      uint32_t e[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) e[u] = (c0 + u < nch) ? TC[(int64_t)(c0 + u) * NCOARSE + tid] : 0u;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (c0 + u < nch) ge1 += chunk_len(g.L, c0 + u) - (int)e[u];
+    }
+    if (tid == 0) sh[0] = 0;
+    const int t0 = block_count(ge1 >= g.keff, tmp) - 1;  // >= 0 because ge(0) = L > keff
+    if (tid == t0 + 1) sh[0] = ge1;                       // ge(32 (t0 + 1)); 0 past the last bin
+    // Stage prefix entries 32 t0 .. 32 t0 + 32 of every chunk (entry NBIN,
+    // past the last bin, is the chunk's length).
+    for (int f0 = 0; f0 < nch * WIN; f0 += 4 * NT) {
+      uint32_t e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int f = f0 + u * NT + tid;
+        const int cc = f / WIN, jj = f - (f / WIN) * WIN, b = CSTEP * t0 + jj;
+        e[u] = (f < nch * WIN) ? ((b < NBIN) ? TF[(int64_t)cc * NBIN + b] : (uint32_t)chunk_len(g.L, cc)) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int f = f0 + u * NT + tid;
+        if (f < nch * WIN) win[f / WIN][f - (f / WIN) * WIN] = (uint16_t)e[u];
+      }
+    }
+    __syncthreads();
+    const int j = tid >> 3, q = tid & 7;  // bin 32 t0 + j; chunks q, q + 8, ...
+    int ge2 = 0;
+    for (int cc = q; cc < nch; cc += 8) ge2 += chunk_len(g.L, cc) - (int)win[cc][j];
+    ge2 += __shfl_xor(ge2, 1);
+    ge2 += __shfl_xor(ge2, 2);
+    ge2 += __shfl_xor(ge2, 4);
+    if (q == 0) ge32[j] = ge2;
+    const int j1 = block_count(q == 0 && ge2 >= g.keff, tmp) - 1;  // >= 0
+    const int b1 = CSTEP * t0 + j1;
+    const int ge_next = (j1 + 1 < CSTEP) ? ge32[j1 + 1] : sh[0];
+    const int need = g.keff - ge_next;  // keys of bin b1 to keep, >= 1
+    const int m = ge32[j1] - ge_next;   // keys in bin b1, >= need
+
+    // ---- per-chunk extent of bin b1, and candidate offsets
+    for (int cc = tid; cc < nch; cc += NT) {
+      const int lo = win[cc][j1], hi = win[cc][j1 + 1];
+      ch_lo[cc] = lo;
+      ch_above[cc] = chunk_len(g.L, cc) - hi;
+      ch_gt[cc] = 0;
+      ch_eq[cc] = 0;
+      ch_cb[cc] = hi - lo;
+    }
+    __syncthreads();
+    {
+      const int a = (2 * tid < nch) ? ch_cb[2 * tid] : 0;
+      const int b = (2 * tid + 1 < nch) ? ch_cb[2 * tid + 1] : 0;
+      int tot;
+      const int ex = block_exscan(a + b, tmp, tot);
+      if (2 * tid < nch) ch_cb[2 * tid] = ex;
+      if (2 * tid + 1 < nch) ch_cb[2 * tid + 1] = ex + a;
+      if (tid == 0) ch_cb[nch] = tot;  // = m
+    }
+    __syncthreads();
+
+    // Candidate i lives in chunk cc (the largest cc with ch_cb[cc] <= i).
+    auto cand_chunk = [&](int i) {
+      int lo = 0, hi = nch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ch_cb[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      return lo;
+    };
+    auto cand_addr = [&](int i, int cc) { return (int64_t)cc * CH + ch_lo[cc] + (i - ch_cb[cc]); };
+    const bool in_lds = m <= MAXC;
+    if (in_lds) {
+      for (int i0 = 0; i0 < m; i0 += 4 * NT) {
+        uint32_t k[4];
+        int cc[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * NT + tid;
+          cc[u] = (i < m) ? cand_chunk(i) : 0;
+          k[u] = (i < m) ? BK[cand_addr(i, cc[u])] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * NT + tid;
+          if (i < m) {
+            candk[i] = k[u];
+            candc[i] = (uint16_t)cc[u];
           }
         }
       }
-    } else {
-      for (int pc = 0; pc < npieces; ++pc) {
-        float v[PER];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-          const int i = pc * PIECE + tid * PER + e;
-          v[e] = (i < L) ? P[i] : 0.0f;
-        }
-#pragma unroll
-        for (int e = 0; e < PER; ++e)
-          if (pc * PIECE + tid * PER + e < L) fn(v[e]);
-      }
+      __syncthreads();
     }
-  };
+    auto visit = [&](auto &&fn) {
+      for (int i = tid; i < m; i += NT) {
+        if (in_lds) {
+          fn(candk[i], (int)candc[i]);
+        } else {
+          const int cc = cand_chunk(i);
+          fn(BK[cand_addr(i, cc)], cc);
+        }
+      }
+    };
 
-  int need = keff, bin1, bin2, bin3, above;
-  find_bin(hist, 2048, need, tmp, &s_bin, &s_above, bin1, above);
-  need -= above;
+    // ---- radix rounds below b1: bits [8, 19), then [0, 8)
+    int rest = need;
+    uint32_t pre = (uint32_t)b1;
+    for (int hi = DSHIFT, lo = DSHIFT - 11;; hi = lo, lo = 0) {
+      for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
+      __syncthreads();
+      const uint32_t dmask = (1u << (hi - lo)) - 1u;
+      visit([&](uint32_t k, int) {
+        if ((k >> hi) == pre) atomicAdd(&hist[(k >> lo) & dmask], 1u);
+      });
+      __syncthreads();
+      // The bin holding the rest-th largest: thread tid owns bins [8 tid, 8 tid + 8).
+      uint32_t hc[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) hc[u] = hist[8 * tid + u];
+      int own = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) own += (int)hc[u];
+      int tot;
+      const int ex = block_exscan(own, tmp, tot);
+      int ab = tot - ex - own;  // keys in bins above this thread's
+#pragma unroll
+      for (int u = 7; u >= 0; --u) {
+        if (ab < rest && ab + (int)hc[u] >= rest) {
+          sh[1] = 8 * tid + u;
+          sh[2] = ab;
+        }
+        ab += (int)hc[u];
+      }
+      __syncthreads();
+      rest -= sh[2];
+      pre = (pre << (hi - lo)) | (uint32_t)sh[1];
+      __syncthreads();
+      if (lo == 0) break;
+    }
+    const uint32_t tau = pre;
+    const int take_eq = rest;  // keys equal to tau to keep (the lowest-positioned), >= 1
 
-  for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
-  __syncthreads();
-  for_each([&](float x) {
-    const uint32_t k = order_key(x);
-    if ((int)(k >> 21) == bin1) atomicAdd(&hist[(k >> 10) & 2047u], 1u);
-  });
-  __syncthreads();
-  find_bin(hist, 2048, need, tmp, &s_bin, &s_above, bin2, above);
-  need -= above;
+    // ---- per-chunk kept counts, and this chunk's first output slot
+    visit([&](uint32_t k, int cc) {
+      if (k > tau) atomicAdd(&ch_gt[cc], 1);
+      else if (k == tau) atomicAdd(&ch_eq[cc], 1);
+    });
+    __syncthreads();
+    int take_me;  // keys equal to tau that this chunk keeps
+    {
+      const int e0 = (2 * tid < nch) ? ch_eq[2 * tid] : 0;
+      const int e1 = (2 * tid + 1 < nch) ? ch_eq[2 * tid + 1] : 0;
+      int tot;
+      const int ex = block_exscan(e0 + e1, tmp, tot);  // equal keys in earlier chunks
+      const int k0 = min(e0, max(0, take_eq - ex));
+      const int k1 = min(e1, max(0, take_eq - ex - e0));
+      const int s0 = (2 * tid < nch) ? ch_above[2 * tid] + ch_gt[2 * tid] + k0 : 0;
+      const int s1 = (2 * tid + 1 < nch) ? ch_above[2 * tid + 1] + ch_gt[2 * tid + 1] + k1 : 0;
+      const int sx = block_exscan(s0 + s1, tmp, tot);
+      if (2 * tid == c) {
+        sh[1] = sx;
+        sh[3] = k0;
+      }
+      if (2 * tid + 1 == c) {
+        sh[1] = sx + s0;
+        sh[3] = k1;
+      }
+      __syncthreads();
+      base = sh[1];
+      take_me = sh[3];
+    }
 
-  const uint32_t pre22 = ((uint32_t)bin1 << 11) | (uint32_t)bin2;
-  for (int i = tid; i < 1024; i += NT) hist[i] = 0u;
-  __syncthreads();
-  for_each([&](float x) {
-    const uint32_t k = order_key(x);
-    if ((k >> 10) == pre22) atomicAdd(&hist[k & 1023u], 1u);
-  });
-  __syncthreads();
-  find_bin(hist, 1024, need, tmp, &s_bin, &s_above, bin3, above);
-  need -= above;
-
-  const uint32_t tau = (pre22 << 10) | (uint32_t)bin3;
-  const int take_eq = need;  // >= 1 by construction
-
-  // ---- ordered compaction, one piece at a time
-  int g_before = 0, e_before = 0;  // counts in earlier pieces (workgroup-uniform)
-  auto compact_piece = [&](int pc, const float (&v)[PER]) {
-    uint32_t key[PER];
+    // ---- ordered compaction of this chunk
+    uint32_t k[PER];
     int gt = 0, eq = 0;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const int i = pc * PIECE + tid * PER + e;
-      key[e] = (i < L) ? order_key(v[e]) : 0u;
-      gt += (i < L) && key[e] > tau;
-      eq += (i < L) && key[e] == tau;
+      const bool valid = first + e < g.L;
+      k[e] = order_key(v[e]);
+      gt += (valid && k[e] > tau) ? 1 : 0;
+      eq += (valid && k[e] == tau) ? 1 : 0;
     }
-    int total;
-    const int packed = block_exscan((gt << 16) | eq, tmp, total);
-    int gb = g_before + (packed >> 16);
-    int eb = e_before + (packed & 0xffff);
-    int pos = gb + min(eb, take_eq);
+    int tot;
+    const int packed = block_exscan((gt << 16) | eq, tmp, tot);
+    int eb = packed & 0xffff;  // keys equal to tau before this thread's, in this chunk
+    int slot = (packed >> 16) + min(eb, take_me);
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const int i = pc * PIECE + tid * PER + e;
-      if (i >= L) continue;
-      if (key[e] > tau) {
-        if (pos < keff) out[pos] = i;
-        ++pos;
-      } else if (key[e] == tau) {
-        if (eb < take_eq) {
-          if (pos < keff) out[pos] = i;
-          ++pos;
-        }
-        ++eb;
+      const bool valid = first + e < g.L;
+      const bool is_eq = valid && k[e] == tau;
+      const bool keep = (valid && k[e] > tau) || (is_eq && eb < take_me);
+      if (keep && base + slot < g.keff) {  // always true; keeps every store inside the segment
+        g.out[base + slot] = first + e;
+        kept[slot] = (uint16_t)(tid * PER + e);
       }
+      slot += keep ? 1 : 0;
+      eb += is_eq ? 1 : 0;
     }
-    g_before += total >> 16;
-    e_before += total & 0xffff;
-  };
-  if constexpr (NP > 0) {
-#pragma unroll
-    for (int pc = 0; pc < NP; ++pc)
-      if (pc < npieces) compact_piece(pc, reg[pc]);
-  } else {
-    for (int pc = 0; pc < npieces; ++pc) {
-      float v[PER];
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const int i = pc * PIECE + tid * PER + e;
-        v[e] = (i < L) ? P[i] : 0.0f;
+    nkept = min((tot >> 16) + min(tot & 0xffff, take_me), g.keff - base);
+  }
+
+  if constexpr (GATHER) {
+    // Copy the kept rows: 16 lanes move one 256-byte row of K and of V, four
+    // rows per lane group in flight.
+    __syncthreads();
+    const int part = tid & 15;
+    constexpr int GR = NT / 16;  // rows per pass
+    auto src = [&](int rr) {  // rows past the end re-read the last row and are not stored
+      return ((g.key0 + p0 + kept[min(rr, nkept - 1)]) * p.Hkv + g.h) * 16 + part;
+    };
+    auto dst = [&](int rr) { return (g.out0 + base + rr) * 16 + part; };
+    for (int r0 = tid >> 4; r0 < nkept; r0 += 4 * GR) {
+      const int64_t s0 = src(r0), s1 = src(r0 + GR), s2 = src(r0 + 2 * GR), s3 = src(r0 + 3 * GR);
+      const uint4 k0 = p.K[s0], k1 = p.K[s1], k2 = p.K[s2], k3 = p.K[s3];
+      const uint4 v0 = p.V[s0], v1 = p.V[s1], v2 = p.V[s2], v3 = p.V[s3];
+      p.K_out[dst(r0)] = k0;
+      p.V_out[dst(r0)] = v0;
+      if (r0 + GR < nkept) {
+        p.K_out[dst(r0 + GR)] = k1;
+        p.V_out[dst(r0 + GR)] = v1;
       }
-      compact_piece(pc, v);
+      if (r0 + 2 * GR < nkept) {
+        p.K_out[dst(r0 + 2 * GR)] = k2;
+        p.V_out[dst(r0 + 2 * GR)] = v2;
+      }
+      if (r0 + 3 * GR < nkept) {
+        p.K_out[dst(r0 + 3 * GR)] = k3;
+        p.V_out[dst(r0 + 3 * GR)] = v3;
+      }
     }
   }
 }
@@ -274,18 +564,12 @@ __global__ __launch_bounds__(NT) void pool_topk_kernel(SelectParams p, SegTable 
 hipError_t launch_pool_topk(const SelectParams &p, const SegTable &t, hipStream_t s) {
   int64_t lmax = 0;
   for (int i = 0; i < t.nseq; ++i) lmax = std::max<int64_t>(lmax, t.key_off[i + 1] - t.key_off[i]);
-  const int64_t pieces = (lmax + PIECE - 1) / PIECE;
-  const dim3 grid(p.Hkv, t.nseq);
-  if (pieces <= 1)
-    hipLaunchKernelGGL(pool_topk_kernel<1>, grid, dim3(NT), 0, s, p, t);
-  else if (pieces <= 2)
-    hipLaunchKernelGGL(pool_topk_kernel<2>, grid, dim3(NT), 0, s, p, t);
-  else if (pieces <= 4)
-    hipLaunchKernelGGL(pool_topk_kernel<4>, grid, dim3(NT), 0, s, p, t);
-  else if (pieces <= 8)
-    hipLaunchKernelGGL(pool_topk_kernel<8>, grid, dim3(NT), 0, s, p, t);
+  const dim3 grid((unsigned)((lmax + CH - 1) / CH), p.Hkv, t.nseq);
+  hipLaunchKernelGGL(pool_bucket_kernel, grid, dim3(NT), 0, s, p, t);
+  if (p.K_out)
+    hipLaunchKernelGGL(select_chunk_kernel<true>, grid, dim3(NT), 0, s, p, t);
   else
-    hipLaunchKernelGGL(pool_topk_kernel<0>, grid, dim3(NT), 0, s, p, t);
+    hipLaunchKernelGGL(select_chunk_kernel<false>, grid, dim3(NT), 0, s, p, t);
   return hipGetLastError();
 }
 

@@ -53,7 +53,8 @@
  *   KVSEL_EINVAL       bad argument (see each function);
  *   KVSEL_EUNSUPPORTED valid but outside what this build implements
  *                      (d != 128, more than 64 KV heads, more than 512
- *                      observation rows per KV head, device is not gfx950);
+ *                      observation rows per KV head, a sequence longer than
+ *                      2^20 keys, device is not gfx950);
  *   KVSEL_EHIP         a HIP runtime call or kernel launch failed; the HIP
  *                      error text is available from kvsel_last_error().
  * No C++ exception crosses this interface.  NaN or Inf inputs give undefined
