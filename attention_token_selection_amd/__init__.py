@@ -16,5 +16,7 @@ from .kvsel import (  # noqa: F401
     kvsel_gather,
     kvsel_plan,
     kvsel_pool_topk,
+    kvsel_row_stats,
     kvsel_score,
+    kvsel_score_from_stats,
 )

@@ -237,17 +237,34 @@ ScoreParams score_params(const Plan &P, const void *Q, const void *K, float *sco
   return sp;
 }
 
-kvsel_status run_score(const Plan &P, const void *Q, const void *K, float *scores, char *ws, hipStream_t st) {
-  ScoreParams sp = score_params(P, Q, K, scores, ws);
+// Pass 1: per-block row statistics into the workspace.
+kvsel_status run_row_stats(const Plan &P, const void *Q, const void *K, char *ws, hipStream_t st) {
+  ScoreParams sp = score_params(P, Q, K, nullptr, ws);
   return for_each_group(P, [&](const SegTable &t, int64_t lmax) {
     sp.key_block = P.kb1;
     hipError_t e = launch_score_pass1(sp, t, (int)((lmax + P.kb1 - 1) / P.kb1), st);
     if (e != hipSuccess) return hip_fail(e, "score pass 1 launch");
+    return KVSEL_OK;
+  });
+}
+
+// Merge of the block statistics into per-row biases, then pass 2.
+kvsel_status run_from_stats(const Plan &P, const void *Q, const void *K, float *scores, char *ws, hipStream_t st) {
+  ScoreParams sp = score_params(P, Q, K, scores, ws);
+  return for_each_group(P, [&](const SegTable &t, int64_t lmax) {
+    sp.key_block = P.kb1;
+    hipError_t e = launch_score_merge(sp, t, st);
+    if (e != hipSuccess) return hip_fail(e, "row statistics merge launch");
     sp.key_block = P.kb2;
     e = launch_score_pass2(sp, t, (int)((lmax + P.kb2 - 1) / P.kb2), st);
     if (e != hipSuccess) return hip_fail(e, "score pass 2 launch");
     return KVSEL_OK;
   });
+}
+
+kvsel_status run_score(const Plan &P, const void *Q, const void *K, float *scores, char *ws, hipStream_t st) {
+  kvsel_status s = run_row_stats(P, Q, K, ws, st);
+  return s == KVSEL_OK ? run_from_stats(P, Q, K, scores, ws, st) : s;
 }
 
 // Pool + top-k; with K_out given, also the K/V compaction (fused).
@@ -333,6 +350,33 @@ KVSEL_API kvsel_status kvsel_score(const kvsel_problem *p, const void *Q, const 
   if (s == KVSEL_OK) s = check_device();
   if (s != KVSEL_OK) return s;
   return run_score(P, Q, K, scores, static_cast<char *>(ws), reinterpret_cast<hipStream_t>(stream));
+}
+
+KVSEL_API kvsel_status kvsel_row_stats(const kvsel_problem *p, const void *Q, const void *K, void *ws,
+                                       size_t ws_bytes, kvsel_stream_t stream) {
+  g_last_error.clear();
+  Plan P;
+  kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = check_ptr(Q, "Q");
+  if (s == KVSEL_OK) s = check_ptr(K, "K");
+  if (s == KVSEL_OK) s = check_ws(P, ws, ws_bytes);
+  if (s == KVSEL_OK) s = check_device();
+  if (s != KVSEL_OK) return s;
+  return run_row_stats(P, Q, K, static_cast<char *>(ws), reinterpret_cast<hipStream_t>(stream));
+}
+
+KVSEL_API kvsel_status kvsel_score_from_stats(const kvsel_problem *p, const void *Q, const void *K, float *scores,
+                                              void *ws, size_t ws_bytes, kvsel_stream_t stream) {
+  g_last_error.clear();
+  Plan P;
+  kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = check_ptr(Q, "Q");
+  if (s == KVSEL_OK) s = check_ptr(K, "K");
+  if (s == KVSEL_OK) s = check_ptr(scores, "scores");
+  if (s == KVSEL_OK) s = check_ws(P, ws, ws_bytes);
+  if (s == KVSEL_OK) s = check_device();
+  if (s != KVSEL_OK) return s;
+  return run_from_stats(P, Q, K, scores, static_cast<char *>(ws), reinterpret_cast<hipStream_t>(stream));
 }
 
 KVSEL_API kvsel_status kvsel_pool_topk(const kvsel_problem *p, const float *scores, float *pooled, int32_t *idx,

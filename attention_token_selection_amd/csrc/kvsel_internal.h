@@ -75,6 +75,7 @@ struct GatherParams {
 };
 
 hipError_t launch_score_pass1(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s);
+hipError_t launch_score_merge(const ScoreParams &p, const SegTable &t, hipStream_t s);  // key_block = pass 1's
 hipError_t launch_score_pass2(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s);
 hipError_t launch_pool_topk(const SelectParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_gather(const GatherParams &p, const SegTable &t, hipStream_t s);

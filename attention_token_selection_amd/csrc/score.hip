@@ -423,8 +423,10 @@ hipError_t launch_pass(const ScoreParams &p, const SegTable &t, int nblk, hipStr
 }  // namespace
 
 hipError_t launch_score_pass1(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
-  hipError_t e = launch_pass<1>(p, t, nblk, s, 0);
-  if (e != hipSuccess) return e;
+  return launch_pass<1>(p, t, nblk, s, 0);
+}
+
+hipError_t launch_score_merge(const ScoreParams &p, const SegTable &t, hipStream_t s) {
   const dim3 grid((p.Rpad + MERGE_ROWS - 1) / MERGE_ROWS, t.nseq * p.Hkv);
   hipLaunchKernelGGL(merge_kernel, grid, dim3(NT), 0, s, p, t);
   return hipGetLastError();

@@ -61,6 +61,10 @@ _lib.kvsel_plan.restype = ctypes.c_int
 _lib.kvsel_plan.argtypes = [_P, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_int64)]
 _lib.kvsel_score.restype = ctypes.c_int
 _lib.kvsel_score.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.kvsel_row_stats.restype = ctypes.c_int
+_lib.kvsel_row_stats.argtypes = [_P, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.kvsel_score_from_stats.restype = ctypes.c_int
+_lib.kvsel_score_from_stats.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.kvsel_pool_topk.restype = ctypes.c_int
 _lib.kvsel_pool_topk.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.kvsel_gather.restype = ctypes.c_int
@@ -214,6 +218,28 @@ def kvsel_score(problem: Problem, Q, K, scores, ws, stream=None):
             _ptr(scores, "scores", torch.float32, n["scores"], dev), _ptr(ws, "ws", torch.uint8, n["ws"], dev))
     with torch.cuda.device(dev):
         _check(_lib.kvsel_score(problem.ref(), *args, ctypes.c_size_t(ws.numel()), _stream(stream, dev)), "kvsel_score")
+
+
+def kvsel_row_stats(problem: Problem, Q, K, ws, stream=None):
+    torch = _torch()
+    n = _sizes(problem)
+    dev = K.device
+    args = (_ptr(Q, "Q", torch.bfloat16, n["Q"], dev), _ptr(K, "K", torch.bfloat16, n["K"], dev),
+            _ptr(ws, "ws", torch.uint8, n["ws"], dev))
+    with torch.cuda.device(dev):
+        _check(_lib.kvsel_row_stats(problem.ref(), *args, ctypes.c_size_t(ws.numel()), _stream(stream, dev)),
+               "kvsel_row_stats")
+
+
+def kvsel_score_from_stats(problem: Problem, Q, K, scores, ws, stream=None):
+    torch = _torch()
+    n = _sizes(problem)
+    dev = K.device
+    args = (_ptr(Q, "Q", torch.bfloat16, n["Q"], dev), _ptr(K, "K", torch.bfloat16, n["K"], dev),
+            _ptr(scores, "scores", torch.float32, n["scores"], dev), _ptr(ws, "ws", torch.uint8, n["ws"], dev))
+    with torch.cuda.device(dev):
+        _check(_lib.kvsel_score_from_stats(problem.ref(), *args, ctypes.c_size_t(ws.numel()), _stream(stream, dev)),
+               "kvsel_score_from_stats")
 
 
 def kvsel_pool_topk(problem: Problem, scores, pooled, idx, ws, stream=None):

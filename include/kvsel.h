@@ -132,6 +132,23 @@ kvsel_status kvsel_score(const kvsel_problem *p, const void *Q, const void *K, f
                          void *ws, size_t ws_bytes, kvsel_stream_t stream);
 
 /*
+ * The two passes of kvsel_score, for callers that schedule them separately
+ * (and for measuring each).  kvsel_row_stats is TideKV's first pass (§4.2):
+ * for every block of keys it records each observation row's running maximum
+ * and rescaled sum of exponentials in the workspace.  kvsel_score_from_stats
+ * merges those block records into each row's normaliser and runs the second
+ * pass, which recomputes the logits and writes the aggregated scores S into
+ * `scores`.  Calling kvsel_row_stats and then kvsel_score_from_stats on the
+ * same stream, problem, inputs and workspace gives exactly the bytes of
+ * kvsel_score; the workspace must not be used by any other call in between.
+ * Arguments and errors as for kvsel_score (kvsel_row_stats has no `scores`).
+ */
+kvsel_status kvsel_row_stats(const kvsel_problem *p, const void *Q, const void *K, void *ws, size_t ws_bytes,
+                             kvsel_stream_t stream);
+kvsel_status kvsel_score_from_stats(const kvsel_problem *p, const void *Q, const void *K, float *scores,
+                                    void *ws, size_t ws_bytes, kvsel_stream_t stream);
+
+/*
  * Steps 5-6: pool the given scores and select the top-k positions.
  * scores: device fp32 input (layout above); pooled: device fp32 output or
  * NULL (then it is kept in the workspace); idx: device int32 output.

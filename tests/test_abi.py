@@ -16,8 +16,9 @@ kv = pytest.importorskip("attention_token_selection_amd.kvsel")
 
 def test_exports_every_declared_function():
     names = kv.exported_functions()
-    assert set(names) >= {"kvsel_plan", "kvsel_score", "kvsel_pool_topk", "kvsel_gather", "kvsel_compress",
-                          "kvsel_abi_version", "kvsel_status_string", "kvsel_last_error"}
+    assert set(names) >= {"kvsel_plan", "kvsel_score", "kvsel_row_stats", "kvsel_score_from_stats",
+                          "kvsel_pool_topk", "kvsel_gather", "kvsel_compress", "kvsel_abi_version",
+                          "kvsel_status_string", "kvsel_last_error"}
     lib = ctypes.CDLL(kv.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -125,6 +126,9 @@ def test_entry_points_validate_before_device():
     assert lib.kvsel_score(p.ref(), A, A, A, A, ctypes.c_size_t(ws - 1), None) == kv.KVSEL_EINVAL
     assert b"too small" in lib.kvsel_last_error()
     assert lib.kvsel_score(p.ref(), A, A, A, ctypes.c_void_p(a + 16), sz, None) == kv.KVSEL_EINVAL
+    assert lib.kvsel_row_stats(p.ref(), A, None, A, sz, None) == kv.KVSEL_EINVAL
+    assert lib.kvsel_row_stats(p.ref(), A, A, A, ctypes.c_size_t(ws - 1), None) == kv.KVSEL_EINVAL
+    assert lib.kvsel_score_from_stats(p.ref(), A, A, None, A, sz, None) == kv.KVSEL_EINVAL
     assert lib.kvsel_pool_topk(p.ref(), A, None, None, A, sz, None) == kv.KVSEL_EINVAL
     assert lib.kvsel_gather(p.ref(), A, A, None, A, A, None) == kv.KVSEL_EINVAL
     assert lib.kvsel_compress(p.ref(), A, A, A, A, A, None, None, A, sz, None) == kv.KVSEL_EINVAL

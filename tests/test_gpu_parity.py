@@ -155,6 +155,25 @@ def test_entry_points_compose_and_repeat(kv):
     assert torch.equal(full["V_out"][:kept], Vo[:kept])
 
 
+def test_two_passes_equal_score(kv):
+    """kvsel_row_stats then kvsel_score_from_stats gives exactly kvsel_score's bytes."""
+    for i in (3, 5, 11):
+        spec = W.small_cases()[i]
+        case = W.make_case(spec)
+        p = kv.Problem(**W.problem_kwargs(spec))
+        Q, K = (case[x].to(DEV) for x in "QK")
+        ws_bytes, _ = kv.kvsel_plan(p)
+        n = sum(spec.seq_lens) * spec.Hkv
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+        one = torch.empty(n, device=DEV)
+        two = torch.empty(n, device=DEV)
+        kv.kvsel_score(p, Q, K, one, ws)
+        kv.kvsel_row_stats(p, Q, K, ws)
+        kv.kvsel_score_from_stats(p, Q, K, two, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(one, two), spec.name
+
+
 def test_workspace_shared_across_problems(kv):
     """One workspace serves several different problems in a row."""
     cases = [W.small_cases()[i] for i in (6, 7, 11, 6)]
