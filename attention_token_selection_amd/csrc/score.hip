@@ -2,12 +2,14 @@
 // (TideKV, "Delayed KV Eviction via Layer-Wise Chunked Prefill", §4.2).
 //
 // Work unit: one workgroup of four waves per (key block, KV head, sequence).
-// The block's keys are streamed in tiles of 32 keys (8 KiB of K).  Every
-// thread prefetches its share of the next PD tiles into registers with
-// coalesced 16-byte loads; a tile is then written to one of two LDS slots in
-// a swizzled layout (16-byte chunk c of key r lands in position c ^ (r & 15)
-// of the row, so the MFMA operand reads below are free of bank conflicts),
-// and after one barrier all four waves read it.  The observation rows
+// The block's keys are streamed in tiles of 32 keys (8 KiB of K), loaded
+// straight from memory into a ring of four LDS slots (global_load_lds, 16
+// bytes per lane, each wave a quarter of the tile) three tiles ahead of the
+// one being consumed.  The lanes' source chunks are chosen so that a slot
+// holds the tile in a swizzled layout (16-byte chunk c of key r sits at
+// position c ^ (r & 15) of the row), which makes the MFMA operand reads
+// below free of bank conflicts; one barrier per tile lets all four waves
+// read it.  The observation rows
 // (R = G * w' per KV head, row = window row * G + query head of the group)
 // are split into row tiles of 32; wave v owns row tiles v, v+4, v+8, v+12
 // and keeps their query fragments in registers for the whole block.
@@ -43,10 +45,11 @@ constexpr int NW = NT / 64;
 constexpr int KT = kKeyTile;             // 32 keys per tile
 constexpr int ROWB = kHeadDim * 2;       // 256 bytes per key row
 constexpr int TILE_BYTES = KT * ROWB;    // 8 KiB
-constexpr int TILE_CHUNKS = TILE_BYTES / 16;
-constexpr int LPT = TILE_CHUNKS / NT;    // 16-byte chunks each thread moves per tile
-static_assert(LPT == 2, "TileRegs holds two chunks");
-constexpr int PD = 4;                    // tiles in flight per workgroup (four named buffers below)
+static_assert(TILE_BYTES == 2 * 16 * NT, "each thread moves two 16-byte chunks per tile");
+constexpr int PD = 4;                    // LDS ring slots; tiles in flight = PD - 1
+// s_waitcnt immediate for vmcnt(2 (PD - 2)) with the other counters left alone.
+constexpr int kWaitTile = 0x3F70 | (2 * (PD - 2));
+static_assert(PD == 4 && 2 * (PD - 2) < 16, "four named slots; vmcnt fits the low field");
 constexpr float kZLimit = 0x1p100f;      // a lane's running sum stays below this
 
 __device__ inline bf16x8 as_frag(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -64,27 +67,23 @@ __device__ inline void lse_merge(float &r, float &z, float r2, float z2) {
   z = a + b;
 }
 
-// A thread's two 16-byte chunks of a tile (plain values, so they stay in
-// registers).  Chunk q of a tile (q = thread, thread + 256) holds 16-byte
-// chunk (q & 15) ^ (row & 15) of key row = q >> 4: the swizzled LDS layout.
-struct TileRegs {
-  uint4 a, b;
-};
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
-// Loads of key tile i0 .. i0+31 from `kt` = the tile's first key row of this
-// head.  Rows past `rmax` (last key of the block minus i0, wave-uniform) are
-// clamped to it, so every load is in bounds and a tile past the end of the
-// block re-reads one cached row; such keys are masked or never consumed.
-__device__ inline TileRegs load_tile(const uint16_t *kt, int rmax, int rowstride, int ra, int ca, int cb) {
-  TileRegs t;
-  t.a = *reinterpret_cast<const uint4 *>(kt + (min(ra, rmax) * rowstride + ca));
-  t.b = *reinterpret_cast<const uint4 *>(kt + (min(ra + 16, rmax) * rowstride + cb));
-  return t;
-}
-
-__device__ inline void store_tile(char *slot, const TileRegs &v) {
-  *reinterpret_cast<uint4 *>(slot + threadIdx.x * 16) = v.a;
-  *reinterpret_cast<uint4 *>(slot + (threadIdx.x + NT) * 16) = v.b;
+// Issues this wave's share of key tile i0 .. i0+31 (`kt` = its first key row
+// of this head) straight into the LDS slot: 16-byte position P = 128 * wave
+// + 64 * i + lane (i = 0, 1) of the slot receives chunk (P & 15) ^ (row & 15)
+// of key row = P >> 4, which leaves the slot in the swizzled layout.  Rows
+// past `rmax` (the block's last key minus i0) re-read that key, so every
+// load is in bounds; such keys are masked or never consumed.
+__device__ inline void issue_tile(char *slot, const uint16_t *kt, int rmax, int rowstride, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int P = 128 * wave + 64 * i + lane;
+    const int row = P >> 4;
+    const uint16_t *src = kt + (int64_t)min(row, rmax) * rowstride + (((P & 15) ^ (row & 15)) * 8);
+    __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)(slot + (128 * wave + 64 * i) * 16), 16, 0, 0);
+  }
 }
 
 // Row bookkeeping: observation row index -> causal limit (last visible key).
@@ -118,8 +117,13 @@ __device__ inline float sum16(const float (&e)[16]) {
 
 // RT: row tiles (of 32 rows) per wave.
 template <int PASS, int RT>
-__global__ __launch_bounds__(NT) void score_kernel(ScoreParams p, SegTable t) {
-  __shared__ __attribute__((aligned(16))) char tiles[2][TILE_BYTES];
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 4 : 1))) void score_kernel(ScoreParams p, SegTable t) {
+  // The LDS ring: one array per slot, so that the compiler can tell a
+  // slot being read from the slots that loads are landing in.
+  __shared__ __attribute__((aligned(16))) char tile0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char tile1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char tile2[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char tile3[TILE_BYTES];
   extern __shared__ float red[];  // pass 2: [NW][key_block] partial sums
 
   const int blk = blockIdx.x;
@@ -185,62 +189,50 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreParams p, SegTable t) {
   const int rowstride = p.Hkv * kHeadDim;  // elements between consecutive keys of one head
   const uint16_t *kblk = p.K + (key0 + kb0) * (int64_t)rowstride + (int64_t)h * kHeadDim;
   const int last = kb1 - 1 - kb0;  // block-relative index of the block's last key
-  // This thread's load slots: rows ra and ra + 16, chunk offsets (elements).
-  const int ra = threadIdx.x >> 4;
-  const int ca = (((threadIdx.x & 15) ^ (ra & 15)) * 8);
-  const int cb = ca;  // row ra + 16 has the same low four bits
   // LDS byte offset of this lane's operand chunk for k-step j: row lr, chunk 2j + hf, swizzled.
   const int rd_base = lr * ROWB;
   const int sw = lr & 15;
 
-  // Loads are issued unconditionally (past the block they re-read its last
-  // row), so every wait below is for exactly the buffer about to be used.
-  // The scheduling barriers keep the four prologue loads in tile order, the
-  // order in which the loop consumes them.
+  // Tiles go straight from memory into a ring of PD = 4 LDS slots, three
+  // tiles ahead of the one being consumed.  Every step issues exactly two
+  // loads per wave (past the block they re-read its last key), so before
+  // step t this wave has tiles t .. t + 2 in flight, and waiting until at
+  // most 2 (PD - 2) loads remain means tile t has landed.
   auto tile_src = [&](int ti) { return kblk + (int64_t)(ti * KT) * rowstride; };
-  TileRegs pf0 = load_tile(tile_src(0), last - 0 * KT, rowstride, ra, ca, cb);
-  __builtin_amdgcn_sched_barrier(0);
-  TileRegs pf1 = load_tile(tile_src(1), last - 1 * KT, rowstride, ra, ca, cb);
-  __builtin_amdgcn_sched_barrier(0);
-  TileRegs pf2 = load_tile(tile_src(2), last - 2 * KT, rowstride, ra, ca, cb);
-  __builtin_amdgcn_sched_barrier(0);
-  TileRegs pf3 = load_tile(tile_src(3), last - 3 * KT, rowstride, ra, ca, cb);
-  __builtin_amdgcn_sched_barrier(0);
+  issue_tile(tile0, tile_src(0), last, rowstride, wave, lane);
+  issue_tile(tile1, tile_src(1), last - KT, rowstride, wave, lane);
+  issue_tile(tile2, tile_src(2), last - 2 * KT, rowstride, wave, lane);
 
-  // Consumes tile ti from `buf` and returns the registers refilled with
-  // tile ti + PD.
-  auto step = [&](TileRegs buf, const int ti) -> TileRegs {
-    char *slot = tiles[ti & 1];
-    store_tile(slot, buf);
-    buf = load_tile(tile_src(ti + PD), last - (ti + PD) * KT, rowstride, ra, ca, cb);
-    __syncthreads();
-    if (ti >= ntile) return buf;  // padding step of the last group of four
+  // Consumes tile ti from `cur` after refilling `nxt` (the slot of tile
+  // ti - 1) with tile ti + 3.
+  auto step = [&](const int ti, const char *cur, char *nxt) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(kWaitTile);  // this wave's part of tile ti is in LDS
+    __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): this wave's reads of tile ti - 1 are done
+    __builtin_amdgcn_s_barrier();           // every wave's part has landed; nxt is free
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    issue_tile(nxt, tile_src(ti + 3), last - (ti + 3) * KT, rowstride, wave, lane);
+    if (ti >= ntile) return;  // padding step of the last group of four
+    const char *slot = cur;
     const int i0 = kb0 + ti * KT;
     if (my_rt == 0) {  // this wave owns no rows (fewer than four row tiles in all)
       if constexpr (PASS == 2)
         if (hf == 0) red[wave * p.key_block + ti * KT + lr] = 0.0f;
-      return buf;
+      return;
     }
 
-    // All eight K fragments of the tile go to distinct registers before the
-    // first MFMA: no LDS read may land in a register that a queued MFMA has
-    // yet to read (a later fragment would otherwise reuse the registers of
-    // an earlier one while the matrix pipe still holds that MFMA).
-    bf16x8 kf[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      kf[j] = as_frag(*reinterpret_cast<const uint4 *>(slot + rd_base + (((2 * j + hf) ^ sw) << 4)));
     f32x16 acc[RT];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
+      const bf16x8 kf = as_frag(*reinterpret_cast<const uint4 *>(slot + rd_base + (((2 * j + hf) ^ sw) << 4)));
 #pragma unroll
       for (int k = 0; k < RT; ++k) {
         if (k < my_rt) {
           const f32x16 c = (j == 0) ? f32x16{} : acc[k];
           if constexpr (PASS == 1)
-            acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[k][j], c, 0, 0, 0);
+            acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[k][j], c, 0, 0, 0);
           else
-            acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[k][j], kf[j], c, 0, 0, 0);
+            acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[k][j], kf, c, 0, 0, 0);
         }
       }
     }
@@ -319,19 +311,15 @@ __global__ __launch_bounds__(NT) void score_kernel(ScoreParams p, SegTable t) {
       s = sum_halves(s);
       if (hf == 0) red[wave * p.key_block + ti * KT + lr] = s;
     }
-    return buf;
   };
-
-  // Whole groups of four steps, no early exit: every path into the loop
-  // head has issued the same loads in the same order, so each wait is exact.
   for (int t0 = 0; t0 < ntile; t0 += PD) {
-    pf0 = step(pf0, t0);
-    pf1 = step(pf1, t0 + 1);
-    pf2 = step(pf2, t0 + 2);
-    pf3 = step(pf3, t0 + 3);
+    step(t0, tile0, tile3);
+    step(t0 + 1, tile1, tile0);
+    step(t0 + 2, tile2, tile1);
+    step(t0 + 3, tile3, tile2);
   }
-  // The last group issued loads for tiles past the block that nobody
-  // consumes; drain them so no load is still in flight when the wave ends.
+  // The last steps issued loads for tiles past the block that nobody
+  // consumes; they write LDS, so drain them before the workgroup can end.
   __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0)
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
