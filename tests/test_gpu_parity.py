@@ -117,6 +117,19 @@ def test_config_parity(kv, i):
     assert st["segments"] == len(SAMPLED[i])
 
 
+@pytest.mark.parametrize("pool,width", [("max", 11), ("avg", 255)])
+def test_wide_pool_end_to_end(kv, pool, width):
+    """Pools wider than 9 positions take the LDS path of the pool kernel."""
+    spec = W.Spec(f"wide_{pool}{width}", [3000, 513], Hq=8, Hkv=2, w=16, pool=pool, pool_kernel=width, k=200,
+                  recipe="plant", plant_frac=0.02)
+    _say(f"wide pool {spec.name}")
+    case = W.make_case(spec)
+    _, out, scores = _run(kv, spec, case)
+    ref = _oracle(spec, case)
+    st = check_against_oracle(spec, case, out, ref, scores=scores)
+    assert st["segments"] == spec.batch * spec.Hkv
+
+
 def test_config2_last_layer(kv):
     spec = W.config(2)
     case = W.make_case(spec, layer=31, device=DEV)
@@ -209,7 +222,7 @@ def _adversarial_scores(kind, L, rng):
 
 
 @pytest.mark.parametrize("kind", ["integer", "all_equal", "two_values", "sorted", "reverse", "tiny_and_zero", "spread"])
-@pytest.mark.parametrize("pool,kernel", [("none", 1), ("max", 7), ("avg", 5)])
+@pytest.mark.parametrize("pool,kernel", [("none", 1), ("max", 7), ("avg", 5), ("max", 11), ("avg", 255)])
 def test_select_exact_on_given_scores(kv, kind, pool, kernel):
     rng = np.random.default_rng(zlib.crc32(f"{kind}/{pool}".encode()))
     lens = [1, 7, 1000, 4099, 70000]
@@ -233,7 +246,9 @@ def test_select_exact_on_given_scores(kv, kind, pool, kernel):
         elif pool == "max":
             np.testing.assert_array_equal(P[soff:soff + L], O.pool1d(seg.astype(np.float64), "max", kernel))
         else:
-            check_scores(P[soff:soff + L], O.pool1d(seg.astype(np.float64), "avg", kernel), rtol=1e-6)
+            # fp32 window sums of up to 255 terms: allow their rounding
+            check_scores(P[soff:soff + L], O.pool1d(seg.astype(np.float64), "avg", kernel),
+                         rtol=1e-6 if kernel <= 9 else 2e-5)
         check_select_exact(I[ooff:ooff + keff], P[soff:soff + L], keff)
 
 
