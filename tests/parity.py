@@ -36,7 +36,9 @@ def check_scores(gpu, ref, what="scores", rtol=RTOL):
         i = bad[0]
         raise AssertionError(f"{what}: {len(bad)} positions beyond {rtol:g} relative; first at {i}: "
                              f"gpu={gpu[i]!r} ref={ref[i]!r}")
-    rel = err / np.maximum(ref, floor)
+    denom = np.maximum(ref, floor)
+    # an all-zero reference segment has no scale: exact zeros count as 0 error
+    rel = np.where(denom > 0, err / np.where(denom > 0, denom, 1.0), np.where(err > 0, np.inf, 0.0))
     return {"max_rel": float(rel.max()) if len(rel) else 0.0,
             "beyond_diag": int((rel > DIAG_RTOL).sum())}
 
