@@ -27,7 +27,9 @@
 //    position wins among equal scores (TideKV §5 keeps original positions;
 //    the DeferKV guide, Phase 3, sorts the kept indices).  When K_out is
 //    given it also copies the kept K and V rows to the compact layout
-//    (TideKV §4.1 and §5).
+//    (TideKV §4.1 and §5); then two workgroups share each chunk, each
+//    copying half of its rows, so the copy is spread over twice as many
+//    compute units.
 //
 // Order keys: the fp32 bits mapped so that a larger value has a larger
 // unsigned key (-0 ranks as +0).
@@ -292,7 +294,10 @@ __global__ __launch_bounds__(NT) void select_chunk_kernel(SelectParams p, SegTab
   __shared__ int sh[4];
 
   const Segment g = segment_of(p, t, blockIdx.y, blockIdx.z);
-  const int c = blockIdx.x;
+  // With the gather, two workgroups share a chunk: both select (the same
+  // result), the first writes the indices, and each copies half the rows.
+  const int c = GATHER ? (blockIdx.x >> 1) : blockIdx.x;
+  const int half = GATHER ? (blockIdx.x & 1) : 0;
   const int p0 = c * CH;
   if (p0 >= g.L) return;  // the whole workgroup leaves together
   if (g.keff <= 0) return;
@@ -307,7 +312,7 @@ __global__ __launch_bounds__(NT) void select_chunk_kernel(SelectParams p, SegTab
     base = p0;
     nkept = n_me;
     for (int i = tid; i < n_me; i += NT) {
-      g.out[p0 + i] = p0 + i;
+      if (half == 0) g.out[p0 + i] = p0 + i;
       kept[i] = (uint16_t)i;
     }
   } else {
@@ -518,7 +523,7 @@ __global__ __launch_bounds__(NT) void select_chunk_kernel(SelectParams p, SegTab
       const bool is_eq = valid && k[e] == tau;
       const bool keep = (valid && k[e] > tau) || (is_eq && eb < take_me);
       if (keep && base + slot < g.keff) {  // always true; keeps every store inside the segment
-        g.out[base + slot] = first + e;
+        if (half == 0) g.out[base + slot] = first + e;
         kept[slot] = (uint16_t)(tid * PER + e);
       }
       slot += keep ? 1 : 0;
@@ -528,33 +533,29 @@ __global__ __launch_bounds__(NT) void select_chunk_kernel(SelectParams p, SegTab
   }
 
   if constexpr (GATHER) {
-    // Copy the kept rows: 16 lanes move one 256-byte row of K and of V, four
-    // rows per lane group in flight.
+    // Copy this workgroup's half of the kept rows (rows 2 r + half): 16
+    // lanes move one 256-byte row of K and of V, four rows per lane group in
+    // flight.  Rows past the end repeat the last row (the same bytes to the
+    // same place), so every load and store is unconditional.
     __syncthreads();
     const int part = tid & 15;
-    constexpr int GR = NT / 16;  // rows per pass
-    auto src = [&](int rr) {  // rows past the end re-read the last row and are not stored
-      return ((g.key0 + p0 + kept[min(rr, nkept - 1)]) * p.Hkv + g.h) * 16 + part;
-    };
-    auto dst = [&](int rr) { return (g.out0 + base + rr) * 16 + part; };
-    for (int r0 = tid >> 4; r0 < nkept; r0 += 4 * GR) {
+    const int nmine = (nkept - half + 1) / 2;  // rows 2 r + half, r < nmine
+    constexpr int GR = NT / 16;                // lane groups
+    auto row_of = [&](int r) { return 2 * min(r, nmine - 1) + half; };
+    auto src = [&](int r) { return ((g.key0 + p0 + kept[row_of(r)]) * p.Hkv + g.h) * 16 + part; };
+    auto dst = [&](int r) { return (g.out0 + base + row_of(r)) * 16 + part; };
+    for (int r0 = tid >> 4; r0 < nmine; r0 += 4 * GR) {
       const int64_t s0 = src(r0), s1 = src(r0 + GR), s2 = src(r0 + 2 * GR), s3 = src(r0 + 3 * GR);
       const uint4 k0 = p.K[s0], k1 = p.K[s1], k2 = p.K[s2], k3 = p.K[s3];
       const uint4 v0 = p.V[s0], v1 = p.V[s1], v2 = p.V[s2], v3 = p.V[s3];
       p.K_out[dst(r0)] = k0;
       p.V_out[dst(r0)] = v0;
-      if (r0 + GR < nkept) {
-        p.K_out[dst(r0 + GR)] = k1;
-        p.V_out[dst(r0 + GR)] = v1;
-      }
-      if (r0 + 2 * GR < nkept) {
-        p.K_out[dst(r0 + 2 * GR)] = k2;
-        p.V_out[dst(r0 + 2 * GR)] = v2;
-      }
-      if (r0 + 3 * GR < nkept) {
-        p.K_out[dst(r0 + 3 * GR)] = k3;
-        p.V_out[dst(r0 + 3 * GR)] = v3;
-      }
+      p.K_out[dst(r0 + GR)] = k1;
+      p.V_out[dst(r0 + GR)] = v1;
+      p.K_out[dst(r0 + 2 * GR)] = k2;
+      p.V_out[dst(r0 + 2 * GR)] = v2;
+      p.K_out[dst(r0 + 3 * GR)] = k3;
+      p.V_out[dst(r0 + 3 * GR)] = v3;
     }
   }
 }
@@ -567,7 +568,7 @@ hipError_t launch_pool_topk(const SelectParams &p, const SegTable &t, hipStream_
   const dim3 grid((unsigned)((lmax + CH - 1) / CH), p.Hkv, t.nseq);
   hipLaunchKernelGGL(pool_bucket_kernel, grid, dim3(NT), 0, s, p, t);
   if (p.K_out)
-    hipLaunchKernelGGL(select_chunk_kernel<true>, grid, dim3(NT), 0, s, p, t);
+    hipLaunchKernelGGL(select_chunk_kernel<true>, dim3(2 * grid.x, grid.y, grid.z), dim3(NT), 0, s, p, t);
   else
     hipLaunchKernelGGL(select_chunk_kernel<false>, grid, dim3(NT), 0, s, p, t);
   return hipGetLastError();
