@@ -28,13 +28,19 @@ What it computes (one sequence ``b`` and one KV head ``h`` at a time):
    scores aggregated at KV-head granularity) and over the window rows.  Row
    weights ``c_r = 1`` without a decode row; with one, ``1 - alpha`` for the
    prompt rows and ``alpha`` for the decode row (the DeferKV guide's
-   prompt-vs-decode weighting, in its two-level form).
+   prompt-vs-decode weighting, in its two-level form).  Optionally the
+   guide's exponential temporal weights instead: ``c_r`` proportional to
+   ``exp(lambda * r)`` over relative row positions ``r = -w+1 .. 0`` (and ``1``
+   for the decode row), normalised to sum to 1.
 6. 1-D pool of odd width ``K`` and stride 1 (no page defines it; reading:
    ``avg`` = zero-padded window sum divided by ``K``, ``max`` = max over the
    in-range positions only).
 7. Top-k: order positions by (descending score, ascending index) and keep the
    first ``min(k, L)``; return them in ascending position order (the DeferKV
    guide sorts the kept indices; TideKV keeps original positions, §5).
+   Optionally the guide's reserved positions (Phase 3): the first ``sink`` and
+   the last ``recent`` positions are kept before any other, lowest position
+   first, and the rest of the budget goes to the highest scores.
 8. Gather: the kept rows of K and V, copied exactly (TideKV §4.2 and §5).
 
 Query-head ``g`` belongs to KV head ``g // G`` with ``G = Hq // Hkv``
@@ -55,6 +61,8 @@ __all__ = [
     "observation_positions",
     "visible_mask",
     "row_weights",
+    "temporal_row_weights",
+    "protected_mask",
     "row_probabilities",
     "head_scores",
     "pool1d",
@@ -114,6 +122,33 @@ def row_weights(w: int, has_decode: bool, alpha: float) -> np.ndarray:
     return c
 
 
+def temporal_row_weights(w: int, has_decode: bool, lam: float) -> np.ndarray:
+    """Exponential temporal weights of the observation rows (DeferKV guide,
+    Phase 2, temporal weighting).
+
+    Row ``j`` of the prompt window (position ``L - w + j``) has relative
+    position ``r = j - (w - 1)``, from ``-w + 1`` up to ``0``; the decode row has
+    ``r = 1``.  ``c_r = exp(lam * r) / sum over the rows of exp(lam * r')``, so
+    the weights sum to 1 and the latest row weighs most.
+    """
+    r = np.arange(w, dtype=np.float64) - (w - 1)
+    if has_decode:
+        r = np.append(r, 1.0)
+    e = np.exp(lam * (r - r.max()))
+    return e / e.sum()
+
+
+def protected_mask(L: int, sink: int, recent: int) -> np.ndarray:
+    """Positions kept whatever their score (DeferKV guide, Phase 3): the first
+    ``sink`` prefix positions (attention sinks) and the last ``recent`` ones
+    (the recent window)."""
+    keep = np.zeros(L, dtype=bool)
+    keep[:max(0, min(int(sink), L))] = True
+    if recent > 0:
+        keep[max(0, L - int(recent)):] = True
+    return keep
+
+
 def row_probabilities(q_rows: np.ndarray, K_h: np.ndarray, vis: np.ndarray, scale: float) -> np.ndarray:
     """Softmax attention probabilities of each observation row over the prefix.
 
@@ -130,19 +165,25 @@ def row_probabilities(q_rows: np.ndarray, K_h: np.ndarray, vis: np.ndarray, scal
 
 
 def head_scores(Q_b: np.ndarray, K_b: np.ndarray, h: int, Hkv: int, *, w: int, has_decode: bool,
-                alpha: float, causal: bool, scale: float) -> np.ndarray:
+                alpha: float, causal: bool, scale: float, weighting: str = "alpha", lam: float = 0.0) -> np.ndarray:
     """Aggregated importance ``S[i]`` of one (sequence, KV head).
 
     ``Q_b`` [w', Hq, d] observation queries of the sequence (decode row last),
     ``K_b`` [L, Hkv, d] its keys.  Sums ``c_r * P`` over the window rows and the
-    ``G`` query heads of group ``h``.
+    ``G`` query heads of group ``h``; ``c_r`` from ``row_weights`` (weighting
+    "alpha") or ``temporal_row_weights`` (weighting "exp").
     """
     L = K_b.shape[0]
     Hq = Q_b.shape[1]
     G = Hq // Hkv
     pos = observation_positions(L, w, has_decode)
     vis = visible_mask(pos, L, causal)
-    c = row_weights(w, has_decode, alpha)
+    if weighting == "alpha":
+        c = row_weights(w, has_decode, alpha)
+    elif weighting == "exp":
+        c = temporal_row_weights(w, has_decode, lam)
+    else:
+        raise ValueError(f"unknown weighting {weighting!r}")
     K_h = K_b[:, h, :]
     S = np.zeros(L, dtype=np.float64)
     for gi in range(G):
@@ -178,15 +219,22 @@ def pool1d(S: np.ndarray, kind: str, kernel: int) -> np.ndarray:
     return out
 
 
-def select_topk(P: np.ndarray, k: int) -> np.ndarray:
+def select_topk(P: np.ndarray, k: int, protected=None) -> np.ndarray:
     """Positions of the ``min(k, L)`` largest values, ascending.
 
     Ordering is by descending value, then ascending position, so among equal
-    values the lower position is kept.
+    values the lower position is kept.  Positions flagged in ``protected``
+    (a boolean mask) come before every other position, in ascending order
+    among themselves, so they are kept first and the rest of the budget goes
+    to the highest-scoring others (the DeferKV guide's reserved sinks and
+    recent window, Phase 3).
     """
     L = P.shape[0]
     keff = max(0, min(int(k), L))
-    order = np.lexsort((np.arange(L), -P))  # primary key: -P, secondary: position
+    prot = np.zeros(L, dtype=bool) if protected is None else np.asarray(protected, dtype=bool)
+    # lexsort: the last key is primary -- protected first, then -P (only for
+    # the unprotected), then position
+    order = np.lexsort((np.arange(L), np.where(prot, 0.0, -P), ~prot))
     return np.sort(order[:keff]).astype(np.int64)
 
 
@@ -268,7 +316,8 @@ def plan_offsets(seq_lens, Hkv: int, budgets) -> np.ndarray:
 
 def compress(Q, K, V, *, seq_lens, Hq: int, Hkv: int, w: int, has_decode: bool = False,
              alpha: float = 0.0, causal: bool = True, scale=None, pool: str = "none",
-             pool_kernel: int = 1, k=None, budgets=None, heads=None):
+             pool_kernel: int = 1, k=None, budgets=None, heads=None, weighting: str = "alpha",
+             lam: float = 0.0, sink: int = 0, recent: int = 0):
     """Whole path for a packed batch.
 
     ``Q`` [B, w', Hq, d]; ``K``, ``V`` [sum L_b, Hkv, d] (sequences packed
@@ -301,9 +350,9 @@ def compress(Q, K, V, *, seq_lens, Hq: int, Hkv: int, w: int, has_decode: bool =
             if want is not None and (b, h) not in want:
                 continue
             S = head_scores(Q[b], K_b, h, Hkv, w=w, has_decode=has_decode, alpha=alpha,
-                            causal=causal, scale=scale)
+                            causal=causal, scale=scale, weighting=weighting, lam=lam)
             P = pool1d(S, pool, pool_kernel)
-            idx = select_topk(P, budgets[b][h])
+            idx = select_topk(P, budgets[b][h], protected_mask(len(S), sink, recent))
             res[(b, h)] = {
                 "scores": S,
                 "pooled": P,

@@ -332,6 +332,65 @@ def test_rejects_nonfinite():
         O.compress(np.zeros((1, 1, 1, 8)), K, K, seq_lens=[4], Hq=1, Hkv=1, w=1, k=1)
 
 
+# ---------------------------------------------------------------- DeferKV variant: temporal weights, reserved positions
+def test_temporal_weights_closed_form():
+    # w = 2 prompt rows and a decode row, lambda = ln 2: relative positions -1, 0, 1 weigh 1 : 2 : 4
+    np.testing.assert_allclose(O.temporal_row_weights(2, True, np.log(2.0)), [1 / 7, 2 / 7, 4 / 7], rtol=1e-14)
+    np.testing.assert_allclose(O.temporal_row_weights(5, False, 0.0), np.full(5, 0.2), rtol=1e-14)
+    c = O.temporal_row_weights(32, True, 0.1)
+    assert abs(c.sum() - 1.0) < 1e-14
+    np.testing.assert_allclose(c[1:] / c[:-1], np.exp(0.1), rtol=1e-12)
+
+
+def test_temporal_weights_applied_to_rows():
+    """Hand keys; prompt row q=+1 at position 7 and decode row q=-1 with
+    lambda = ln 3: weights 1/4 and 3/4 of the two rows' probabilities, whose
+    values are those of the 8-token worked examples."""
+    j = _hand()
+    a, b, c = 0.328455, 0.044452, 0.120832  # P of the row q=+1 at position 7
+    p_plus = np.array([a, b, b, c, b, b, b, a])
+    s_ex3 = np.array([0.352457, 0.221802, 0.221802, 0.186076, 0.221802, 0.221802, 0.221802, 0.352457])
+    p_minus = s_ex3 - p_plus  # the row q=-1 (the two rows of the G=2 example sum to s_ex3)
+    keys = j["keys_c0"]
+    K = np.zeros((8, 1, 128))
+    K[:, 0, 0] = keys
+    Q = np.zeros((2, 1, 128))
+    Q[0, 0, 0] = 1.0
+    Q[1, 0, 0] = -1.0
+    S = O.head_scores(Q, K, 0, 1, w=1, has_decode=True, alpha=0.0, causal=True, scale=1.0,
+                      weighting="exp", lam=np.log(3.0))
+    np.testing.assert_allclose(S, 0.25 * p_plus + 0.75 * p_minus, atol=2e-6)
+
+
+def test_reserved_positions_kept_first():
+    a, b, c = 0.328455, 0.044452, 0.120832
+    P = np.array([a, b, b, c, b, b, b, a])
+    prot = O.protected_mask(8, 1, 2)  # sink {0}, recent {6, 7}
+    assert prot.tolist() == [True, False, False, False, False, False, True, True]
+    assert O.select_topk(P, 4, prot).tolist() == [0, 3, 6, 7]
+    assert O.select_topk(P, 5, prot).tolist() == [0, 1, 3, 6, 7]  # tie among the b's: lowest position
+    assert O.select_topk(P, 2, prot).tolist() == [0, 6]  # budget below the reserve: lowest reserved positions
+    assert O.select_topk(P, 8, prot).tolist() == list(range(8))
+    assert O.protected_mask(3, 5, 5).all()
+    assert not O.protected_mask(6, 0, 0).any()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_reserve_matches_mask_and_topk(seed):
+    """Budget at least the reserve: same as masking the reserved positions out,
+    taking the top (k - sink - recent) of the rest and adding the reserve."""
+    rng = np.random.default_rng(seed)
+    L, sink, recent = 50, 4, 6
+    P = rng.random(L)
+    for k in (10, 21, 50):
+        masked = P.copy()
+        masked[:sink] = -np.inf
+        masked[L - recent:] = -np.inf
+        top = np.argsort(-masked, kind="stable")[:k - sink - recent]
+        expect = sorted(set(range(sink)) | set(range(L - recent, L)) | set(top.tolist()))
+        assert O.select_topk(P, k, O.protected_mask(L, sink, recent)).tolist() == expect
+
+
 # ---------------------------------------------------------------- planted mistakes
 def _pins_pass():
     """Run the pins above in-process; return False as soon as one fails."""
@@ -346,6 +405,10 @@ def _pins_pass():
         lambda: [test_pool_matches_torch(k) for k in (3, 5)],
         lambda: [test_topk_matches_exhaustive(s) for s in range(6)],
         test_gather_is_take,
+        test_temporal_weights_closed_form,
+        test_temporal_weights_applied_to_rows,
+        test_reserved_positions_kept_first,
+        lambda: [test_reserve_matches_mask_and_topk(s) for s in range(2)],
     ]
     for c in checks:
         try:
@@ -375,11 +438,27 @@ def _swapped_alpha(w, has_decode, alpha):
     return c
 
 
-def _high_index_ties(P, k):
+def _high_index_ties(P, k, protected=None):
     L = len(P)
     keff = max(0, min(int(k), L))
-    order = np.lexsort((-np.arange(L), -P))
+    prot = np.zeros(L, dtype=bool) if protected is None else np.asarray(protected, dtype=bool)
+    order = np.lexsort((-np.arange(L), np.where(prot, 0.0, -P), ~prot))
     return np.sort(order[:keff])
+
+
+def _unnormalised_temporal(w, has_decode, lam):
+    r = np.arange(w, dtype=np.float64) - (w - 1)
+    if has_decode:
+        r = np.append(r, 1.0)
+    return np.exp(lam * r)
+
+
+def _recent_off_by_one(L, sink, recent):
+    keep = np.zeros(L, dtype=bool)
+    keep[:max(0, min(int(sink), L))] = True
+    if recent > 0:
+        keep[max(0, L - int(recent) - 1):L - 1] = True
+    return keep
 
 
 def _avg_exclude_pad(S, kind, kernel):
@@ -415,6 +494,8 @@ MUTATIONS = {
     "window_off_by_one": ("observation_positions", _off_by_one_window),
     "softmax_not_per_row": ("row_probabilities", _no_max_subtraction_sum_mismatch),
     "gather_wrong_head": ("gather_rows", _wrong_gather),
+    "temporal_weights_unnormalised": ("temporal_row_weights", _unnormalised_temporal),
+    "recent_window_off_by_one": ("protected_mask", _recent_off_by_one),
 }
 
 
