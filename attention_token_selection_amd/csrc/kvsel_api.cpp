@@ -30,6 +30,8 @@ struct Plan {
   int B, Hq, Hkv, G, w, wp, R, nrt, Rpad;
   int has_decode, causal, pool, pool_kernel;
   float alpha, cl2;
+  int weighting = 0, sink = 0, recent = 0;
+  float lam2 = 0.0f, log2norm = 0.0f;
   std::vector<int64_t> seq_off;  // B + 1
   std::vector<int32_t> keff;     // B * Hkv
   std::vector<int64_t> out_off;  // B * Hkv + 1
@@ -70,6 +72,11 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   if (p->key_chunk < 0 || p->key_chunk % kKeyTile != 0)
     return fail(KVSEL_EINVAL, "key_chunk must be 0 or a positive multiple of 32");
   if (!p->budgets_h && p->k < 0) return fail(KVSEL_EINVAL, "k must be >= 0");
+  if (p->weighting != KVSEL_WEIGHT_ALPHA && p->weighting != KVSEL_WEIGHT_EXP)
+    return fail(KVSEL_EINVAL, "unknown weighting");
+  if (p->weighting == KVSEL_WEIGHT_EXP && !(std::isfinite(p->lambda) && p->lambda >= 0.0f))
+    return fail(KVSEL_EINVAL, "lambda must be finite and >= 0");
+  if (p->sink_tokens < 0 || p->recent_tokens < 0) return fail(KVSEL_EINVAL, "sink_tokens and recent_tokens must be >= 0");
 
   P.B = p->batch;
   P.Hq = p->Hq;
@@ -117,6 +124,19 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   P.alpha = p->alpha;
   P.pool = p->pool;
   P.pool_kernel = (p->pool == KVSEL_POOL_NONE) ? 1 : p->pool_kernel;
+  P.weighting = p->weighting;
+  P.sink = p->sink_tokens;
+  P.recent = p->recent_tokens;
+  if (P.weighting == KVSEL_WEIGHT_EXP) {
+    // c_r = exp(lambda r) / sum_r' exp(lambda r') over r = -w+1 .. 0 (.. 1):
+    // kept in base 2 and relative to the largest r, so nothing overflows.
+    const double lam = p->lambda;
+    const int rmax = p->has_decode ? 1 : 0;
+    double sum = 0.0;
+    for (int j = 0; j < P.w + p->has_decode; ++j) sum += std::exp(lam * (double)(j - (P.w - 1) - rmax));
+    P.lam2 = (float)(lam * 1.4426950408889634);
+    P.log2norm = (float)std::log2(sum);
+  }
   const float scale = (p->scale == 0.0f) ? 1.0f / std::sqrt((float)p->d) : p->scale;
   P.cl2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
 
@@ -233,6 +253,9 @@ ScoreParams score_params(const Plan &P, const void *Q, const void *K, float *sco
   sp.causal = P.causal;
   sp.cl2 = P.cl2;
   sp.alpha = P.alpha;
+  sp.weighting = P.weighting;
+  sp.lam2 = P.lam2;
+  sp.log2norm = P.log2norm;
   sp.nblk1_max = P.nblk1_max;
   return sp;
 }
@@ -286,6 +309,8 @@ kvsel_status run_select(const Plan &P, const float *scores, float *pooled, int32
   sp.Hkv = P.Hkv;
   sp.pool = P.pool;
   sp.pool_kernel = P.pool_kernel;
+  sp.sink = P.sink;
+  sp.recent = P.recent;
   return for_each_group(P, [&](const SegTable &t, int64_t) {
     hipError_t e = launch_pool_topk(sp, t, st);
     if (e != hipSuccess) return hip_fail(e, "pool/top-k launch");

@@ -43,6 +43,9 @@ struct ScoreParams {
   int has_decode, causal;
   float cl2;                    // scale * log2(e)
   float alpha;
+  int weighting;                // 0: alpha weights; 1: exponential temporal weights
+  float lam2;                   // weighting 1: lambda * log2(e)
+  float log2norm;               // weighting 1: log2 of sum_r exp(lambda (r - r_max))
   int key_block;                // keys per workgroup in this pass (multiple of 32)
   int nblk1_max;                // pass 1 blocks per segment of the longest sequence
 };
@@ -58,6 +61,7 @@ struct SelectParams {
   int Hkv;
   int pool;              // 0 none, 1 avg, 2 max
   int pool_kernel;       // odd
+  int sink, recent;      // reserved positions: [0, sink) and [L - recent, L) of every sequence
   // Optional K/V compaction fused into the selection (K_out == nullptr: off).
   const uint4 *K;        // rows of d bf16 = 16 x uint4
   const uint4 *V;

@@ -386,11 +386,18 @@ __global__ __launch_bounds__(NT) void merge_kernel(ScoreParams p, SegTable t) {
   if (sh != 0 || row >= p.Rpad) return;
 #pragma unroll
   for (int k = 1; k < MERGE_SPLIT; ++k) lse_merge(r, z, shares[k][lrow].x, shares[k][lrow].y);
-  const int wr = row / p.G;
-  float c = 1.0f;
-  if (p.has_decode) c = (wr < p.w) ? (1.0f - p.alpha) : p.alpha;
-  float out = INFINITY;
-  if (row < p.R && c > 0.0f && z > 0.0f) out = r + log2f(z) - log2f(c);
+  const int wr = row / p.G;  // observation row: window rows 0 .. w-1, then the decode row
+  float lc;                  // log2 of the row's weight c_r
+  if (p.weighting == 1) {
+    // c_r = 2^(lambda log2(e) (r - r_max)) / norm, relative position r = wr - (w - 1)
+    lc = p.lam2 * (float)(wr - (p.w - 1) - p.has_decode) - p.log2norm;
+  } else {
+    float c = 1.0f;
+    if (p.has_decode) c = (wr < p.w) ? (1.0f - p.alpha) : p.alpha;
+    lc = (c > 0.0f) ? log2f(c) : -INFINITY;
+  }
+  float out = INFINITY;  // a row of weight 0 (or without visible keys) contributes nothing
+  if (row < p.R && lc > -INFINITY && z > 0.0f) out = r + log2f(z) - lc;
   p.bias[(int64_t)seg * p.Rpad + row] = out;
 }
 

@@ -32,7 +32,8 @@
 //    compute units.
 //
 // Order keys: the fp32 bits mapped so that a larger value has a larger
-// unsigned key (-0 ranks as +0).
+// unsigned key (-0 ranks as +0); reserved positions (DeferKV guide, Phase 3:
+// attention sinks and the recent window) take the largest key of all.
 #include "kvsel_internal.h"
 
 namespace kvsel {
@@ -62,6 +63,13 @@ __device__ inline uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The key a position competes with: reserved positions (the first `sink`
+// and the last `recent` of the sequence) take the largest key, above every
+// value's, so they are kept first (lowest position first among them).
+__device__ inline uint32_t select_key(float f, int pos, int L, int sink, int recent) {
+  return (pos < sink || pos >= L - recent) ? 0xffffffffu : order_key(f);
 }
 
 // N consecutive values of X from position `first` on (first may be
@@ -234,7 +242,7 @@ __global__ __launch_bounds__(NT) void pool_bucket_kernel(SelectParams p, SegTabl
   uint32_t bin[PER], rank[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    bin[e] = order_key(v[e]) >> DSHIFT;
+    bin[e] = select_key(v[e], first + e, g.L, p.sink, p.recent) >> DSHIFT;
     rank[e] = (first + e < g.L) ? atomicAdd(&hist[bin[e]], 1u) : 0u;
   }
   __syncthreads();
@@ -273,7 +281,7 @@ __global__ __launch_bounds__(NT) void pool_bucket_kernel(SelectParams p, SegTabl
   uint32_t *bk = p.bucket + tab * CH;
 #pragma unroll
   for (int e = 0; e < PER; ++e)
-    if (first + e < g.L) bk[hist[bin[e]] + rank[e]] = order_key(v[e]);
+    if (first + e < g.L) bk[hist[bin[e]] + rank[e]] = select_key(v[e], first + e, g.L, p.sink, p.recent);
 }
 
 // ---------------------------------------------------------------- 2. select + compaction per chunk
@@ -509,7 +517,7 @@ __global__ __launch_bounds__(NT) void select_chunk_kernel(SelectParams p, SegTab
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const bool valid = first + e < g.L;
-      k[e] = order_key(v[e]);
+      k[e] = select_key(v[e], first + e, g.L, p.sink, p.recent);
       gt += (valid && k[e] > tau) ? 1 : 0;
       eq += (valid && k[e] == tau) ? 1 : 0;
     }

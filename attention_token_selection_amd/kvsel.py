@@ -26,6 +26,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 KVSEL_OK, KVSEL_EINVAL, KVSEL_EUNSUPPORTED, KVSEL_EHIP = 0, 1, 2, 3
 POOLS = {"none": 0, "avg": 1, "max": 2}
+WEIGHTINGS = {"alpha": 0, "exp": 1}
 
 
 class KvselProblem(ctypes.Structure):
@@ -48,6 +49,10 @@ class KvselProblem(ctypes.Structure):
         ("k", ctypes.c_int32),
         ("budgets_h", ctypes.POINTER(ctypes.c_int32)),
         ("key_chunk", ctypes.c_int32),
+        ("weighting", ctypes.c_int32),
+        ("lambda_", ctypes.c_float),
+        ("sink_tokens", ctypes.c_int32),
+        ("recent_tokens", ctypes.c_int32),
     ]
 
 
@@ -107,7 +112,8 @@ class Problem:
     def __init__(self, *, Hq: int, Hkv: int, w: int, d: int = 128, seq_lens: Optional[Sequence[int]] = None,
                  L: int = 0, batch: int = 1, has_decode: bool = False, alpha: float = 0.0, causal: bool = True,
                  scale: float = 0.0, pool: str = "none", pool_kernel: int = 1, k: int = 0,
-                 budgets=None, key_chunk: int = 0):
+                 budgets=None, key_chunk: int = 0, weighting: str = "alpha", lam: float = 0.0, sink: int = 0,
+                 recent: int = 0):
         if seq_lens is None:
             seq_lens = [int(L)] * int(batch)
         self.seq_lens = [int(x) for x in seq_lens]
@@ -138,6 +144,10 @@ class Problem:
         s.k = self.k
         s.budgets_h = ctypes.cast(self._budgets, ctypes.POINTER(ctypes.c_int32)) if self._budgets else None
         s.key_chunk = int(key_chunk)
+        s.weighting = WEIGHTINGS[weighting] if isinstance(weighting, str) else int(weighting)
+        s.lambda_ = float(lam)
+        s.sink_tokens = int(sink)
+        s.recent_tokens = int(recent)
         self.struct = s
 
     @property

@@ -19,12 +19,17 @@
  *   4. S[i] = sum over the G = Hq/Hkv query heads of group h and over the rows
  *      of c_r * p_r[i] (TideKV §4.2, grouped-query aggregation at KV-head
  *      granularity); c_r = 1 without a decode row, else 1-alpha for prompt
- *      rows and alpha for the decode row (DeferKV Guide, Phase 2 weighting);
+ *      rows and alpha for the decode row (DeferKV Guide, Phase 2 weighting),
+ *      or the guide's exponential temporal weights (enum kvsel_weighting);
  *   5. a stride-1 1-D pool of odd width (avg: zero-padded sum / width; max:
  *      over in-range positions) -- not defined on the pages;
  *   6. top-k: the min(k_bh, L_b) positions with the largest pooled score,
  *      lower position first among equal scores, reported ascending (TideKV
- *      §5 keeps original positions; DeferKV Guide, Phase 3, sorts them);
+ *      §5 keeps original positions; DeferKV Guide, Phase 3, sorts them).
+ *      Reserved positions (the first sink_tokens and the last recent_tokens
+ *      of the sequence; DeferKV Guide, Phase 3) are kept before any other,
+ *      lowest position first if the budget cannot hold them all, and the
+ *      rest of the budget goes to the highest scores;
  *   7. gather of the kept K and V rows (TideKV §4.2 and §5, compact KV-head
  *      layout with per-head offsets, §4.1).
  * Query head g belongs to KV head g / G.
@@ -70,7 +75,7 @@
 extern "C" {
 #endif
 
-#define KVSEL_ABI_VERSION 1
+#define KVSEL_ABI_VERSION 2
 
 /* Same type as hipStream_t; NULL means the default stream. */
 typedef struct ihipStream_t *kvsel_stream_t;
@@ -87,6 +92,18 @@ typedef enum kvsel_pool {
   KVSEL_POOL_AVG = 1,
   KVSEL_POOL_MAX = 2
 } kvsel_pool;
+
+/* Weights c_r of the observation rows in the aggregated score. */
+typedef enum kvsel_weighting {
+  /* 1 for every row without a decode row; with one, 1 - alpha for the prompt
+   * rows and alpha for the decode row. */
+  KVSEL_WEIGHT_ALPHA = 0,
+  /* The DeferKV guide's exponential temporal weights (Phase 2): relative
+   * positions r = -w+1 .. 0 for the prompt rows (oldest first) and r = 1 for
+   * the decode row; c_r = exp(lambda * r) / sum over the rows of
+   * exp(lambda * r'), so the weights sum to 1. */
+  KVSEL_WEIGHT_EXP = 1
+} kvsel_weighting;
 
 /* Problem description, shared by every entry point.  Host memory. */
 typedef struct kvsel_problem {
@@ -106,6 +123,10 @@ typedef struct kvsel_problem {
   int32_t k;                     /* uniform budget >= 0 when budgets_h is NULL */
   const int32_t *budgets_h;      /* host, B*Hkv budgets (>= 0, sequence-major), or NULL */
   int32_t key_chunk;             /* keys per pass-1 statistics block (multiple of 32), 0 = library choice */
+  int32_t weighting;             /* a kvsel_weighting value; 0 is KVSEL_WEIGHT_ALPHA */
+  float lambda;                  /* KVSEL_WEIGHT_EXP: finite, >= 0 (0 gives equal weights) */
+  int32_t sink_tokens;           /* >= 0: positions 0 .. sink-1 of every sequence are always kept */
+  int32_t recent_tokens;         /* >= 0: positions L_b-recent .. L_b-1 are always kept */
 } kvsel_problem;
 
 /* KVSEL_ABI_VERSION of the loaded library. */

@@ -6,7 +6,9 @@ Tolerances (fp32 accumulation of exact bf16 products, fp32 exp2; fp64 oracle):
   entries from failing);
 * kept positions: same count, ascending, and any position in one set but not
   the other must have an oracle pooled score within RTOL of the oracle's k-th
-  largest value (several selections are correct near ties);
+  largest value (several selections are correct near ties); reserved (sink and
+  recent) positions are kept first, so the k-th value is taken over the others
+  with the budget left after them;
 * gathered K/V: bit-exact copies of the rows the GPU chose.
 A second, tighter band (DIAG_RTOL) is reported, not enforced.
 """
@@ -50,7 +52,16 @@ def kth_value(P, k):
     return P[order[k - 1]]
 
 
-def check_selection(gpu_idx, ref_idx, P_ref, keff, L, rtol=RTOL):
+def reserved_mask(L, sink=0, recent=0):
+    """Positions always kept: the first ``sink`` and the last ``recent``."""
+    m = np.zeros(L, dtype=bool)
+    m[:min(sink, L)] = True
+    if recent > 0:
+        m[max(0, L - recent):] = True
+    return m
+
+
+def check_selection(gpu_idx, ref_idx, P_ref, keff, L, rtol=RTOL, reserved=None):
     gpu_idx = np.asarray(gpu_idx, dtype=np.int64)
     ref_idx = np.asarray(ref_idx, dtype=np.int64)
     assert len(gpu_idx) == keff == len(ref_idx), (len(gpu_idx), keff, len(ref_idx))
@@ -59,7 +70,13 @@ def check_selection(gpu_idx, ref_idx, P_ref, keff, L, rtol=RTOL):
     assert np.all(np.diff(gpu_idx) > 0), "positions must be strictly ascending"
     assert gpu_idx[0] >= 0 and gpu_idx[-1] < L
     diff = np.setxor1d(gpu_idx, ref_idx)
-    tau = kth_value(P_ref, keff)
+    if reserved is not None and reserved.any():
+        # reserved positions are not chosen by score: both sides keep the same ones
+        assert not reserved[diff].any(), f"reserved positions {diff[reserved[diff]][:10]} differ"
+        others = np.nonzero(~reserved)[0]
+        tau = kth_value(P_ref[others], keff - int(reserved.sum()))
+    else:
+        tau = kth_value(P_ref, keff)
     near = np.abs(P_ref[diff] - tau) <= rtol * tau
     assert np.all(near), f"positions {diff[~near][:10]} differ and are not near-ties (tau={tau})"
     return len(diff)
@@ -82,11 +99,16 @@ def check_finite(x, what):
     assert not bad.any(), f"{what}: {int(bad.sum())} non-finite values, runs {_runs(bad)}"
 
 
-def check_select_exact(gpu_idx, gpu_pooled32, keff, where=""):
-    """Top-k of the GPU's own fp32 pooled scores, from a CPU stable sort."""
+def check_select_exact(gpu_idx, gpu_pooled32, keff, where="", reserved=None):
+    """Top-k of the GPU's own fp32 pooled scores, from a CPU stable sort
+    (reserved positions first, in position order, when a mask is given)."""
     P = np.asarray(gpu_pooled32, dtype=np.float32)
     check_finite(P, f"{where} pooled")
-    order = np.argsort(-P, kind="stable")
+    if reserved is not None and reserved.any():
+        rest = np.nonzero(~reserved)[0]
+        order = np.concatenate([np.nonzero(reserved)[0], rest[np.argsort(-P[rest], kind="stable")]])
+    else:
+        order = np.argsort(-P, kind="stable")
     expect = np.sort(order[:keff])
     got = np.asarray(gpu_idx, dtype=np.int64)
     if not np.array_equal(got, expect):
@@ -130,6 +152,7 @@ def check_against_oracle(spec, case, out, ref, heads=None, scores=None):
     stats = {"near_tie_diffs": 0, "max_rel": 0.0, "beyond_diag": 0, "segments": 0}
     for (b, h, L, soff, ooff, keff) in segments(spec, out["out_offsets"]):
         gidx = idx[ooff:ooff + keff]
+        res = reserved_mask(L, getattr(spec, "sink", 0), getattr(spec, "recent", 0))
         # gathered rows are exact copies of the rows the GPU chose (all segments)
         if keff:
             rows = torch.from_numpy(starts[b] + gidx.astype(np.int64))
@@ -138,7 +161,7 @@ def check_against_oracle(spec, case, out, ref, heads=None, scores=None):
         if sc is not None:
             check_finite(sc[soff:soff + L], f"segment {(b, h)} scores")
         if pooled is not None:
-            check_select_exact(gidx, pooled[soff:soff + L], keff, where=f"segment {(b, h)}")
+            check_select_exact(gidx, pooled[soff:soff + L], keff, where=f"segment {(b, h)}", reserved=res)
         if heads is not None and (b, h) not in heads:
             continue
         r = ref[(b, h)]
@@ -148,6 +171,6 @@ def check_against_oracle(spec, case, out, ref, heads=None, scores=None):
             stats["beyond_diag"] += st["beyond_diag"]
         if sc is not None:
             check_scores(sc[soff:soff + L], r["scores"], f"scores{(b, h)}")
-        stats["near_tie_diffs"] += check_selection(gidx, r["idx"], r["pooled"], keff, L)
+        stats["near_tie_diffs"] += check_selection(gidx, r["idx"], r["pooled"], keff, L, reserved=res)
         stats["segments"] += 1
     return stats

@@ -31,8 +31,8 @@ def test_exports_every_declared_function():
 
 def test_abi_version_matches_header():
     with open(kv.HEADER_PATH) as f:
-        assert "#define KVSEL_ABI_VERSION 1" in f.read()
-    assert kv.abi_version() == 1
+        assert "#define KVSEL_ABI_VERSION 2" in f.read()
+    assert kv.abi_version() == 2
 
 
 def test_status_strings():
@@ -69,6 +69,12 @@ BAD = {
     "decode_flag": dict(has_decode=2),
     "scale_inf": dict(scale=float("inf")),
     "budget_negative": dict(budgets=[[1, -1]]),
+    "weighting_unknown": dict(weighting=2),
+    "lambda_negative": dict(weighting="exp", lam=-0.1),
+    "lambda_nan": dict(weighting="exp", lam=float("nan")),
+    "lambda_inf": dict(weighting="exp", lam=float("inf")),
+    "sink_negative": dict(sink=-1),
+    "recent_negative": dict(recent=-2),
 }
 
 
@@ -155,7 +161,8 @@ def test_struct_layout_matches_c():
 #include "kvsel.h"
 #define F(x) printf("%s %zu\n", #x, offsetof(kvsel_problem, x));
 int main(void) { F(batch) F(Hq) F(Hkv) F(d) F(L) F(seq_offsets_h) F(w) F(has_decode) F(alpha) F(causal)
-  F(scale) F(pool) F(pool_kernel) F(k) F(budgets_h) F(key_chunk) printf("size %zu\n", sizeof(kvsel_problem)); return 0; }
+  F(scale) F(pool) F(pool_kernel) F(k) F(budgets_h) F(key_chunk) F(weighting) F(lambda) F(sink_tokens)
+  F(recent_tokens) printf("size %zu\n", sizeof(kvsel_problem)); return 0; }
 '''
     import tempfile
 
@@ -168,5 +175,6 @@ int main(void) { F(batch) F(Hq) F(Hkv) F(d) F(L) F(seq_offsets_h) F(w) F(has_dec
         out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
     got = dict(line.split() for line in out.splitlines())
     for name, _ in kv.KvselProblem._fields_:
-        assert int(got[name]) == getattr(kv.KvselProblem, name).offset, name
+        c_name = name.rstrip("_")  # "lambda" is a Python keyword
+        assert int(got[c_name]) == getattr(kv.KvselProblem, name).offset, name
     assert int(got["size"]) == ctypes.sizeof(kv.KvselProblem)

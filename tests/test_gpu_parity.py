@@ -18,7 +18,7 @@ import torch
 
 import oracle.kvsel_oracle as O
 import workloads as W
-from parity import check_against_oracle, check_scores, check_select_exact, segments, to_np64
+from parity import check_against_oracle, check_scores, check_select_exact, reserved_mask, segments, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -250,6 +250,88 @@ def test_select_exact_on_given_scores(kv, kind, pool, kernel):
             check_scores(P[soff:soff + L], O.pool1d(seg.astype(np.float64), "avg", kernel),
                          rtol=1e-6 if kernel <= 9 else 2e-5)
         check_select_exact(I[ooff:ooff + keff], P[soff:soff + L], keff)
+
+
+@pytest.mark.parametrize("kind", ["two_values", "all_equal", "spread", "reverse"])
+@pytest.mark.parametrize("sink,recent", [(16, 32), (0, 100), (5000, 0), (3, 70000), (2047, 2049)])
+def test_select_reserved_on_given_scores(kv, kind, sink, recent):
+    """Reserved sink/recent positions are kept first, then the highest scores;
+    budgets below, at and above the reserved count."""
+    rng = np.random.default_rng(zlib.crc32(f"{kind}/{sink}/{recent}".encode()))
+    lens = [1, 7, 1000, 4099, 70000]
+    Hkv = 2
+    budgets = [[1, 0], [3, 7], [40, 999], [4099, 3000], [2048, 6000]]
+    p = kv.Problem(Hq=2, Hkv=Hkv, w=1, seq_lens=lens, pool="max", pool_kernel=7, budgets=budgets, sink=sink,
+                   recent=recent)
+    ws, offs = kv.kvsel_plan(p)
+    S = np.concatenate([_adversarial_scores(kind, L, rng) for L in lens for _ in range(Hkv)])
+    scores = torch.from_numpy(S).to(DEV)
+    pooled = torch.empty_like(scores)
+    idx = torch.empty(offs[-1], dtype=torch.int32, device=DEV)
+    kv.kvsel_pool_topk(p, scores, pooled, idx, torch.empty(ws, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    P = pooled.cpu().numpy()
+    I = idx.cpu().numpy()
+    spec = W.Spec("given", lens, Hq=2, Hkv=Hkv, pool="max", pool_kernel=7, budgets=budgets)
+    for (b, h, L, soff, ooff, keff) in segments(spec, offs):
+        # the pooled output holds the real pooled values, reserved or not
+        np.testing.assert_array_equal(P[soff:soff + L], O.pool1d(S[soff:soff + L].astype(np.float64), "max", 7))
+        res = reserved_mask(L, sink, recent)
+        check_select_exact(I[ooff:ooff + keff], P[soff:soff + L], keff, where=f"segment {(b, h)}", reserved=res)
+        # and the oracle's own selection rule agrees exactly on these fp32 values
+        ref = O.select_topk(P[soff:soff + L].astype(np.float64), keff, O.protected_mask(L, sink, recent))
+        np.testing.assert_array_equal(I[ooff:ooff + keff], ref)
+
+
+def test_deferkv_full_size(kv):
+    """The guide's defaults on a 32K-key layer: exp weights (lambda 0.1) over
+    32 prompt rows and the decode row, 16 sinks and 32 recent kept."""
+    spec = W.deferkv_full()
+    heads = [(0, 0), (0, 5)]
+    _say(f"{spec.name}: generating")
+    case = W.make_case(spec, layer=0, device=DEV)
+    _, out, scores = _run(kv, spec, case)
+    _say(f"{spec.name}: oracle on {heads}")
+    case_cpu = {k: v.cpu() for k, v in case.items()}
+    ref = _oracle(spec, case_cpu, heads=heads)
+    st = check_against_oracle(spec, case_cpu, out, ref, heads=heads, scores=scores)
+    _say(f"{spec.name}: {st}")
+    assert st["segments"] == len(heads)
+
+
+def test_exp_weights_closed_forms(kv):
+    """lambda = 0 weights every row 1/w' (so w' times the scores equal the
+    unweighted sum); a very large lambda leaves only the newest row."""
+    base = dict(Hq=8, Hkv=2, w=8, seq_lens=[900, 300], causal=True, pool="none", k=0)
+    spec = W.Spec("exp_closed", [900, 300], Hq=8, Hkv=2, w=8, has_decode=True, recipe="decode_corr")
+    case = W.make_case(spec)
+    Q, K = (case[x].to(DEV) for x in "QK")
+    n = sum(spec.seq_lens) * spec.Hkv
+
+    def score(**kw):
+        p = kv.Problem(**base, **kw)
+        ws, _ = kv.kvsel_plan(p)
+        out = torch.empty(n, device=DEV)
+        kv.kvsel_score(p, Q, K, out, torch.empty(ws, dtype=torch.uint8, device=DEV))
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64)
+
+    # prompt rows only: there the alpha weighting gives every row weight 1
+    Qp = Q[:, :8].contiguous()
+    p_alpha = kv.Problem(**base)
+    p_exp0 = kv.Problem(**base, weighting="exp", lam=0.0)
+    ws, _ = kv.kvsel_plan(p_alpha)
+    a = torch.empty(n, device=DEV)
+    e = torch.empty(n, device=DEV)
+    wsb = torch.empty(ws, dtype=torch.uint8, device=DEV)
+    kv.kvsel_score(p_alpha, Qp, K, a, wsb)
+    kv.kvsel_score(p_exp0, Qp, K, e, wsb)
+    torch.cuda.synchronize()
+    check_scores(8.0 * e.cpu().numpy().astype(np.float64), a.cpu().numpy().astype(np.float64), "lambda=0")
+    # lambda huge: the decode row alone, which is alpha = 1
+    big = score(has_decode=True, weighting="exp", lam=1000.0)
+    dec = score(has_decode=True, alpha=1.0)
+    check_scores(big, dec, "lambda=1000")
 
 
 # ---------------------------------------------------------------- gather on given indices

@@ -53,6 +53,10 @@ class Spec:
     k: int = 0
     budgets: Optional[List[List[int]]] = None  # [B][Hkv]
     key_chunk: int = 0
+    weighting: str = "alpha"  # alpha | exp (temporal row weights)
+    lam: float = 0.0  # exp weighting: c_r proportional to exp(lam * r)
+    sink: int = 0  # reserved prefix positions
+    recent: int = 0  # reserved suffix positions
     layers: int = 1
     recipe: str = "plant"  # plant | runs | zipf | decode_corr | plain | hand
     plant_frac: float = 0.02
@@ -205,6 +209,13 @@ def config(i: int) -> Spec:
     raise ValueError(i)
 
 
+def deferkv_full() -> Spec:
+    """The DeferKV guide's defaults (lambda 0.1, 16 sinks, 32 recent) on the
+    32K-key Llama-3.1-8B-like layer, with the decode-step row."""
+    return Spec("deferkv_L32k_exp0.1_sink16_recent32_max7_k2048", [32768], w=32, has_decode=True, pool="max",
+                pool_kernel=7, k=2048, weighting="exp", lam=0.1, sink=16, recent=32, recipe="decode_corr")
+
+
 def small_cases():
     """Small shapes spanning several key tiles, ragged tails and edge cases."""
     cases = [
@@ -233,6 +244,15 @@ def small_cases():
         Spec("s_many_seqs", [40 + 13 * i for i in range(10)], Hq=16, Hkv=8, w=4, pool="avg", pool_kernel=3,
              k=9, recipe="plant", plant_frac=0.05),
         Spec("s_hkv64", [70], Hq=64, Hkv=64, w=3, pool="max", pool_kernel=3, k=10, recipe="plain"),
+        # DeferKV-style: exponential temporal row weights and reserved sink / recent positions
+        Spec("s_exp_sink_recent", [3000], Hq=32, Hkv=8, w=32, has_decode=True, pool="max", pool_kernel=7,
+             k=200, weighting="exp", lam=0.1, sink=16, recent=32, recipe="decode_corr"),
+        Spec("s_exp_nodecode", [700], Hq=16, Hkv=4, w=16, pool="avg", pool_kernel=5, k=60, weighting="exp",
+             lam=0.5, recipe="plant", plant_frac=0.05),
+        Spec("s_reserve_over_budget", [500, 90], Hq=8, Hkv=2, w=8, pool="avg", pool_kernel=3,
+             budgets=[[10, 40], [90, 3]], sink=8, recent=24, recipe="plant"),
+        Spec("s_reserve_whole_seq", [2100], Hq=8, Hkv=2, w=8, has_decode=True, weighting="exp", lam=2.0,
+             pool="max", pool_kernel=3, k=2090, sink=2100, recent=0, recipe="plain"),
     ]
     return cases
 
@@ -242,11 +262,13 @@ def problem_kwargs(spec: Spec) -> dict:
     return dict(Hq=spec.Hq, Hkv=spec.Hkv, d=spec.d, w=spec.w, seq_lens=list(spec.seq_lens),
                 has_decode=spec.has_decode, alpha=spec.alpha, causal=spec.causal, scale=spec.scale,
                 pool=spec.pool, pool_kernel=spec.pool_kernel, k=spec.k, budgets=spec.budgets,
-                key_chunk=spec.key_chunk)
+                key_chunk=spec.key_chunk, weighting=spec.weighting, lam=spec.lam, sink=spec.sink,
+                recent=spec.recent)
 
 
 def oracle_kwargs(spec: Spec) -> dict:
     """Keyword arguments describing ``spec`` to the oracle's ``compress``."""
     return dict(seq_lens=list(spec.seq_lens), Hq=spec.Hq, Hkv=spec.Hkv, w=spec.w, has_decode=spec.has_decode,
                 alpha=spec.alpha, causal=spec.causal, scale=(spec.scale if spec.scale else None), pool=spec.pool,
-                pool_kernel=spec.pool_kernel, k=spec.k, budgets=spec.budgets)
+                pool_kernel=spec.pool_kernel, k=spec.k, budgets=spec.budgets, weighting=spec.weighting,
+                lam=spec.lam, sink=spec.sink, recent=spec.recent)
