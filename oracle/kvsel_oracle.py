@@ -31,7 +31,11 @@ What it computes (one sequence ``b`` and one KV head ``h`` at a time):
    prompt-vs-decode weighting, in its two-level form).  Optionally the
    guide's exponential temporal weights instead: ``c_r`` proportional to
    ``exp(lambda * r)`` over relative row positions ``r = -w+1 .. 0`` (and ``1``
-   for the decode row), normalised to sum to 1.
+   for the decode row), normalised to sum to 1.  Optionally the guide's
+   grouped-query shortcut instead of the per-head sum: the group's queries
+   are averaged into one query per row first (the mean rounded once to
+   bfloat16, the dtype of the queries it averages), and that single row's
+   softmax is weighted and summed over the rows.
 6. 1-D pool of odd width ``K`` and stride 1 (no page defines it; reading:
    ``avg`` = zero-padded window sum divided by ``K``, ``max`` = max over the
    in-range positions only).
@@ -64,6 +68,8 @@ __all__ = [
     "temporal_row_weights",
     "protected_mask",
     "row_probabilities",
+    "round_to_bf16",
+    "mean_query_rows",
     "head_scores",
     "pool1d",
     "select_topk",
@@ -164,14 +170,41 @@ def row_probabilities(q_rows: np.ndarray, K_h: np.ndarray, vis: np.ndarray, scal
     return e / z
 
 
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits and float32's exponent range, so its
+    spacing at ``|x|`` in ``[2^e, 2^(e+1))`` is ``2^(e-7)`` (never below the
+    subnormal spacing ``2^-133``).  Each value is divided by its spacing,
+    rounded to an integer with ties to even (``numpy.rint``) and scaled back.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    nz = x != 0
+    _, e = np.frexp(x[nz])  # |x| = m * 2^e with 0.5 <= m < 1, so |x| in [2^(e-1), 2^e)
+    q = np.maximum(e - 8, -133)  # exponent of the spacing
+    out[nz] = np.ldexp(np.rint(np.ldexp(x[nz], -q)), q)
+    return out
+
+
+def mean_query_rows(Q_b: np.ndarray, h: int, G: int) -> np.ndarray:
+    """The DeferKV guide's grouped-query shortcut (Phase 2 code): one query
+    per observation row, the mean of the ``G`` query heads of group ``h``,
+    rounded to bfloat16 like the queries it averages.  [w', Hq, d] -> [w', d]."""
+    return round_to_bf16(Q_b[:, h * G:(h + 1) * G, :].mean(axis=1))
+
+
 def head_scores(Q_b: np.ndarray, K_b: np.ndarray, h: int, Hkv: int, *, w: int, has_decode: bool,
-                alpha: float, causal: bool, scale: float, weighting: str = "alpha", lam: float = 0.0) -> np.ndarray:
+                alpha: float, causal: bool, scale: float, weighting: str = "alpha", lam: float = 0.0,
+                gqa: str = "sum") -> np.ndarray:
     """Aggregated importance ``S[i]`` of one (sequence, KV head).
 
     ``Q_b`` [w', Hq, d] observation queries of the sequence (decode row last),
     ``K_b`` [L, Hkv, d] its keys.  Sums ``c_r * P`` over the window rows and the
-    ``G`` query heads of group ``h``; ``c_r`` from ``row_weights`` (weighting
-    "alpha") or ``temporal_row_weights`` (weighting "exp").
+    ``G`` query heads of group ``h`` (``gqa`` "sum"), or over the rows of the
+    group's mean query (``gqa`` "mean", see ``mean_query_rows``); ``c_r`` from
+    ``row_weights`` (weighting "alpha") or ``temporal_row_weights`` (weighting
+    "exp").
     """
     L = K_b.shape[0]
     Hq = Q_b.shape[1]
@@ -185,10 +218,15 @@ def head_scores(Q_b: np.ndarray, K_b: np.ndarray, h: int, Hkv: int, *, w: int, h
     else:
         raise ValueError(f"unknown weighting {weighting!r}")
     K_h = K_b[:, h, :]
+    if gqa == "sum":
+        query_sets = [Q_b[:, h * G + gi, :] for gi in range(G)]
+    elif gqa == "mean":
+        query_sets = [mean_query_rows(Q_b, h, G)]
+    else:
+        raise ValueError(f"unknown gqa {gqa!r}")
     S = np.zeros(L, dtype=np.float64)
-    for gi in range(G):
-        g = h * G + gi
-        P = row_probabilities(Q_b[:, g, :], K_h, vis, scale)
+    for q in query_sets:
+        P = row_probabilities(q, K_h, vis, scale)
         S += (c[:, None] * P).sum(axis=0)
     return S
 
@@ -317,7 +355,7 @@ def plan_offsets(seq_lens, Hkv: int, budgets) -> np.ndarray:
 def compress(Q, K, V, *, seq_lens, Hq: int, Hkv: int, w: int, has_decode: bool = False,
              alpha: float = 0.0, causal: bool = True, scale=None, pool: str = "none",
              pool_kernel: int = 1, k=None, budgets=None, heads=None, weighting: str = "alpha",
-             lam: float = 0.0, sink: int = 0, recent: int = 0):
+             lam: float = 0.0, sink: int = 0, recent: int = 0, gqa: str = "sum"):
     """Whole path for a packed batch.
 
     ``Q`` [B, w', Hq, d]; ``K``, ``V`` [sum L_b, Hkv, d] (sequences packed
@@ -350,7 +388,7 @@ def compress(Q, K, V, *, seq_lens, Hq: int, Hkv: int, w: int, has_decode: bool =
             if want is not None and (b, h) not in want:
                 continue
             S = head_scores(Q[b], K_b, h, Hkv, w=w, has_decode=has_decode, alpha=alpha,
-                            causal=causal, scale=scale, weighting=weighting, lam=lam)
+                            causal=causal, scale=scale, weighting=weighting, lam=lam, gqa=gqa)
             P = pool1d(S, pool, pool_kernel)
             idx = select_topk(P, budgets[b][h], protected_mask(len(S), sink, recent))
             res[(b, h)] = {

@@ -391,6 +391,61 @@ def test_reserve_matches_mask_and_topk(seed):
         assert O.select_topk(P, k, O.protected_mask(L, sink, recent)).tolist() == expect
 
 
+def test_round_to_bf16_matches_torch_conversion():
+    """float32 -> bfloat16 in torch rounds to nearest, ties to even; on values
+    that float32 holds exactly the oracle's rounding must agree bit for bit."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.integers(-40, 38, 20000)).astype(np.float32)
+    # exact halfway cases between neighbouring bfloat16 values, both parities
+    base = torch.randn(4000).to(torch.bfloat16).to(torch.float32).numpy()
+    ulp = np.ldexp(1.0, np.frexp(base.astype(np.float64))[1] - 8).astype(np.float32)
+    ties = (base.astype(np.float64) + 0.5 * ulp).astype(np.float32)
+    sub = (rng.random(2000) * 2.0 ** -126).astype(np.float32)  # bfloat16 subnormal range
+    for v in (x, ties, sub, np.array([0.0, -0.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8], dtype=np.float32)):
+        want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+        np.testing.assert_array_equal(O.round_to_bf16(v.astype(np.float64)), want)
+    assert O.round_to_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0  # tie, to the even neighbour
+    assert O.round_to_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+
+
+def test_mean_query_matches_torch_bf16_mean():
+    """torch's mean over bfloat16 queries (what the DeferKV guide's code runs)
+    gives the same rows: the exact mean rounded once to bfloat16."""
+    g = torch.Generator().manual_seed(3)
+    Q = (torch.randn(9, 32, 128, generator=g) * 11.3).to(torch.bfloat16)
+    for h in (0, 3, 7):
+        want = Q[:, 4 * h:4 * h + 4, :].mean(dim=1).to(torch.float64).numpy()
+        np.testing.assert_array_equal(O.mean_query_rows(Q.to(torch.float64).numpy(), h, 4), want)
+
+
+def test_mean_query_hand_groups():
+    """Hand keys, one window row at position 7, Hq = 4, Hkv = 2.  Group 0 holds
+    queries +1 and -1 (mean 0: uniform 1/8 over the 8 visible keys); group 1
+    holds +1 and +1 (mean +1: the worked example's row q=+1)."""
+    j = _hand()
+    a, b, c = 0.328455, 0.044452, 0.120832
+    K = np.zeros((8, 2, 128))
+    K[:, :, 0] = np.asarray(j["keys_c0"])[:, None]
+    Q = np.zeros((1, 4, 128))
+    Q[0, :, 0] = [1.0, -1.0, 1.0, 1.0]
+    kw = dict(w=1, has_decode=False, alpha=0.0, causal=True, scale=1.0, gqa="mean")
+    np.testing.assert_allclose(O.head_scores(Q, K, 0, 2, **kw), np.full(8, 0.125), rtol=1e-14)
+    np.testing.assert_allclose(O.head_scores(Q, K, 1, 2, **kw), [a, b, b, c, b, b, b, a], atol=2e-6)
+
+
+def test_mean_query_equal_heads_is_sum_over_G():
+    """When every query head of a group holds the same bfloat16 query, the mean
+    is that query, so the mean-query score is the per-head sum divided by G."""
+    rng = np.random.default_rng(8)
+    L, G, w = 300, 4, 6
+    K = rng.standard_normal((L, 1, 128)) / np.sqrt(128)
+    q = O.round_to_bf16(rng.standard_normal((w + 1, 1, 128)) * np.sqrt(128))
+    Q = np.repeat(q, G, axis=1)
+    kw = dict(w=w, has_decode=True, alpha=0.0, causal=True, scale=1.0 / np.sqrt(128), weighting="exp", lam=0.1)
+    np.testing.assert_allclose(O.head_scores(Q, K, 0, 1, gqa="mean", **kw),
+                               O.head_scores(Q, K, 0, 1, gqa="sum", **kw) / G, rtol=1e-12)
+
+
 # ---------------------------------------------------------------- planted mistakes
 def _pins_pass():
     """Run the pins above in-process; return False as soon as one fails."""
@@ -409,6 +464,10 @@ def _pins_pass():
         test_temporal_weights_applied_to_rows,
         test_reserved_positions_kept_first,
         lambda: [test_reserve_matches_mask_and_topk(s) for s in range(2)],
+        test_round_to_bf16_matches_torch_conversion,
+        test_mean_query_matches_torch_bf16_mean,
+        test_mean_query_hand_groups,
+        test_mean_query_equal_heads_is_sum_over_G,
     ]
     for c in checks:
         try:
@@ -461,6 +520,25 @@ def _recent_off_by_one(L, sink, recent):
     return keep
 
 
+def _bf16_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    nz = x != 0
+    _, e = np.frexp(x[nz])
+    q = np.maximum(e - 8, -133)
+    out[nz] = np.ldexp(np.trunc(np.ldexp(x[nz], -q)), q)
+    return out
+
+
+def _mean_query_unrounded(Q_b, h, G):
+    return Q_b[:, h * G:(h + 1) * G, :].mean(axis=1)
+
+
+def _mean_query_strided(Q_b, h, G):
+    Hkv = Q_b.shape[1] // G
+    return O.round_to_bf16(Q_b[:, h::Hkv, :].mean(axis=1))
+
+
 def _avg_exclude_pad(S, kind, kernel):
     if kind != "avg":
         return O.pool1d.__wrapped__(S, kind, kernel)
@@ -496,6 +574,9 @@ MUTATIONS = {
     "gather_wrong_head": ("gather_rows", _wrong_gather),
     "temporal_weights_unnormalised": ("temporal_row_weights", _unnormalised_temporal),
     "recent_window_off_by_one": ("protected_mask", _recent_off_by_one),
+    "bf16_rounding_truncates": ("round_to_bf16", _bf16_truncate),
+    "mean_query_not_rounded": ("mean_query_rows", _mean_query_unrounded),
+    "mean_query_strided_groups": ("mean_query_rows", _mean_query_strided),
 }
 
 
