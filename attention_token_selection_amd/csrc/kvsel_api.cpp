@@ -31,6 +31,9 @@ struct Plan {
   int has_decode, causal, pool, pool_kernel;
   float alpha, cl2;
   int weighting = 0, sink = 0, recent = 0;
+  int gqa = 0;          // KVSEL_GQA_MEAN_QUERY: Hq and G below describe the mean queries
+  int Hq_in = 0, G_in = 0;  // the caller's query heads and group size
+  size_t off_qmean = 0;
   float lam2 = 0.0f, log2norm = 0.0f;
   std::vector<int64_t> seq_off;  // B + 1
   std::vector<int32_t> keff;     // B * Hkv
@@ -77,11 +80,19 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   if (p->weighting == KVSEL_WEIGHT_EXP && !(std::isfinite(p->lambda) && p->lambda >= 0.0f))
     return fail(KVSEL_EINVAL, "lambda must be finite and >= 0");
   if (p->sink_tokens < 0 || p->recent_tokens < 0) return fail(KVSEL_EINVAL, "sink_tokens and recent_tokens must be >= 0");
+  if (p->gqa != KVSEL_GQA_SUM && p->gqa != KVSEL_GQA_MEAN_QUERY) return fail(KVSEL_EINVAL, "unknown gqa");
 
   P.B = p->batch;
   P.Hq = p->Hq;
   P.Hkv = p->Hkv;
   P.G = p->Hq / p->Hkv;
+  P.Hq_in = P.Hq;
+  P.G_in = P.G;
+  P.gqa = p->gqa;
+  if (P.gqa == KVSEL_GQA_MEAN_QUERY) {  // the kernels score one mean query per KV head
+    P.Hq = P.Hkv;
+    P.G = 1;
+  }
   P.w = p->w;
   P.wp = p->w + p->has_decode;
   P.seq_off.assign(P.B + 1, 0);
@@ -166,6 +177,8 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   off = align_up(off + nchunks * (kSelectBins / 32) * sizeof(uint16_t), 256);
   P.off_bucket = off;
   off = align_up(off + nchunks * kSelectChunk * sizeof(uint32_t), 256);
+  P.off_qmean = off;
+  if (P.gqa == KVSEL_GQA_MEAN_QUERY) off = align_up(off + (size_t)P.B * P.wp * P.Hkv * p->d * sizeof(uint16_t), 256);
   P.ws_bytes = off;
   return KVSEL_OK;
 }
@@ -237,6 +250,7 @@ ScoreParams score_params(const Plan &P, const void *Q, const void *K, float *sco
   ScoreParams sp;
   std::memset(&sp, 0, sizeof(sp));
   sp.Q = static_cast<const uint16_t *>(Q);
+  if (P.gqa == KVSEL_GQA_MEAN_QUERY) sp.Q = reinterpret_cast<const uint16_t *>(ws + P.off_qmean);
   sp.K = static_cast<const uint16_t *>(K);
   sp.scores = scores;
   sp.partials = reinterpret_cast<float2 *>(ws + P.off_partials);
@@ -262,6 +276,17 @@ ScoreParams score_params(const Plan &P, const void *Q, const void *K, float *sco
 
 // Pass 1: per-block row statistics into the workspace.
 kvsel_status run_row_stats(const Plan &P, const void *Q, const void *K, char *ws, hipStream_t st) {
+  if (P.gqa == KVSEL_GQA_MEAN_QUERY) {
+    QueryMeanParams qp;
+    qp.Q = static_cast<const uint4 *>(Q);
+    qp.Qm = reinterpret_cast<uint4 *>(ws + P.off_qmean);
+    qp.Hq = P.Hq_in;
+    qp.Hkv = P.Hkv;
+    qp.G = P.G_in;
+    qp.items = P.B * P.wp * P.Hkv;
+    hipError_t e = launch_query_mean(qp, st);
+    if (e != hipSuccess) return hip_fail(e, "query mean launch");
+  }
   ScoreParams sp = score_params(P, Q, K, nullptr, ws);
   return for_each_group(P, [&](const SegTable &t, int64_t lmax) {
     sp.key_block = P.kb1;

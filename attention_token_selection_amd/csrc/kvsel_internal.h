@@ -50,6 +50,15 @@ struct ScoreParams {
   int nblk1_max;                // pass 1 blocks per segment of the longest sequence
 };
 
+// The mean query of every (sequence, observation row, KV head): the G query
+// heads of the group averaged, rounded to bf16.
+struct QueryMeanParams {
+  const uint4 *Q;  // bf16 [B][w'][Hq][d], 16 uint4 per row of d = 128
+  uint4 *Qm;       // bf16 [B][w'][Hkv][d]
+  int Hq, Hkv, G;
+  int items;       // B * w' * Hkv
+};
+
 struct SelectParams {
   const float *scores;
   float *pooled;
@@ -78,6 +87,7 @@ struct GatherParams {
   int Hkv;
 };
 
+hipError_t launch_query_mean(const QueryMeanParams &p, hipStream_t s);
 hipError_t launch_score_pass1(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s);
 hipError_t launch_score_merge(const ScoreParams &p, const SegTable &t, hipStream_t s);  // key_block = pass 1's
 hipError_t launch_score_pass2(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s);

@@ -27,6 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 KVSEL_OK, KVSEL_EINVAL, KVSEL_EUNSUPPORTED, KVSEL_EHIP = 0, 1, 2, 3
 POOLS = {"none": 0, "avg": 1, "max": 2}
 WEIGHTINGS = {"alpha": 0, "exp": 1}
+GQAS = {"sum": 0, "mean": 1}
 
 
 class KvselProblem(ctypes.Structure):
@@ -53,6 +54,7 @@ class KvselProblem(ctypes.Structure):
         ("lambda_", ctypes.c_float),
         ("sink_tokens", ctypes.c_int32),
         ("recent_tokens", ctypes.c_int32),
+        ("gqa", ctypes.c_int32),
     ]
 
 
@@ -113,7 +115,7 @@ class Problem:
                  L: int = 0, batch: int = 1, has_decode: bool = False, alpha: float = 0.0, causal: bool = True,
                  scale: float = 0.0, pool: str = "none", pool_kernel: int = 1, k: int = 0,
                  budgets=None, key_chunk: int = 0, weighting: str = "alpha", lam: float = 0.0, sink: int = 0,
-                 recent: int = 0):
+                 recent: int = 0, gqa: str = "sum"):
         if seq_lens is None:
             seq_lens = [int(L)] * int(batch)
         self.seq_lens = [int(x) for x in seq_lens]
@@ -148,6 +150,7 @@ class Problem:
         s.lambda_ = float(lam)
         s.sink_tokens = int(sink)
         s.recent_tokens = int(recent)
+        s.gqa = GQAS[gqa] if isinstance(gqa, str) else int(gqa)
         self.struct = s
 
     @property

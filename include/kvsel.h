@@ -20,7 +20,9 @@
  *      of c_r * p_r[i] (TideKV §4.2, grouped-query aggregation at KV-head
  *      granularity); c_r = 1 without a decode row, else 1-alpha for prompt
  *      rows and alpha for the decode row (DeferKV Guide, Phase 2 weighting),
- *      or the guide's exponential temporal weights (enum kvsel_weighting);
+ *      or the guide's exponential temporal weights (enum kvsel_weighting).
+ *      With KVSEL_GQA_MEAN_QUERY the group's G heads are first averaged into
+ *      one query per row (enum kvsel_gqa) and the sum over heads drops out;
  *   5. a stride-1 1-D pool of odd width (avg: zero-padded sum / width; max:
  *      over in-range positions) -- not defined on the pages;
  *   6. top-k: the min(k_bh, L_b) positions with the largest pooled score,
@@ -105,6 +107,18 @@ typedef enum kvsel_weighting {
   KVSEL_WEIGHT_EXP = 1
 } kvsel_weighting;
 
+/* How the Hq/Hkv query heads of a KV head's group enter the score. */
+typedef enum kvsel_gqa {
+  /* A softmax per query head, then the sum over the group's heads (TideKV
+   * §4.2, scores aggregated at KV-head granularity). */
+  KVSEL_GQA_SUM = 0,
+  /* The DeferKV guide's shortcut (Phase 2 code): the group's queries are
+   * averaged into one query per observation row, the mean rounded to the
+   * nearest bf16 value (ties to even), and that row's softmax takes the
+   * place of the G heads' sum.  A different score, at 1/G of the work. */
+  KVSEL_GQA_MEAN_QUERY = 1
+} kvsel_gqa;
+
 /* Problem description, shared by every entry point.  Host memory. */
 typedef struct kvsel_problem {
   int32_t batch;                 /* B >= 1 sequences */
@@ -127,6 +141,7 @@ typedef struct kvsel_problem {
   float lambda;                  /* KVSEL_WEIGHT_EXP: finite, >= 0 (0 gives equal weights) */
   int32_t sink_tokens;           /* >= 0: positions 0 .. sink-1 of every sequence are always kept */
   int32_t recent_tokens;         /* >= 0: positions L_b-recent .. L_b-1 are always kept */
+  int32_t gqa;                   /* a kvsel_gqa value; 0 is KVSEL_GQA_SUM */
 } kvsel_problem;
 
 /* KVSEL_ABI_VERSION of the loaded library. */
@@ -161,7 +176,9 @@ kvsel_status kvsel_score(const kvsel_problem *p, const void *Q, const void *K, f
  * pass, which recomputes the logits and writes the aggregated scores S into
  * `scores`.  Calling kvsel_row_stats and then kvsel_score_from_stats on the
  * same stream, problem, inputs and workspace gives exactly the bytes of
- * kvsel_score; the workspace must not be used by any other call in between.
+ * kvsel_score; the workspace must not be used by any other call in between
+ * (with KVSEL_GQA_MEAN_QUERY it also carries the mean queries, which
+ * kvsel_row_stats forms and the second pass reads instead of Q).
  * Arguments and errors as for kvsel_score (kvsel_row_stats has no `scores`).
  */
 kvsel_status kvsel_row_stats(const kvsel_problem *p, const void *Q, const void *K, void *ws, size_t ws_bytes,

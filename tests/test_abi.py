@@ -75,6 +75,7 @@ BAD = {
     "lambda_inf": dict(weighting="exp", lam=float("inf")),
     "sink_negative": dict(sink=-1),
     "recent_negative": dict(recent=-2),
+    "gqa_unknown": dict(gqa=2),
 }
 
 
@@ -162,7 +163,7 @@ def test_struct_layout_matches_c():
 #define F(x) printf("%s %zu\n", #x, offsetof(kvsel_problem, x));
 int main(void) { F(batch) F(Hq) F(Hkv) F(d) F(L) F(seq_offsets_h) F(w) F(has_decode) F(alpha) F(causal)
   F(scale) F(pool) F(pool_kernel) F(k) F(budgets_h) F(key_chunk) F(weighting) F(lambda) F(sink_tokens)
-  F(recent_tokens) printf("size %zu\n", sizeof(kvsel_problem)); return 0; }
+  F(recent_tokens) F(gqa) printf("size %zu\n", sizeof(kvsel_problem)); return 0; }
 '''
     import tempfile
 

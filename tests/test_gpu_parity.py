@@ -283,10 +283,12 @@ def test_select_reserved_on_given_scores(kv, kind, sink, recent):
         np.testing.assert_array_equal(I[ooff:ooff + keff], ref)
 
 
-def test_deferkv_full_size(kv):
+@pytest.mark.parametrize("make", [W.deferkv_full, W.deferkv_guide_full], ids=["sum", "mean_query"])
+def test_deferkv_full_size(kv, make):
     """The guide's defaults on a 32K-key layer: exp weights (lambda 0.1) over
-    32 prompt rows and the decode row, 16 sinks and 32 recent kept."""
-    spec = W.deferkv_full()
+    32 prompt rows and the decode row, 16 sinks and 32 recent kept; with the
+    per-head sum, and with the guide's mean query per group."""
+    spec = make()
     heads = [(0, 0), (0, 5)]
     _say(f"{spec.name}: generating")
     case = W.make_case(spec, layer=0, device=DEV)

@@ -57,6 +57,7 @@ class Spec:
     lam: float = 0.0  # exp weighting: c_r proportional to exp(lam * r)
     sink: int = 0  # reserved prefix positions
     recent: int = 0  # reserved suffix positions
+    gqa: str = "sum"  # sum (per-head softmax, summed) | mean (one mean query per group)
     layers: int = 1
     recipe: str = "plant"  # plant | runs | zipf | decode_corr | plain | hand
     plant_frac: float = 0.02
@@ -216,6 +217,13 @@ def deferkv_full() -> Spec:
                 pool_kernel=7, k=2048, weighting="exp", lam=0.1, sink=16, recent=32, recipe="decode_corr")
 
 
+def deferkv_guide_full() -> Spec:
+    """The guide's whole recipe on the same layer: its defaults plus the
+    group's queries averaged into one query per row."""
+    return dataclasses.replace(deferkv_full(), name="deferkv_L32k_meanq_exp0.1_sink16_recent32_max7_k2048",
+                               gqa="mean")
+
+
 def small_cases():
     """Small shapes spanning several key tiles, ragged tails and edge cases."""
     cases = [
@@ -253,6 +261,12 @@ def small_cases():
              budgets=[[10, 40], [90, 3]], sink=8, recent=24, recipe="plant"),
         Spec("s_reserve_whole_seq", [2100], Hq=8, Hkv=2, w=8, has_decode=True, weighting="exp", lam=2.0,
              pool="max", pool_kernel=3, k=2090, sink=2100, recent=0, recipe="plain"),
+        # the guide's mean-query grouped attention
+        Spec("s_meanq_guide", [2500, 700], Hq=32, Hkv=8, w=32, has_decode=True, pool="max", pool_kernel=7, k=150,
+             weighting="exp", lam=0.1, sink=16, recent=32, gqa="mean", recipe="decode_corr"),
+        Spec("s_meanq_G3_alpha", [1000], Hq=12, Hkv=4, w=20, has_decode=True, alpha=0.5, pool="avg",
+             pool_kernel=5, k=90, gqa="mean", recipe="plant", plant_frac=0.03),
+        Spec("s_meanq_G1", [333], Hq=4, Hkv=4, w=5, pool="none", k=40, gqa="mean", recipe="plant"),
     ]
     return cases
 
@@ -263,7 +277,7 @@ def problem_kwargs(spec: Spec) -> dict:
                 has_decode=spec.has_decode, alpha=spec.alpha, causal=spec.causal, scale=spec.scale,
                 pool=spec.pool, pool_kernel=spec.pool_kernel, k=spec.k, budgets=spec.budgets,
                 key_chunk=spec.key_chunk, weighting=spec.weighting, lam=spec.lam, sink=spec.sink,
-                recent=spec.recent)
+                recent=spec.recent, gqa=spec.gqa)
 
 
 def oracle_kwargs(spec: Spec) -> dict:
@@ -271,4 +285,4 @@ def oracle_kwargs(spec: Spec) -> dict:
     return dict(seq_lens=list(spec.seq_lens), Hq=spec.Hq, Hkv=spec.Hkv, w=spec.w, has_decode=spec.has_decode,
                 alpha=spec.alpha, causal=spec.causal, scale=(spec.scale if spec.scale else None), pool=spec.pool,
                 pool_kernel=spec.pool_kernel, k=spec.k, budgets=spec.budgets, weighting=spec.weighting,
-                lam=spec.lam, sink=spec.sink, recent=spec.recent)
+                lam=spec.lam, sink=spec.sink, recent=spec.recent, gqa=spec.gqa)
