@@ -47,6 +47,15 @@ What it computes (one sequence ``b`` and one KV head ``h`` at a time):
    first, and the rest of the budget goes to the highest scores.
 8. Gather: the kept rows of K and V, copied exactly (TideKV §4.2 and §5).
 
+Also the warm-up placement of "KVDrive: A Holistic Multi-Tier KV Cache
+Management System for Long-Context LLM Inference" (§7.1, importance-guided
+warm-up): the aggregated scores of step 5, summed over the KV heads of a
+sequence and over the model's layers, give one importance value per prefix
+position (``importance_profile``); ranked by (descending importance,
+ascending position), the first ``n_fast`` positions go to the fastest tier
+(GPU memory), the next ``n_mid`` to the middle tier (host memory) and the
+rest stay in the backing store only (``tier_labels``).
+
 Query-head ``g`` belongs to KV head ``g // G`` with ``G = Hq // Hkv``
 (consecutive grouping, as the DeferKV guide's code reshapes the heads).
 
@@ -78,6 +87,8 @@ __all__ = [
     "blockwise_head_scores",
     "plan_offsets",
     "compress",
+    "importance_profile",
+    "tier_labels",
 ]
 
 
@@ -399,3 +410,48 @@ def compress(Q, K, V, *, seq_lens, Hq: int, Hkv: int, w: int, has_decode: bool =
                 "V_out": gather_rows(V_b, idx, h),
             }
     return res
+
+
+def importance_profile(layers, *, seq_lens, Hq: int, Hkv: int, w: int, has_decode: bool = False,
+                       alpha: float = 0.0, causal: bool = True, scale=None, weighting: str = "alpha",
+                       lam: float = 0.0, gqa: str = "sum"):
+    """KVDrive §7.1: the importance of every prefix position, the observation
+    rows' attention aggregated over all heads and all layers.
+
+    ``layers``: a list of ``(Q, K)`` pairs, one per layer, in the layouts of
+    :func:`compress` (float64 arrays holding the bf16 input values).  Each
+    layer contributes the aggregated score ``S`` of every KV head
+    (:func:`head_scores`); returns one float64 array of length ``L_b`` per
+    sequence with the sum over layers and KV heads.
+    """
+    B = len(seq_lens)
+    starts = np.concatenate([[0], np.cumsum(seq_lens)])
+    prof = [np.zeros(int(L)) for L in seq_lens]
+    for Q, K in layers:
+        Q = np.asarray(Q, dtype=np.float64)
+        K = np.asarray(K, dtype=np.float64)
+        _check_finite(Q, K)
+        sc = (1.0 / np.sqrt(K.shape[2])) if scale is None else scale
+        for b in range(B):
+            K_b = K[starts[b]:starts[b + 1]]
+            for h in range(Hkv):
+                prof[b] += head_scores(Q[b], K_b, h, Hkv, w=w, has_decode=has_decode, alpha=alpha,
+                                       causal=causal, scale=sc, weighting=weighting, lam=lam, gqa=gqa)
+    return prof
+
+
+def tier_labels(profile: np.ndarray, n_fast: int, n_mid: int, pool: str = "none", pool_kernel: int = 1):
+    """KVDrive §7.1 placement of one sequence: rank the (optionally pooled)
+    importance values, highest first and the lower position first among
+    equal values; rank < n_fast -> tier 0 (GPU memory), rank < n_fast + n_mid
+    -> tier 1 (host memory), otherwise tier 2 (the backing store only).
+    Returns int8 labels, one per position."""
+    P = pool1d(np.asarray(profile, dtype=np.float64), pool, pool_kernel)
+    L = len(P)
+    order = np.lexsort((np.arange(L), -P))  # last key first: descending value, then ascending position
+    rank = np.empty(L, dtype=np.int64)
+    rank[order] = np.arange(L)
+    labels = np.full(L, 2, dtype=np.int8)
+    labels[rank < int(n_fast) + int(n_mid)] = 1
+    labels[rank < int(n_fast)] = 0
+    return labels

@@ -446,6 +446,90 @@ def test_mean_query_equal_heads_is_sum_over_G():
                                O.head_scores(Q, K, 0, 1, gqa="sum", **kw) / G, rtol=1e-12)
 
 
+def test_tier_labels_hand():
+    """Importance 3, 1, 3, 2, 2, 0 ranks positions 0, 2, 3, 4, 1, 5 (equal
+    values: lower position first); two fast and two middle slots."""
+    prof = np.array([3.0, 1.0, 3.0, 2.0, 2.0, 0.0])
+    assert O.tier_labels(prof, 2, 2).tolist() == [0, 2, 0, 1, 1, 2]
+    assert O.tier_labels(prof, 1, 2).tolist() == [0, 2, 1, 1, 2, 2]
+    assert O.tier_labels(prof, 0, 3).tolist() == [1, 2, 1, 1, 2, 2]
+    assert O.tier_labels(prof, 6, 4).tolist() == [0] * 6
+    assert O.tier_labels(prof, 3, 100).tolist() == [0, 1, 0, 0, 1, 1]
+    # max pool of width 3: 3, 3, 3, 3, 2, 2 -> positions 0..3 tie at 3
+    assert O.tier_labels(prof, 2, 1, "max", 3).tolist() == [0, 0, 1, 2, 2, 2]
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_tier_labels_invariants(seed):
+    """Tier sizes are min(n_fast, L), then min(n_mid, rest); every fast value
+    is >= every middle value >= every backing-store value."""
+    rng = np.random.default_rng(seed)
+    L = 500
+    prof = rng.integers(0, 20, L).astype(np.float64)  # many ties
+    for nf, nm in ((0, 0), (10, 40), (123, 0), (499, 5), (600, 1)):
+        lab = O.tier_labels(prof, nf, nm)
+        n0 = min(nf, L)
+        n1 = min(nm, L - n0)
+        assert (lab == 0).sum() == n0 and (lab == 1).sum() == n1 and (lab == 2).sum() == L - n0 - n1
+        for a, b in ((0, 1), (1, 2), (0, 2)):
+            if (lab == a).any() and (lab == b).any():
+                lo = prof[lab == a].min()
+                hi = prof[lab == b].max()
+                assert lo >= hi
+                # at a tie across the boundary the lower positions sit in the faster tier
+                if lo == hi:
+                    assert np.nonzero((lab == a) & (prof == lo))[0].max() < np.nonzero((lab == b) & (prof == hi))[0].min()
+
+
+def test_importance_profile_mass():
+    """Each KV head's score sums to G times the row weights' sum (every row is
+    a distribution), so a profile over n layers sums to n * Hq * sum(c_r)."""
+    rng = np.random.default_rng(4)
+    seq_lens = [90, 41]
+    Hq, Hkv, w = 8, 2, 5
+    layers = []
+    for _ in range(3):
+        Q = rng.standard_normal((2, w + 1, Hq, 128))
+        K = rng.standard_normal((sum(seq_lens), Hkv, 128)) / np.sqrt(128)
+        layers.append((Q, K))
+    prof = O.importance_profile(layers, seq_lens=seq_lens, Hq=Hq, Hkv=Hkv, w=w, has_decode=True, alpha=0.25)
+    for b, L in enumerate(seq_lens):
+        assert prof[b].shape == (L,)
+        assert abs(prof[b].sum() - 3 * Hq * (w * 0.75 + 0.25)) < 1e-9
+
+
+def test_importance_profile_hand():
+    """Hand keys.  Layer 1: KV head 0 with the query +1 and KV head 1 with the
+    query -1, one window row at position 7 (G = 1): together the worked
+    example's two-row score.  Layer 2: zero queries, 1/8 per key and head."""
+    j = _hand()
+    s_ex3 = np.array([0.352457, 0.221802, 0.221802, 0.186076, 0.221802, 0.221802, 0.221802, 0.352457])
+    K = np.zeros((8, 2, 128))
+    K[:, :, 0] = np.asarray(j["keys_c0"])[:, None]
+    Q1 = np.zeros((1, 1, 2, 128))
+    Q1[0, 0, 0, 0] = 1.0
+    Q1[0, 0, 1, 0] = -1.0
+    Q2 = np.zeros((1, 1, 2, 128))
+    prof = O.importance_profile([(Q1, K), (Q2, K)], seq_lens=[8], Hq=2, Hkv=2, w=1, scale=1.0)[0]
+    np.testing.assert_allclose(prof, s_ex3 + 2 * 0.125, atol=3e-6)
+
+
+def test_importance_profile_zero_queries():
+    """Zero queries make every row uniform over its visible keys: a causal
+    window row at position p adds 1/(p+1) to keys 0..p, the decode row 1/L to
+    every key; summed over Hq query heads and the layers."""
+    L, w, Hq, Hkv = 12, 3, 4, 2
+    Q = np.zeros((1, w + 1, Hq, 128))
+    K = np.random.default_rng(0).standard_normal((L, Hkv, 128))
+    prof = O.importance_profile([(Q, K), (Q, K)], seq_lens=[L], Hq=Hq, Hkv=Hkv, w=w, has_decode=True,
+                                alpha=0.5)[0]
+    want = np.zeros(L)
+    for p in range(L - w, L):
+        want[:p + 1] += 0.5 / (p + 1)
+    want += 0.5 / L
+    np.testing.assert_allclose(prof, 2 * Hq * want, rtol=1e-12)
+
+
 # ---------------------------------------------------------------- planted mistakes
 def _pins_pass():
     """Run the pins above in-process; return False as soon as one fails."""
@@ -468,6 +552,11 @@ def _pins_pass():
         test_mean_query_matches_torch_bf16_mean,
         test_mean_query_hand_groups,
         test_mean_query_equal_heads_is_sum_over_G,
+        test_tier_labels_hand,
+        lambda: [test_tier_labels_invariants(s) for s in range(2)],
+        test_importance_profile_mass,
+        test_importance_profile_hand,
+        test_importance_profile_zero_queries,
     ]
     for c in checks:
         try:
@@ -539,6 +628,43 @@ def _mean_query_strided(Q_b, h, G):
     return O.round_to_bf16(Q_b[:, h::Hkv, :].mean(axis=1))
 
 
+def _tiers_high_index_ties(profile, n_fast, n_mid, pool="none", pool_kernel=1):
+    P = O.pool1d(np.asarray(profile, dtype=np.float64), pool, pool_kernel)
+    L = len(P)
+    order = np.lexsort((-np.arange(L), -P))
+    rank = np.empty(L, dtype=np.int64)
+    rank[order] = np.arange(L)
+    lab = np.full(L, 2, dtype=np.int8)
+    lab[rank < n_fast + n_mid] = 1
+    lab[rank < n_fast] = 0
+    return lab
+
+
+def _tiers_mid_counts_from_zero(profile, n_fast, n_mid, pool="none", pool_kernel=1):
+    P = O.pool1d(np.asarray(profile, dtype=np.float64), pool, pool_kernel)
+    L = len(P)
+    order = np.lexsort((np.arange(L), -P))
+    rank = np.empty(L, dtype=np.int64)
+    rank[order] = np.arange(L)
+    lab = np.full(L, 2, dtype=np.int8)
+    lab[rank < n_mid] = 1  # the middle tier's slots not offset by the fast tier's
+    lab[rank < n_fast] = 0
+    return lab
+
+
+def _profile_one_head(layers, *, seq_lens, Hq, Hkv, w, has_decode=False, alpha=0.0, causal=True, scale=None,
+                      weighting="alpha", lam=0.0, gqa="sum"):
+    starts = np.concatenate([[0], np.cumsum(seq_lens)])
+    prof = [np.zeros(int(L)) for L in seq_lens]
+    for Q, K in layers:
+        sc = (1.0 / np.sqrt(K.shape[2])) if scale is None else scale
+        for b in range(len(seq_lens)):
+            prof[b] += Hkv * O.head_scores(Q[b], K[starts[b]:starts[b + 1]], 0, Hkv, w=w, has_decode=has_decode,
+                                           alpha=alpha, causal=causal, scale=sc, weighting=weighting, lam=lam,
+                                           gqa=gqa)
+    return prof
+
+
 def _avg_exclude_pad(S, kind, kernel):
     if kind != "avg":
         return O.pool1d.__wrapped__(S, kind, kernel)
@@ -577,6 +703,9 @@ MUTATIONS = {
     "bf16_rounding_truncates": ("round_to_bf16", _bf16_truncate),
     "mean_query_not_rounded": ("mean_query_rows", _mean_query_unrounded),
     "mean_query_strided_groups": ("mean_query_rows", _mean_query_strided),
+    "tiers_ties_to_higher_index": ("tier_labels", _tiers_high_index_ties),
+    "tiers_middle_not_offset": ("tier_labels", _tiers_mid_counts_from_zero),
+    "profile_head_0_times_Hkv": ("importance_profile", _profile_one_head),
 }
 
 
