@@ -16,7 +16,9 @@ from .kvsel import (  # noqa: F401
     kvsel_gather,
     kvsel_plan,
     kvsel_pool_topk,
+    kvsel_profile_layer,
     kvsel_row_stats,
     kvsel_score,
     kvsel_score_from_stats,
+    kvsel_tier_rank,
 )

@@ -485,3 +485,91 @@ KVSEL_API kvsel_status kvsel_compress(const kvsel_problem *p, const void *Q, con
   if (any_kept(P)) return run_select(P, scores, pool_buf, idx, wsb, st, K, V, K_out, V_out);
   return run_select(P, scores, pool_buf, idx, wsb, st);
 }
+
+namespace {
+
+// The ranking of a warm-up profile as a selection problem: one segment per
+// sequence (a single "head"), budget min(n, L_b), no reserved positions.
+Plan tier_plan(const Plan &P, int64_t n) {
+  Plan V = P;
+  V.Hkv = 1;
+  V.sink = 0;
+  V.recent = 0;
+  V.keff.assign((size_t)P.B, 0);
+  V.out_off.assign((size_t)P.B + 1, 0);
+  for (int b = 0; b < P.B; ++b) {
+    const int64_t Lb = P.seq_off[b + 1] - P.seq_off[b];
+    V.keff[b] = (int32_t)std::min<int64_t>(n, Lb);
+    V.out_off[b + 1] = V.out_off[b] + V.keff[b];
+  }
+  return V;
+}
+
+}  // namespace
+
+KVSEL_API kvsel_status kvsel_profile_layer(const kvsel_problem *p, const void *Q, const void *K, float *profile,
+                                           int32_t accumulate, void *ws, size_t ws_bytes, kvsel_stream_t stream) {
+  g_last_error.clear();
+  Plan P;
+  kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = check_ptr(Q, "Q");
+  if (s == KVSEL_OK) s = check_ptr(K, "K");
+  if (s == KVSEL_OK) s = check_ptr(profile, "profile");
+  if (s == KVSEL_OK && accumulate != 0 && accumulate != 1) s = fail(KVSEL_EINVAL, "accumulate must be 0 or 1");
+  if (s == KVSEL_OK) s = check_ws(P, ws, ws_bytes);
+  if (s == KVSEL_OK) s = check_device();
+  if (s != KVSEL_OK) return s;
+  char *wsb = static_cast<char *>(ws);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float *scores = reinterpret_cast<float *>(wsb + P.off_scores);
+  s = run_score(P, Q, K, scores, wsb, st);
+  if (s != KVSEL_OK) return s;
+  ProfileParams pp;
+  pp.scores = scores;
+  pp.profile = profile;
+  pp.Hkv = P.Hkv;
+  pp.accumulate = accumulate;
+  return for_each_group(P, [&](const SegTable &t, int64_t lmax) {
+    hipError_t e = launch_profile(pp, t, lmax, st);
+    if (e != hipSuccess) return hip_fail(e, "profile launch");
+    return KVSEL_OK;
+  });
+}
+
+KVSEL_API kvsel_status kvsel_tier_rank(const kvsel_problem *p, const float *profile, int64_t n_fast, int64_t n_mid,
+                                       int8_t *tier, void *ws, size_t ws_bytes, kvsel_stream_t stream) {
+  g_last_error.clear();
+  Plan P;
+  kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = check_ptr(profile, "profile");
+  if (s == KVSEL_OK) s = check_ptr(tier, "tier");
+  if (s == KVSEL_OK && (n_fast < 0 || n_mid < 0)) s = fail(KVSEL_EINVAL, "n_fast and n_mid must be >= 0");
+  if (s == KVSEL_OK) s = check_ws(P, ws, ws_bytes);
+  if (s == KVSEL_OK) s = check_device();
+  if (s != KVSEL_OK) return s;
+  char *wsb = static_cast<char *>(ws);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // The selection's positions go where the per-head scores would live; the
+  // pooled profile where the pooled scores would.  Both regions hold at
+  // least sum L_b four-byte values.
+  int32_t *idx = reinterpret_cast<int32_t *>(wsb + P.off_scores);
+  float *pooled = reinterpret_cast<float *>(wsb + P.off_pooled);
+  hipError_t e = launch_tier_fill(tier, P.seq_off[P.B], st);
+  if (e != hipSuccess) return hip_fail(e, "tier fill launch");
+  const int64_t cap = P.Lmax;  // a budget beyond the longest sequence keeps everything
+  const int64_t ranks[2] = {std::min(cap, n_fast) + std::min(cap, n_mid), std::min(cap, n_fast)};
+  for (int pass = 0; pass < 2; ++pass) {
+    const Plan V = tier_plan(P, ranks[pass]);
+    if (!any_kept(V)) continue;
+    s = run_select(V, profile, pooled, idx, wsb, st);
+    if (s != KVSEL_OK) return s;
+    const int label = 1 - pass;  // the middle tier's selection first, then the fast tier's
+    s = for_each_group(V, [&](const SegTable &t, int64_t) {
+      hipError_t e2 = launch_tier_mark(idx, tier, label, t, st);
+      if (e2 != hipSuccess) return hip_fail(e2, "tier mark launch");
+      return KVSEL_OK;
+    });
+    if (s != KVSEL_OK) return s;
+  }
+  return KVSEL_OK;
+}

@@ -78,6 +78,14 @@ struct SelectParams {
   uint4 *V_out;
 };
 
+// Warm-up profile: per sequence, the sum over KV heads of the scores.
+struct ProfileParams {
+  const float *scores;  // layout of the public ABI: segment (b, h) at Hkv * key_off[b] + h * L_b
+  float *profile;       // [sum L], sequence b at key_off[b]
+  int Hkv;
+  int accumulate;       // 1: add to the profile; 0: overwrite it
+};
+
 struct GatherParams {
   const int32_t *idx;
   const uint4 *K;   // rows of d bf16 = 16 x uint4
@@ -88,6 +96,9 @@ struct GatherParams {
 };
 
 hipError_t launch_query_mean(const QueryMeanParams &p, hipStream_t s);
+hipError_t launch_profile(const ProfileParams &p, const SegTable &t, int64_t lmax, hipStream_t s);
+hipError_t launch_tier_fill(int8_t *tier, int64_t n, hipStream_t s);
+hipError_t launch_tier_mark(const int32_t *idx, int8_t *tier, int label, const SegTable &t, hipStream_t s);
 hipError_t launch_score_pass1(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s);
 hipError_t launch_score_merge(const ScoreParams &p, const SegTable &t, hipStream_t s);  // key_block = pass 1's
 hipError_t launch_score_pass2(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s);

@@ -78,6 +78,10 @@ _lib.kvsel_gather.restype = ctypes.c_int
 _lib.kvsel_gather.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.kvsel_compress.restype = ctypes.c_int
 _lib.kvsel_compress.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.kvsel_profile_layer.restype = ctypes.c_int
+_lib.kvsel_profile_layer.argtypes = [_P, _vp, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
+_lib.kvsel_tier_rank.restype = ctypes.c_int
+_lib.kvsel_tier_rank.argtypes = [_P, _vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp, ctypes.c_size_t, _vp]
 
 
 class KvselError(RuntimeError):
@@ -296,6 +300,31 @@ def kvsel_compress(problem: Problem, Q, K, V, idx, K_out, V_out, pooled, ws, str
     with torch.cuda.device(dev):
         _check(_lib.kvsel_compress(problem.ref(), *args, ctypes.c_size_t(ws.numel()), _stream(stream, dev)),
                "kvsel_compress")
+
+def kvsel_profile_layer(problem: Problem, Q, K, profile, ws, accumulate: bool = False, stream=None):
+    """One layer's contribution to the warm-up importance profile [sum L]."""
+    torch = _torch()
+    n = _sizes(problem)
+    dev = K.device
+    args = (_ptr(Q, "Q", torch.bfloat16, n["Q"], dev), _ptr(K, "K", torch.bfloat16, n["K"], dev),
+            _ptr(profile, "profile", torch.float32, problem.total_keys, dev), ctypes.c_int32(int(accumulate)),
+            _ptr(ws, "ws", torch.uint8, n["ws"], dev))
+    with torch.cuda.device(dev):
+        _check(_lib.kvsel_profile_layer(problem.ref(), *args, ctypes.c_size_t(ws.numel()), _stream(stream, dev)),
+               "kvsel_profile_layer")
+
+
+def kvsel_tier_rank(problem: Problem, profile, n_fast: int, n_mid: int, tier, ws, stream=None):
+    """Three-tier labels (int8 [sum L]: 0 fast, 1 middle, 2 backing) from the profile."""
+    torch = _torch()
+    n = _sizes(problem)
+    dev = profile.device
+    args = (_ptr(profile, "profile", torch.float32, problem.total_keys, dev), ctypes.c_int64(int(n_fast)),
+            ctypes.c_int64(int(n_mid)), _ptr(tier, "tier", torch.int8, problem.total_keys, dev),
+            _ptr(ws, "ws", torch.uint8, n["ws"], dev))
+    with torch.cuda.device(dev):
+        _check(_lib.kvsel_tier_rank(problem.ref(), *args, ctypes.c_size_t(ws.numel()), _stream(stream, dev)),
+               "kvsel_tier_rank")
 
 
 def alloc_outputs(problem: Problem, device, pooled: bool = True):

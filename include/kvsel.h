@@ -211,6 +211,38 @@ kvsel_status kvsel_compress(const kvsel_problem *p, const void *Q, const void *K
                             int32_t *idx, void *K_out, void *V_out, float *pooled,
                             void *ws, size_t ws_bytes, kvsel_stream_t stream);
 
+/*
+ * Importance-guided warm-up (KVDrive, "A Holistic Multi-Tier KV Cache
+ * Management System for Long-Context LLM Inference", §7.1): the observation
+ * rows' attention over every prefix key, aggregated over the heads and the
+ * layers of the model, ranks the prefix positions for placement in memory
+ * tiers.
+ *
+ * kvsel_profile_layer: steps 1-4 for one layer's Q and K, then the sum of
+ * S over the KV heads of each sequence, written to `profile` (accumulate =
+ * 0) or added to it (accumulate = 1).  Calling it once per layer (the first
+ * with 0) sums over the layers.  profile: device fp32 [sum_b L_b], sequence
+ * b at seq_offsets[b], 16-byte aligned.  Every field of *p applies as for
+ * kvsel_score; budgets, pool and reserved positions are not used.
+ *
+ * kvsel_tier_rank: pools the profile with the problem's pool kind and
+ * width, ranks the positions of each sequence by descending pooled value
+ * (the lower position first among equal values), and writes one label per
+ * position to `tier` (device int8 [sum_b L_b], 16-byte aligned): 0 for the
+ * first n_fast positions (GPU memory), 1 for the next n_mid (host memory),
+ * 2 for the rest (the backing store only).  n_fast, n_mid >= 0; the tiers
+ * simply run out on short sequences.  The problem's budgets, heads,
+ * reserved positions and query fields are not used, but *p must be valid;
+ * ws must hold kvsel_plan's size for *p.
+ *
+ * Errors as for kvsel_score; KVSEL_EINVAL also for accumulate not 0 or 1
+ * and for a negative n_fast or n_mid.
+ */
+kvsel_status kvsel_profile_layer(const kvsel_problem *p, const void *Q, const void *K, float *profile,
+                                 int32_t accumulate, void *ws, size_t ws_bytes, kvsel_stream_t stream);
+kvsel_status kvsel_tier_rank(const kvsel_problem *p, const float *profile, int64_t n_fast, int64_t n_mid,
+                             int8_t *tier, void *ws, size_t ws_bytes, kvsel_stream_t stream);
+
 /* Static text for a status code. */
 const char *kvsel_status_string(kvsel_status s);
 

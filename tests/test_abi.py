@@ -139,6 +139,14 @@ def test_entry_points_validate_before_device():
     assert lib.kvsel_pool_topk(p.ref(), A, None, None, A, sz, None) == kv.KVSEL_EINVAL
     assert lib.kvsel_gather(p.ref(), A, A, None, A, A, None) == kv.KVSEL_EINVAL
     assert lib.kvsel_compress(p.ref(), A, A, A, A, A, None, None, A, sz, None) == kv.KVSEL_EINVAL
+    assert lib.kvsel_profile_layer(p.ref(), A, A, None, 0, A, sz, None) == kv.KVSEL_EINVAL
+    assert lib.kvsel_profile_layer(p.ref(), A, A, A, 2, A, sz, None) == kv.KVSEL_EINVAL
+    assert b"accumulate" in lib.kvsel_last_error()
+    assert lib.kvsel_profile_layer(p.ref(), A, A, A, 1, A, ctypes.c_size_t(ws - 1), None) == kv.KVSEL_EINVAL
+    assert lib.kvsel_tier_rank(p.ref(), A, 1, 1, None, A, sz, None) == kv.KVSEL_EINVAL
+    assert lib.kvsel_tier_rank(p.ref(), A, -1, 1, A, A, sz, None) == kv.KVSEL_EINVAL
+    assert lib.kvsel_tier_rank(p.ref(), A, 1, -5, A, A, sz, None) == kv.KVSEL_EINVAL
+    assert lib.kvsel_tier_rank(p.ref(), ctypes.c_void_p(a + 4), 1, 1, A, A, sz, None) == kv.KVSEL_EINVAL
     if not os.path.exists("/dev/kfd"):
         st = lib.kvsel_score(p.ref(), A, A, A, A, sz, None)
         assert st == kv.KVSEL_EHIP
