@@ -56,6 +56,14 @@ ascending position), the first ``n_fast`` positions go to the fastest tier
 (GPU memory), the next ``n_mid`` to the middle tier (host memory) and the
 rest stay in the backing store only (``tier_labels``).
 
+And adaptive budgets: KVDrive's 2-D window scaling (§5.2) chooses one size
+per (layer, head) from a few candidates to maximise the summed benefit under
+a total memory budget, with a greedy rule that starts every pair at its
+smallest size and repeatedly enlarges the pair whose next step has the
+highest benefit-to-cost ratio (``greedy_allocate``).  Here a pair's size is
+its KV budget ``k`` (cost ``k`` entries) and its benefit the importance it
+keeps, the sum of its ``k`` largest pooled scores (``topk_mass``).
+
 Query-head ``g`` belongs to KV head ``g // G`` with ``G = Hq // Hkv``
 (consecutive grouping, as the DeferKV guide's code reshapes the heads).
 
@@ -89,6 +97,8 @@ __all__ = [
     "compress",
     "importance_profile",
     "tier_labels",
+    "topk_mass",
+    "greedy_allocate",
 ]
 
 
@@ -455,3 +465,48 @@ def tier_labels(profile: np.ndarray, n_fast: int, n_mid: int, pool: str = "none"
     labels[rank < int(n_fast) + int(n_mid)] = 1
     labels[rank < int(n_fast)] = 0
     return labels
+
+
+def topk_mass(P: np.ndarray, sizes) -> np.ndarray:
+    """Importance kept by a budget: for each candidate ``k`` in ``sizes``, the
+    sum of the ``min(k, L)`` largest values of ``P``."""
+    desc = np.sort(np.asarray(P, dtype=np.float64))[::-1]
+    cum = np.concatenate([[0.0], np.cumsum(desc)])
+    return np.array([cum[min(int(k), len(desc))] for k in sizes])
+
+
+def greedy_allocate(benefit, sizes, total: int) -> np.ndarray:
+    """KVDrive §5.2's greedy for the multiple-choice knapsack.
+
+    ``benefit`` [items][len(sizes)]: benefit of each candidate size (sizes
+    ascending, the cost of a size is the size itself); ``total``: the budget.
+    Every item starts at its smallest size.  While some item's next size
+    fits the remaining budget and adds benefit, the one with the largest
+    (added benefit) / (added cost) is enlarged by one step; equal ratios go to
+    the lower item index.  Returns the chosen size index of every item
+    (all 0 if even the smallest sizes exceed the budget).
+    """
+    benefit = np.asarray(benefit, dtype=np.float64)
+    sizes = [int(x) for x in sizes]
+    n = benefit.shape[0]
+    choice = np.zeros(n, dtype=np.int64)
+    left = int(total) - n * sizes[0]
+    if left < 0:
+        return choice
+    while True:
+        best, best_ratio = -1, 0.0
+        for i in range(n):
+            j = choice[i]
+            if j + 1 >= len(sizes):
+                continue
+            dc = sizes[j + 1] - sizes[j]
+            db = benefit[i, j + 1] - benefit[i, j]
+            if dc > left or db <= 0.0:
+                continue
+            ratio = db / dc if dc > 0 else np.inf
+            if ratio > best_ratio:
+                best, best_ratio = i, ratio
+        if best < 0:
+            return choice
+        left -= sizes[choice[best] + 1] - sizes[choice[best]]
+        choice[best] += 1

@@ -530,6 +530,57 @@ def test_importance_profile_zero_queries():
     np.testing.assert_allclose(prof, 2 * Hq * want, rtol=1e-12)
 
 
+def test_topk_mass_hand_and_brute_force():
+    P = np.array([0.5, 2.0, 1.0, 2.0, 0.25])
+    np.testing.assert_array_equal(O.topk_mass(P, [0, 1, 2, 3, 5, 9]), [0.0, 2.0, 4.0, 5.0, 5.75, 5.75])
+    rng = np.random.default_rng(2)
+    P = rng.random(9)
+    for k in range(10):
+        best = max((sum(P[list(c)]) for c in itertools.combinations(range(9), k)), default=0.0)
+        assert abs(O.topk_mass(P, [k])[0] - best) < 1e-12
+
+
+def test_greedy_allocate_hand():
+    """Sizes 0, 2, 4 (cost = size).  Item 0 gains 5 then 1; item 1 gains 3
+    then 3; item 2 gains 1 then 10.  Budget 6: ratios 2.5, 1.5, 0.5 -> item 0
+    to size 2; then 0.5, 1.5, 0.5 -> item 1; then 0.5, 1.5, 0.5 -> item 1 to
+    size 4; budget spent.  The optimum (item 0 to 2, item 2 to 4: 5 + 11 = 16)
+    beats the greedy's 5 + 6 = 11, which pins the greedy rule itself."""
+    benefit = [[0, 5, 6], [0, 3, 6], [0, 1, 11]]
+    assert O.greedy_allocate(benefit, [0, 2, 4], 6).tolist() == [1, 2, 0]
+    assert O.greedy_allocate(benefit, [0, 2, 4], 1).tolist() == [0, 0, 0]  # no step fits
+    assert O.greedy_allocate(benefit, [0, 2, 4], 100).tolist() == [2, 2, 2]
+    assert O.greedy_allocate(benefit, [1, 2, 4], 2).tolist() == [0, 0, 0]  # smallest sizes over budget
+    # equal ratios: the lower item index first
+    assert O.greedy_allocate([[0, 4], [0, 4]], [0, 2], 2).tolist() == [1, 0]
+    # unequal step costs (sizes 0, 1, 3): item 0's second step adds more (0.7)
+    # but at a lower ratio (0.35) than item 1's first step (0.5 per entry)
+    assert O.greedy_allocate([[0, 1.0, 1.7], [0, 0.5, 0.6]], [0, 1, 3], 3).tolist() == [1, 1]
+    # the best ratio (item 1's second step, 1.5) does not fit the 1 entry left;
+    # the best step that fits (item 0's first) is taken instead
+    assert O.greedy_allocate([[0, 0.1, 10], [0, 0.5, 5.0]], [0, 1, 4], 2).tolist() == [1, 1]
+    # a step that adds nothing is not taken
+    assert O.greedy_allocate([[0, 0, 0], [0, 1, 1]], [0, 1, 2], 10).tolist() == [0, 1]
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_greedy_allocate_optimal_on_concave_uniform_steps(seed):
+    """With equal size steps and concave benefits (top-k masses are: each step
+    adds the next-largest values), the greedy is the exhaustive optimum."""
+    rng = np.random.default_rng(seed)
+    sizes = [0, 3, 6, 9, 12]
+    items = 4
+    benefit = np.stack([O.topk_mass(rng.random(12) ** 3, sizes) for _ in range(items)])
+    for total in (0, 5, 9, 17, 30, 48):
+        got = O.greedy_allocate(benefit, sizes, total)
+        value = sum(benefit[i, got[i]] for i in range(items))
+        assert sum(sizes[j] for j in got) <= total
+        best = max(sum(benefit[i, c[i]] for i in range(items))
+                   for c in itertools.product(range(len(sizes)), repeat=items)
+                   if sum(sizes[j] for j in c) <= total)
+        assert abs(value - best) < 1e-12
+
+
 # ---------------------------------------------------------------- planted mistakes
 def _pins_pass():
     """Run the pins above in-process; return False as soon as one fails."""
@@ -557,6 +608,9 @@ def _pins_pass():
         test_importance_profile_mass,
         test_importance_profile_hand,
         test_importance_profile_zero_queries,
+        test_topk_mass_hand_and_brute_force,
+        test_greedy_allocate_hand,
+        lambda: [test_greedy_allocate_optimal_on_concave_uniform_steps(s) for s in range(2)],
     ]
     for c in checks:
         try:
@@ -665,6 +719,54 @@ def _profile_one_head(layers, *, seq_lens, Hq, Hkv, w, has_decode=False, alpha=0
     return prof
 
 
+def _mass_ascending(P, sizes):
+    asc = np.sort(np.asarray(P, dtype=np.float64))
+    cum = np.concatenate([[0.0], np.cumsum(asc)])
+    return np.array([cum[min(int(k), len(asc))] for k in sizes])
+
+
+def _greedy_by_benefit_not_ratio(benefit, sizes, total):
+    benefit = np.asarray(benefit, dtype=np.float64)
+    n = benefit.shape[0]
+    choice = np.zeros(n, dtype=np.int64)
+    left = int(total) - n * sizes[0]
+    if left < 0:
+        return choice
+    while True:
+        best, best_gain = -1, 0.0
+        for i in range(n):
+            j = choice[i]
+            if j + 1 >= len(sizes) or sizes[j + 1] - sizes[j] > left:
+                continue
+            gain = benefit[i, j + 1] - benefit[i, j]
+            if gain > best_gain:
+                best, best_gain = i, gain
+        if best < 0:
+            return choice
+        left -= sizes[choice[best] + 1] - sizes[choice[best]]
+        choice[best] += 1
+
+
+def _greedy_stops_at_first_misfit(benefit, sizes, total):
+    benefit = np.asarray(benefit, dtype=np.float64)
+    n = benefit.shape[0]
+    choice = np.zeros(n, dtype=np.int64)
+    left = int(total) - n * sizes[0]
+    while left >= 0:
+        cands = [((benefit[i, choice[i] + 1] - benefit[i, choice[i]]) / (sizes[choice[i] + 1] - sizes[choice[i]]), -i)
+                 for i in range(n) if choice[i] + 1 < len(sizes)]
+        if not cands:
+            break
+        r, mi = max(cands)
+        i = -mi
+        dc = sizes[choice[i] + 1] - sizes[choice[i]]
+        if r <= 0 or dc > left:
+            break
+        left -= dc
+        choice[i] += 1
+    return choice
+
+
 def _avg_exclude_pad(S, kind, kernel):
     if kind != "avg":
         return O.pool1d.__wrapped__(S, kind, kernel)
@@ -706,6 +808,9 @@ MUTATIONS = {
     "tiers_ties_to_higher_index": ("tier_labels", _tiers_high_index_ties),
     "tiers_middle_not_offset": ("tier_labels", _tiers_mid_counts_from_zero),
     "profile_head_0_times_Hkv": ("importance_profile", _profile_one_head),
+    "mass_of_smallest_values": ("topk_mass", _mass_ascending),
+    "greedy_by_gain_not_ratio": ("greedy_allocate", _greedy_by_benefit_not_ratio),
+    "greedy_stops_at_first_misfit": ("greedy_allocate", _greedy_stops_at_first_misfit),
 }
 
 
