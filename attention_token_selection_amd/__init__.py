@@ -12,6 +12,7 @@ from .kvsel import (  # noqa: F401
     bind_compress,
     compress,
     exported_functions,
+    kvsel_allocate_budgets,
     kvsel_compress,
     kvsel_gather,
     kvsel_plan,
@@ -21,4 +22,5 @@ from .kvsel import (  # noqa: F401
     kvsel_score,
     kvsel_score_from_stats,
     kvsel_tier_rank,
+    kvsel_topk_mass,
 )

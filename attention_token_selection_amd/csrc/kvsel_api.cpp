@@ -573,3 +573,99 @@ KVSEL_API kvsel_status kvsel_tier_rank(const kvsel_problem *p, const float *prof
   }
   return KVSEL_OK;
 }
+
+KVSEL_API kvsel_status kvsel_topk_mass(const kvsel_problem *p, const float *pooled, int32_t n_sizes,
+                                       const int32_t *sizes_h, float *mass, void *ws, size_t ws_bytes,
+                                       kvsel_stream_t stream) {
+  g_last_error.clear();
+  Plan P;
+  kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = check_ptr(pooled, "pooled");
+  if (s == KVSEL_OK) s = check_ptr(mass, "mass");
+  if (s == KVSEL_OK && (n_sizes < 1 || !sizes_h)) s = fail(KVSEL_EINVAL, "need n_sizes >= 1 candidate sizes");
+  for (int j = 0; s == KVSEL_OK && j < n_sizes; ++j)
+    if (sizes_h[j] < 0) s = fail(KVSEL_EINVAL, "sizes must be >= 0");
+  if (s == KVSEL_OK) s = check_ws(P, ws, ws_bytes);
+  if (s == KVSEL_OK) s = check_device();
+  if (s != KVSEL_OK) return s;
+  char *wsb = static_cast<char *>(ws);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // Kept positions where the unpooled scores would live (at most sum L_b * Hkv).
+  int32_t *idx = reinterpret_cast<int32_t *>(wsb + P.off_scores);
+  float *copy = reinterpret_cast<float *>(wsb + P.off_pooled);
+  for (int j = 0; j < n_sizes; ++j) {
+    // The given pooled scores, unpooled again, with the uniform budget
+    // sizes_h[j] and no reserved positions.
+    Plan V = P;
+    V.pool = KVSEL_POOL_NONE;
+    V.pool_kernel = 1;
+    V.sink = 0;
+    V.recent = 0;
+    for (int b = 0; b < P.B; ++b) {
+      const int64_t Lb = P.seq_off[b + 1] - P.seq_off[b];
+      for (int h = 0; h < P.Hkv; ++h) {
+        const size_t sg = (size_t)b * P.Hkv + h;
+        V.keff[sg] = (int32_t)std::min<int64_t>(sizes_h[j], Lb);
+        V.out_off[sg + 1] = V.out_off[sg] + V.keff[sg];
+      }
+    }
+    s = run_select(V, pooled, copy, idx, wsb, st);
+    if (s != KVSEL_OK) return s;
+    MassParams mp;
+    mp.pooled = pooled;
+    mp.idx = idx;
+    mp.mass = mass;
+    mp.Hkv = P.Hkv;
+    mp.n_sizes = n_sizes;
+    mp.j = j;
+    s = for_each_group(V, [&](const SegTable &t, int64_t) {
+      hipError_t e = launch_mass(mp, t, st);
+      if (e != hipSuccess) return hip_fail(e, "mass launch");
+      return KVSEL_OK;
+    });
+    if (s != KVSEL_OK) return s;
+  }
+  return KVSEL_OK;
+}
+
+KVSEL_API kvsel_status kvsel_allocate_budgets(int32_t n_items, int32_t n_sizes, const int32_t *sizes_h,
+                                              const double *benefit_h, int64_t total, int32_t *budgets_h) {
+  g_last_error.clear();
+  if (n_items < 0 || n_sizes < 1) return fail(KVSEL_EINVAL, "need n_items >= 0 and n_sizes >= 1");
+  if (n_items == 0) return KVSEL_OK;
+  if (!sizes_h || !benefit_h || !budgets_h) return fail(KVSEL_EINVAL, "NULL argument");
+  for (int j = 0; j < n_sizes; ++j) {
+    if (sizes_h[j] < 0) return fail(KVSEL_EINVAL, "sizes must be >= 0");
+    if (j > 0 && sizes_h[j] <= sizes_h[j - 1]) return fail(KVSEL_EINVAL, "sizes must be strictly increasing");
+  }
+  for (int64_t i = 0; i < (int64_t)n_items * n_sizes; ++i)
+    if (!std::isfinite(benefit_h[i])) return fail(KVSEL_EINVAL, "benefits must be finite");
+  // Every pair starts at the smallest size; then the step with the largest
+  // added benefit per added entry among those that fit is taken, lowest pair
+  // first on equal ratios, until no step fits or adds benefit.
+  std::vector<int> choice((size_t)n_items, 0);
+  int64_t left = total - (int64_t)n_items * sizes_h[0];
+  if (left >= 0) {
+    for (;;) {
+      int best = -1;
+      double best_ratio = 0.0;
+      for (int i = 0; i < n_items; ++i) {
+        const int j = choice[i];
+        if (j + 1 >= n_sizes) continue;
+        const int64_t dc = (int64_t)sizes_h[j + 1] - sizes_h[j];
+        const double db = benefit_h[(int64_t)i * n_sizes + j + 1] - benefit_h[(int64_t)i * n_sizes + j];
+        if (dc > left || !(db > 0.0)) continue;
+        const double ratio = db / (double)dc;
+        if (ratio > best_ratio) {
+          best = i;
+          best_ratio = ratio;
+        }
+      }
+      if (best < 0) break;
+      left -= (int64_t)sizes_h[choice[best] + 1] - sizes_h[choice[best]];
+      ++choice[best];
+    }
+  }
+  for (int i = 0; i < n_items; ++i) budgets_h[i] = sizes_h[choice[i]];
+  return KVSEL_OK;
+}

@@ -86,6 +86,16 @@ struct ProfileParams {
   int accumulate;       // 1: add to the profile; 0: overwrite it
 };
 
+// Kept importance: per segment, the sum of pooled[idx] over its kept positions.
+struct MassParams {
+  const float *pooled;  // layout of the public ABI
+  const int32_t *idx;   // kept positions, segments at out_off
+  float *mass;          // [segments][n_sizes]
+  int Hkv;
+  int n_sizes;
+  int j;                // the column written by this launch
+};
+
 struct GatherParams {
   const int32_t *idx;
   const uint4 *K;   // rows of d bf16 = 16 x uint4
@@ -98,6 +108,7 @@ struct GatherParams {
 hipError_t launch_query_mean(const QueryMeanParams &p, hipStream_t s);
 hipError_t launch_profile(const ProfileParams &p, const SegTable &t, int64_t lmax, hipStream_t s);
 hipError_t launch_tier_fill(int8_t *tier, int64_t n, hipStream_t s);
+hipError_t launch_mass(const MassParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_tier_mark(const int32_t *idx, int8_t *tier, int label, const SegTable &t, hipStream_t s);
 hipError_t launch_score_pass1(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s);
 hipError_t launch_score_merge(const ScoreParams &p, const SegTable &t, hipStream_t s);  // key_block = pass 1's

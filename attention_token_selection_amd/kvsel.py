@@ -82,6 +82,10 @@ _lib.kvsel_profile_layer.restype = ctypes.c_int
 _lib.kvsel_profile_layer.argtypes = [_P, _vp, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
 _lib.kvsel_tier_rank.restype = ctypes.c_int
 _lib.kvsel_tier_rank.argtypes = [_P, _vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.kvsel_topk_mass.restype = ctypes.c_int
+_lib.kvsel_topk_mass.argtypes = [_P, _vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.kvsel_allocate_budgets.restype = ctypes.c_int
+_lib.kvsel_allocate_budgets.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, ctypes.c_int64, _vp]
 
 
 class KvselError(RuntimeError):
@@ -325,6 +329,35 @@ def kvsel_tier_rank(problem: Problem, profile, n_fast: int, n_mid: int, tier, ws
     with torch.cuda.device(dev):
         _check(_lib.kvsel_tier_rank(problem.ref(), *args, ctypes.c_size_t(ws.numel()), _stream(stream, dev)),
                "kvsel_tier_rank")
+
+def kvsel_topk_mass(problem: Problem, pooled, sizes, mass, ws, stream=None):
+    """Kept importance of each candidate budget: mass [B*Hkv][len(sizes)] fp32."""
+    torch = _torch()
+    n = _sizes(problem)
+    dev = pooled.device
+    sz = (ctypes.c_int32 * len(sizes))(*[int(x) for x in sizes])
+    args = (_ptr(pooled, "pooled", torch.float32, n["scores"], dev), ctypes.c_int32(len(sizes)),
+            ctypes.cast(sz, ctypes.c_void_p),
+            _ptr(mass, "mass", torch.float32, problem.batch * problem.Hkv * len(sizes), dev),
+            _ptr(ws, "ws", torch.uint8, n["ws"], dev))
+    with torch.cuda.device(dev):
+        _check(_lib.kvsel_topk_mass(problem.ref(), *args, ctypes.c_size_t(ws.numel()), _stream(stream, dev)),
+               "kvsel_topk_mass")
+
+
+def kvsel_allocate_budgets(benefit, sizes, total: int):
+    """Host-side greedy allocation: benefit [items][len(sizes)] -> budgets [items] (numpy int32)."""
+    import numpy as np
+
+    b = np.ascontiguousarray(benefit, dtype=np.float64)
+    items, ns = b.shape
+    if ns != len(sizes):
+        raise ValueError("benefit needs one column per candidate size")
+    sz = np.ascontiguousarray(sizes, dtype=np.int32)
+    out = np.zeros(items, dtype=np.int32)
+    _check(_lib.kvsel_allocate_budgets(items, ns, sz.ctypes.data, b.ctypes.data, int(total), out.ctypes.data),
+           "kvsel_allocate_budgets")
+    return out
 
 
 def alloc_outputs(problem: Problem, device, pooled: bool = True):

@@ -101,6 +101,84 @@ def cpu_baseline(spec, cases, budget_s):
                       f"{total:.1f} s of numpy fp64 oracle time on the host"}
 
 
+def _graph_ms(torch, stream, fn, reps):
+    """Milliseconds of one replay of the launches `fn` makes, captured into a
+    graph (best of `reps` replays after a warm-up replay)."""
+    with torch.cuda.stream(stream):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps + 1):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del g
+    return min(times[1:])
+
+
+def time_variants(kv, W, spec, cases, outs, stream, reps):
+    """The same 32 layers through the DeferKV variant (one decode-step row,
+    exponential row weights with lambda 0.1, 16 sinks and 32 recent kept), the
+    same with the guide's mean query per group, and KVDrive's warm-up (profile
+    over all layers, then the three-tier ranking with 2048 fast and 8192
+    middle slots)."""
+    import torch
+
+    dev = cases[0]["K"].device
+    L = spec.seq_lens[0]
+    g = torch.Generator(device=dev)
+    g.manual_seed(20261203)
+    # the first decode step's query: one more observation row per layer
+    Qd = []
+    for c in cases:
+        row = torch.randn(spec.batch, 1, spec.Hq, spec.d, generator=g, device=dev) * (spec.d ** 0.5)
+        Qd.append(torch.cat([c["Q"], row.to(torch.bfloat16)], dim=1).contiguous())
+    res = {}
+    base = W.problem_kwargs(spec)
+    for name, extra in (("deferkv_exp0.1_sink16_recent32", dict(gqa="sum")),
+                        ("deferkv_exp0.1_sink16_recent32_mean_query", dict(gqa="mean"))):
+        kw = dict(base, has_decode=True, weighting="exp", lam=0.1, sink=16, recent=32, **extra)
+        pv = kv.Problem(**kw)
+        wsb, _ = kv.kvsel_plan(pv)
+        wsv = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        calls = [kv.bind_compress(pv, q, c["K"], c["V"], o["idx"], o["K_out"], o["V_out"], None, wsv, stream)
+                 for q, c, o in zip(Qd, cases, outs)]
+
+        def run():
+            for call in calls:
+                call()
+
+        ms = _graph_ms(torch, stream, run, reps)
+        res[name] = {"ms_per_step": ms, "tokens_per_s": L * spec.layers * spec.batch / (ms * 1e-3),
+                     "what": "kvsel_compress per layer, 32 layers, w'=33 (decode row), k=2048"}
+        del wsv
+    pw = kv.Problem(**dict(base, pool="none"))
+    wsb, _ = kv.kvsel_plan(pw)
+    wsw = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    prof = torch.empty(sum(spec.seq_lens), dtype=torch.float32, device=dev)
+    tier = torch.empty(sum(spec.seq_lens), dtype=torch.int8, device=dev)
+
+    def warm():
+        for l, c in enumerate(cases):
+            kv.kvsel_profile_layer(pw, c["Q"], c["K"], prof, wsw, accumulate=l > 0, stream=stream)
+        kv.kvsel_tier_rank(pw, prof, 2048, 8192, tier, wsw, stream=stream)
+
+    ms = _graph_ms(torch, stream, warm, reps)
+    res["kvdrive_warmup_32layers_tiers_2048_8192"] = {
+        "ms_per_step": ms, "tokens_per_s": L * spec.layers * spec.batch / (ms * 1e-3),
+        "what": "kvsel_profile_layer for 32 layers, then kvsel_tier_rank"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +188,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle time the CPU baseline runs for, in whole layers (0: skip)")
     ap.add_argument("--stage-reps", type=int, default=3)
+    ap.add_argument("--variants", type=int, default=1,
+                    help="also time the DeferKV and KVDrive warm-up variants on the same layers (0: skip)")
+    ap.add_argument("--variants-only", type=int, default=0,
+                    help="only time the variants and print them (for a kernel trace of the variants alone)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run torch's plain device copy of MIB MiB (5 times) and exit: the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -149,6 +231,9 @@ def main():
         o["ws"] = ws  # one workspace: the layers run one after another on one stream
 
     stream = torch.cuda.Stream(device=dev)
+    if args.variants_only:
+        print(json.dumps({"variants": time_variants(kv, W, spec, cases, outs, stream, args.stage_reps)}), flush=True)
+        return
     calls = [kv.bind_compress(p, c["Q"], c["K"], c["V"], o["idx"], o["K_out"], o["V_out"], None, ws, stream)
              for c, o in zip(cases, outs)]
 
@@ -235,6 +320,8 @@ def main():
     achieved = pass1_bytes / (stage["row_stats"] * 1e-6) / 1e9
     traffic = counted_traffic()
 
+    variants = time_variants(kv, W, spec, cases, outs, stream, args.stage_reps) if args.variants else None
+
     cpu = None
     if args.cpu_seconds > 0:
         print(f"[bench] cpu oracle baseline, about {args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
@@ -271,6 +358,7 @@ def main():
             "traffic": traffic,
         },
         "cpu_baseline": cpu,
+        "variants": variants,
     }
     print(json.dumps(line), flush=True)
 

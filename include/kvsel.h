@@ -243,6 +243,38 @@ kvsel_status kvsel_profile_layer(const kvsel_problem *p, const void *Q, const vo
 kvsel_status kvsel_tier_rank(const kvsel_problem *p, const float *profile, int64_t n_fast, int64_t n_mid,
                              int8_t *tier, void *ws, size_t ws_bytes, kvsel_stream_t stream);
 
+/*
+ * Adaptive budgets from KVDrive's 2-D window scaling (§5.2): choose one size
+ * per (layer, head) pair out of a few candidates to maximise the summed
+ * benefit under a total budget.  Here a pair's size is its KV budget k and
+ * its benefit the importance it keeps.
+ *
+ * kvsel_topk_mass: for each of the n_sizes candidate budgets sizes_h[j]
+ * (host, >= 0), the sum of the min(sizes_h[j], L_b) largest values of every
+ * (sequence, KV head) segment of `pooled` (device fp32, the layout of
+ * kvsel_pool_topk's pooled output), into mass (device fp32
+ * [B*Hkv][n_sizes], segment-major).  The kept set is exactly the top-k of
+ * the given fp32 values (ties to the lower position); the sum is fp32 in a
+ * fixed order.  The problem's pool, budgets and reserved positions are not
+ * used; ws must hold kvsel_plan's size for *p.
+ *
+ * kvsel_allocate_budgets (host only, no device): the greedy of §5.2.  Every
+ * one of the n_items pairs starts at sizes_h[0] (strictly increasing,
+ * >= 0); while some pair's next size fits what is left of `total` and adds
+ * benefit, the step with the largest (added benefit) / (added entries) is
+ * taken, the lower pair index first on equal ratios.  benefit_h: host
+ * double [n_items][n_sizes], finite.  budgets_h (host int32 [n_items]):
+ * the chosen size of every pair (sizes_h[0] everywhere if even those exceed
+ * total), ready to be a layer's budgets_h.
+ *
+ * Errors: KVSEL_EINVAL for NULL or invalid arguments (and as for
+ * kvsel_pool_topk in kvsel_topk_mass).
+ */
+kvsel_status kvsel_topk_mass(const kvsel_problem *p, const float *pooled, int32_t n_sizes, const int32_t *sizes_h,
+                             float *mass, void *ws, size_t ws_bytes, kvsel_stream_t stream);
+kvsel_status kvsel_allocate_budgets(int32_t n_items, int32_t n_sizes, const int32_t *sizes_h,
+                                    const double *benefit_h, int64_t total, int32_t *budgets_h);
+
 /* Static text for a status code. */
 const char *kvsel_status_string(kvsel_status s);
 

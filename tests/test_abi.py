@@ -187,3 +187,31 @@ int main(void) { F(batch) F(Hq) F(Hkv) F(d) F(L) F(seq_offsets_h) F(w) F(has_dec
         c_name = name.rstrip("_")  # "lambda" is a Python keyword
         assert int(got[c_name]) == getattr(kv.KvselProblem, name).offset, name
     assert int(got["size"]) == ctypes.sizeof(kv.KvselProblem)
+
+
+# ---------------------------------------------------------------- host-only budget allocation
+@pytest.mark.parametrize("seed", range(6))
+def test_allocate_budgets_matches_oracle(seed):
+    """The library's greedy (host C) makes the oracle's choices on random
+    instances: concave top-k masses and arbitrary benefits, uneven sizes."""
+    rng = np.random.default_rng(seed)
+    sizes = [0, 64, 256, 512, 1024, 4096] if seed % 2 else [16, 17, 40, 41, 300]
+    items = int(rng.integers(1, 70))
+    if seed < 3:
+        benefit = np.stack([O.topk_mass(rng.random(4096) ** 4, sizes) for _ in range(items)])
+    else:
+        benefit = rng.random((items, len(sizes))) * 10
+    for total in (0, sizes[0] * items, sizes[0] * items + 1, 500 * items, 10 ** 9):
+        got = kv.kvsel_allocate_budgets(benefit, sizes, total)
+        want = np.asarray(sizes)[O.greedy_allocate(benefit, sizes, total)]
+        np.testing.assert_array_equal(got, want)
+        if total >= sizes[0] * items:
+            assert int(got.astype(np.int64).sum()) <= total
+
+
+def test_allocate_budgets_hand_and_validation():
+    assert kv.kvsel_allocate_budgets([[0, 5, 6], [0, 3, 6], [0, 1, 11]], [0, 2, 4], 6).tolist() == [2, 4, 0]
+    assert kv.kvsel_allocate_budgets(np.zeros((0, 2)), [0, 1], 5).tolist() == []
+    for bad in (([[0, 1]], [1, 1], 5), ([[0, 1]], [-1, 1], 5), ([[0, float("nan")]], [0, 1], 5)):
+        with pytest.raises(kv.KvselError):
+            kv.kvsel_allocate_budgets(*bad)
