@@ -56,6 +56,12 @@ ascending position), the first ``n_fast`` positions go to the fastest tier
 (GPU memory), the next ``n_mid`` to the middle tier (host memory) and the
 rest stay in the backing store only (``tier_labels``).
 
+TideKV's memory-bounded form of steps 4-7 (§4.2) is ``streaming_select``:
+pass 1 as in ``blockwise_row_stats``; pass 2 visits the key blocks in order,
+scores (and pools) one block at a time and merges its positions into a
+running top-k, so no per-position buffer over the whole prefix is kept.  It
+reaches the same selection as ``select_topk`` on the whole pooled score.
+
 And adaptive budgets: KVDrive's 2-D window scaling (§5.2) chooses one size
 per (layer, head) from a few candidates to maximise the summed benefit under
 a total memory budget, with a greedy rule that starts every pair at its
@@ -99,6 +105,7 @@ __all__ = [
     "tier_labels",
     "topk_mass",
     "greedy_allocate",
+    "streaming_select",
 ]
 
 
@@ -510,3 +517,62 @@ def greedy_allocate(benefit, sizes, total: int) -> np.ndarray:
             return choice
         left -= sizes[choice[best] + 1] - sizes[choice[best]]
         choice[best] += 1
+
+
+def streaming_select(Q_b: np.ndarray, K_b: np.ndarray, h: int, Hkv: int, *, w: int, has_decode: bool,
+                     alpha: float, causal: bool, scale: float, block: int, k: int, pool: str = "none",
+                     pool_kernel: int = 1, weighting: str = "alpha", lam: float = 0.0, gqa: str = "sum",
+                     sink: int = 0, recent: int = 0) -> np.ndarray:
+    """TideKV §4.2's two-pass blockwise streaming top-k for one (sequence, KV head).
+
+    Pass 1 collects each observation row's (M, Z) over the key blocks.  Pass 2
+    walks the blocks in order; for block [s, e) it recomputes the normalised
+    probabilities of the keys [s - r, e + r) (r = the pool's half width, so
+    the pool of every position of the block sees its real neighbours), forms
+    the block's aggregated and pooled scores, and keeps the best ``k`` of
+    (running top-k) + (block positions), ordered as ``select_topk`` orders
+    them.  The memory held besides one block is the running top-k.  Returns
+    the kept positions ascending.
+    """
+    L = K_b.shape[0]
+    Hq = Q_b.shape[1]
+    G = Hq // Hkv
+    pos = observation_positions(L, w, has_decode)
+    vis = visible_mask(pos, L, causal)
+    c = row_weights(w, has_decode, alpha) if weighting == "alpha" else temporal_row_weights(w, has_decode, lam)
+    K_h = K_b[:, h, :]
+    if gqa == "sum":
+        query_sets = [Q_b[:, h * G + gi, :] for gi in range(G)]
+    else:
+        query_sets = [mean_query_rows(Q_b, h, G)]
+    stats = [blockwise_row_stats(q, K_h, vis, scale, block) for q in query_sets]
+    r = 0 if pool == "none" else (pool_kernel - 1) // 2
+    prot_all = protected_mask(L, sink, recent)
+    keep = max(0, min(int(k), L))
+    run_val = np.zeros(0)
+    run_pos = np.zeros(0, dtype=np.int64)
+    for start in range(0, L, block):
+        stop = min(L, start + block)
+        lo, hi = max(0, start - r), min(L, stop + r)
+        S = np.zeros(hi - lo)
+        for q, (M, Z) in zip(query_sets, stats):
+            logits = scale * (q @ K_h[lo:hi].T)
+            pr = np.where(vis[:, lo:hi], np.exp(logits - M[:, None]), 0.0) / Z[:, None]
+            S += (c[:, None] * pr).sum(axis=0)
+        # pool the block's positions from S on [lo, hi); outside [0, L) as in pool1d
+        P = np.empty(stop - start)
+        for i in range(start, stop):
+            a, b = i - r, i + r + 1
+            win = S[max(a, lo) - lo:min(b, hi) - lo]
+            if pool == "avg":
+                P[i - start] = win.sum() / pool_kernel
+            elif pool == "max":
+                P[i - start] = win.max()
+            else:
+                P[i - start] = S[i - lo]
+        val = np.concatenate([run_val, P])
+        cand = np.concatenate([run_pos, np.arange(start, stop)])
+        prot = prot_all[cand]
+        order = np.lexsort((cand, np.where(prot, 0.0, -val), ~prot))[:keep]
+        run_val, run_pos = val[order], cand[order]
+    return np.sort(run_pos)

@@ -581,6 +581,28 @@ def test_greedy_allocate_optimal_on_concave_uniform_steps(seed):
         assert abs(value - best) < 1e-12
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_streaming_select_equals_whole_prefix_selection(seed):
+    """TideKV's blockwise streaming top-k keeps exactly the positions the
+    whole-prefix selection keeps (continuous random inputs: no ties), for
+    blocks smaller than the pool, ragged last blocks, budgets above the
+    length, reserved positions, both weightings and both GQA modes."""
+    rng = np.random.default_rng(seed)
+    L, Hq, Hkv, w = 157, 8, 2, 6
+    K = rng.standard_normal((L, Hkv, 128)) / np.sqrt(128)
+    Q = O.round_to_bf16(rng.standard_normal((w + 1, Hq, 128)) * np.sqrt(128) * 0.3)
+    pool, kern = [("none", 1), ("avg", 5), ("max", 7), ("avg", 3)][seed]
+    kw = dict(w=w, has_decode=True, alpha=0.3, causal=seed != 2, scale=1.0 / np.sqrt(128))
+    extra = [dict(), dict(weighting="exp", lam=0.1), dict(gqa="mean"), dict(weighting="exp", lam=1.0, gqa="mean")][seed]
+    for h in range(Hkv):
+        P = O.pool1d(O.head_scores(Q, K, h, Hkv, **kw, **extra), pool, kern)
+        for block, k, sink, recent in ((16, 20, 0, 0), (2, 40, 3, 5), (64, 200, 0, 0), (157, 9, 4, 4), (5, 0, 0, 0)):
+            got = O.streaming_select(Q, K, h, Hkv, **kw, **extra, block=block, k=k, pool=pool, pool_kernel=kern,
+                                     sink=sink, recent=recent)
+            want = O.select_topk(P, k, O.protected_mask(L, sink, recent))
+            np.testing.assert_array_equal(got, want)
+
+
 # ---------------------------------------------------------------- planted mistakes
 def _pins_pass():
     """Run the pins above in-process; return False as soon as one fails."""
@@ -611,6 +633,7 @@ def _pins_pass():
         test_topk_mass_hand_and_brute_force,
         test_greedy_allocate_hand,
         lambda: [test_greedy_allocate_optimal_on_concave_uniform_steps(s) for s in range(2)],
+        lambda: [test_streaming_select_equals_whole_prefix_selection(s) for s in range(4)],
     ]
     for c in checks:
         try:
@@ -767,6 +790,16 @@ def _greedy_stops_at_first_misfit(benefit, sizes, total):
     return choice
 
 
+def _streaming_no_halo(Q_b, K_b, h, Hkv, *, w, has_decode, alpha, causal, scale, block, k, pool="none",
+                       pool_kernel=1, weighting="alpha", lam=0.0, gqa="sum", sink=0, recent=0):
+    # each block pooled on its own, zero padded at the block's edges
+    L = K_b.shape[0]
+    S = O.head_scores(Q_b, K_b, h, Hkv, w=w, has_decode=has_decode, alpha=alpha, causal=causal, scale=scale,
+                      weighting=weighting, lam=lam, gqa=gqa)
+    P = np.concatenate([O.pool1d(S[s:s + block], pool, pool_kernel) for s in range(0, L, block)])
+    return O.select_topk(P, k, O.protected_mask(L, sink, recent))
+
+
 def _avg_exclude_pad(S, kind, kernel):
     if kind != "avg":
         return O.pool1d.__wrapped__(S, kind, kernel)
@@ -811,6 +844,7 @@ MUTATIONS = {
     "mass_of_smallest_values": ("topk_mass", _mass_ascending),
     "greedy_by_gain_not_ratio": ("greedy_allocate", _greedy_by_benefit_not_ratio),
     "greedy_stops_at_first_misfit": ("greedy_allocate", _greedy_stops_at_first_misfit),
+    "streaming_pool_without_halo": ("streaming_select", _streaming_no_halo),
 }
 
 
