@@ -4,6 +4,7 @@
 #include "kvsel_internal.h"
 
 #include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -32,6 +33,10 @@ struct Plan {
   float alpha, cl2;
   int weighting = 0, sink = 0, recent = 0;
   int gqa = 0;          // KVSEL_GQA_MEAN_QUERY: Hq and G below describe the mean queries
+  // Streaming (bounded workspace): keys per step, pool half width, running
+  // top-k slots per segment, candidate row length, pass-1 blocks per step.
+  int stream = 0, halo = 0, kslot = 0, lv = 0, nblk1_c = 0;
+  size_t off_run = 0, off_sbuf = 0, off_cand[2] = {0, 0}, off_candp = 0, off_selidx = 0, off_pos[2] = {0, 0};
   int Hq_in = 0, G_in = 0;  // the caller's query heads and group size
   size_t off_qmean = 0;
   float lam2 = 0.0f, log2norm = 0.0f;
@@ -54,6 +59,55 @@ int auto_key_block(int64_t head_keys, int64_t cap) {
   kb = std::max<int64_t>(kb, 2 * kKeyTile);
   kb = std::min<int64_t>(kb, cap);
   return (int)kb;
+}
+
+// Workspace of the streaming form (TideKV §4.2's bounded temporary memory):
+// every part is sized by the keys per step, the budgets and the rows, never
+// by the prefix length.
+kvsel_status plan_streaming(const kvsel_problem *p, Plan &P) {
+  const size_t nseg = (size_t)P.B * P.Hkv;
+  P.stream = p->stream_keys;
+  P.halo = (P.pool == KVSEL_POOL_NONE) ? 0 : (P.pool_kernel - 1) / 2;
+  int32_t kmax = 0;
+  for (int32_t k : P.keff) kmax = std::max(kmax, k);
+  P.kslot = kmax;
+  const int64_t lv = (int64_t)P.kslot + P.stream;
+  if (lv > (int64_t)kMaxChunks * kSelectChunk)
+    return fail(KVSEL_EUNSUPPORTED, "stream_keys plus the largest budget exceed 2^20");
+  P.lv = (int)lv;
+  // A step has fewer keys than a whole prefix; blocks of at least 128 keys
+  // keep each workgroup's query loads small next to its key loads.
+  const int64_t step_keys = (int64_t)P.stream * P.B * P.Hkv;
+  P.kb1 = p->key_chunk > 0 ? p->key_chunk : std::max(128, auto_key_block(step_keys, 4096));
+  P.kb2 = std::max(128, auto_key_block(step_keys, 2048));
+  P.nblk1_c = (P.stream + P.kb1 - 1) / P.kb1;
+  P.nblk1_max = P.nblk1_c;
+  P.nchunk_max = (P.lv + kSelectChunk - 1) / kSelectChunk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  P.off_partials = take(nseg * P.nblk1_c * P.Rpad * sizeof(float2));
+  P.off_run = take(nseg * P.Rpad * sizeof(float2));
+  P.off_bias = take(nseg * P.Rpad * sizeof(float));
+  P.off_sbuf = take(nseg * ((size_t)P.stream + 2 * P.halo) * sizeof(float));
+  P.off_cand[0] = take(nseg * P.lv * sizeof(float));
+  P.off_cand[1] = take(nseg * P.lv * sizeof(float));
+  P.off_candp = take(nseg * P.lv * sizeof(float));
+  P.off_selidx = take(nseg * std::max(1, P.kslot) * sizeof(int32_t));
+  P.off_pos[0] = take(nseg * std::max(1, P.kslot) * sizeof(int32_t));
+  P.off_pos[1] = take(nseg * std::max(1, P.kslot) * sizeof(int32_t));
+  const size_t nchunks = nseg * (size_t)P.nchunk_max;
+  P.off_tfine = take(nchunks * kSelectBins * sizeof(uint16_t));
+  P.off_tcoarse = take(nchunks * (kSelectBins / 32) * sizeof(uint16_t));
+  P.off_bucket = take(nchunks * kSelectChunk * sizeof(uint32_t));
+  P.off_qmean = off;
+  if (P.gqa == KVSEL_GQA_MEAN_QUERY) take((size_t)P.B * P.wp * P.Hkv * p->d * sizeof(uint16_t));
+  P.off_scores = P.off_pooled = 0;  // no whole-prefix buffers in this form
+  P.ws_bytes = off;
+  return KVSEL_OK;
 }
 
 kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
@@ -81,6 +135,8 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
     return fail(KVSEL_EINVAL, "lambda must be finite and >= 0");
   if (p->sink_tokens < 0 || p->recent_tokens < 0) return fail(KVSEL_EINVAL, "sink_tokens and recent_tokens must be >= 0");
   if (p->gqa != KVSEL_GQA_SUM && p->gqa != KVSEL_GQA_MEAN_QUERY) return fail(KVSEL_EINVAL, "unknown gqa");
+  if (p->stream_keys < 0 || p->stream_keys % kSelectChunk != 0)
+    return fail(KVSEL_EINVAL, "stream_keys must be 0 or a positive multiple of 2048");
 
   P.B = p->batch;
   P.Hq = p->Hq;
@@ -160,6 +216,7 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   P.nblk2_max = (int)((P.Lmax + P.kb2 - 1) / P.kb2);
 
   const size_t nseg = (size_t)P.B * P.Hkv;
+  if (p->stream_keys > 0) return plan_streaming(p, P);
   size_t off = 0;
   P.off_partials = off;
   off = align_up(off + nseg * P.nblk1_max * P.Rpad * sizeof(float2), 256);
@@ -271,6 +328,10 @@ ScoreParams score_params(const Plan &P, const void *Q, const void *K, float *sco
   sp.lam2 = P.lam2;
   sp.log2norm = P.log2norm;
   sp.nblk1_max = P.nblk1_max;
+  sp.key_begin = 0;
+  sp.key_end = INT_MAX;
+  sp.out_stride = 0;
+  sp.out_origin = 0;
   return sp;
 }
 
@@ -363,6 +424,156 @@ bool any_kept(const Plan &P) { return P.out_off.back() > 0; }
 
 }  // namespace
 
+namespace {
+
+// TideKV §4.2's streaming form of steps 1-7 with a workspace bounded by the
+// keys per step: pass 1 step by step into running row states, the merge
+// into biases, then pass 2 step by step, each step's pooled scores merged
+// into the running top-k by the exact selection kernels, and the gather.
+kvsel_status run_compress_streaming(const Plan &P, const void *Q, const void *K, const void *V, int32_t *idx,
+                                    void *K_out, void *V_out, char *ws, hipStream_t st) {
+  if (P.gqa == KVSEL_GQA_MEAN_QUERY) {
+    QueryMeanParams qp;
+    qp.Q = static_cast<const uint4 *>(Q);
+    qp.Qm = reinterpret_cast<uint4 *>(ws + P.off_qmean);
+    qp.Hq = P.Hq_in;
+    qp.Hkv = P.Hkv;
+    qp.G = P.G_in;
+    qp.items = P.B * P.wp * P.Hkv;
+    hipError_t e = launch_query_mean(qp, st);
+    if (e != hipSuccess) return hip_fail(e, "query mean launch");
+  }
+  const int nsteps = (int)((P.Lmax + P.stream - 1) / P.stream);
+  float2 *run = reinterpret_cast<float2 *>(ws + P.off_run);
+  ScoreParams sp = score_params(P, Q, K, nullptr, ws);
+  kvsel_status s = KVSEL_OK;
+  // Pass 1, step by step.
+  for (int c = 0; c < nsteps && s == KVSEL_OK; ++c) {
+    const int c0 = c * P.stream;
+    sp.key_block = P.kb1;
+    sp.key_begin = c0;
+    sp.key_end = c0 + P.stream;
+    s = for_each_group(P, [&](const SegTable &t, int64_t lmax) {
+      if (c0 < lmax) {
+        const int nblk = (int)((std::min<int64_t>(lmax, c0 + P.stream) - c0 + P.kb1 - 1) / P.kb1);
+        hipError_t e = launch_score_pass1(sp, t, nblk, st);
+        if (e != hipSuccess) return hip_fail(e, "score pass 1 launch");
+      }
+      hipError_t e = launch_stream_stats(sp, t, run, c == 0, st);
+      if (e != hipSuccess) return hip_fail(e, "row statistics fold launch");
+      return KVSEL_OK;
+    });
+  }
+  if (s != KVSEL_OK) return s;
+  // Biases from the running states: the merge over a single "block".
+  {
+    ScoreParams mp = sp;
+    mp.partials = run;
+    mp.nblk1_max = 1;
+    mp.key_block = 1 << 30;
+    s = for_each_group(P, [&](const SegTable &t, int64_t) {
+      hipError_t e = launch_score_merge(mp, t, st);
+      if (e != hipSuccess) return hip_fail(e, "row statistics merge launch");
+      return KVSEL_OK;
+    });
+    if (s != KVSEL_OK) return s;
+  }
+  // Pass 2 and the running selection, step by step.
+  StreamParams q;
+  q.S = reinterpret_cast<const float *>(ws + P.off_sbuf);
+  q.S_stride = (int64_t)P.stream + 2 * P.halo;
+  q.lv = P.lv;
+  q.kslot = P.kslot;
+  q.stream = P.stream;
+  q.Hkv = P.Hkv;
+  q.pool = P.pool;
+  q.pool_kernel = P.pool_kernel;
+  q.sink = P.sink;
+  q.recent = P.recent;
+  q.sel = reinterpret_cast<const int32_t *>(ws + P.off_selidx);
+  int cur = 0;
+  q.cand = reinterpret_cast<float *>(ws + P.off_cand[cur]);
+  s = for_each_group(P, [&](const SegTable &t, int64_t) {
+    hipError_t e = launch_stream_init(q, t, st);
+    if (e != hipSuccess) return hip_fail(e, "streaming init launch");
+    return KVSEL_OK;
+  });
+  if (s != KVSEL_OK) return s;
+  sp.scores = reinterpret_cast<float *>(ws + P.off_sbuf);
+  sp.out_stride = q.S_stride;
+  for (int c = 0; c < nsteps; ++c) {
+    const int c0 = c * P.stream;
+    sp.key_block = P.kb2;
+    sp.key_begin = std::max(0, c0 - P.halo);
+    sp.key_end = c0 + P.stream + P.halo;
+    sp.out_origin = c0 - P.halo;
+    q.c0 = c0;
+    q.S_origin = c0 - P.halo;
+    q.cand = reinterpret_cast<float *>(ws + P.off_cand[cur]);
+    q.cand_next = reinterpret_cast<float *>(ws + P.off_cand[cur ^ 1]);
+    q.pos_in = reinterpret_cast<const int32_t *>(ws + P.off_pos[cur]);
+    q.pos_out = reinterpret_cast<int32_t *>(ws + P.off_pos[cur ^ 1]);
+    s = for_each_group(P, [&](const SegTable &t, int64_t lmax) {
+      if (sp.key_begin < lmax) {
+        const int64_t hi = std::min<int64_t>(lmax, sp.key_end);
+        const int nblk = (int)((hi - sp.key_begin + P.kb2 - 1) / P.kb2);
+        hipError_t e = launch_score_pass2(sp, t, nblk, st);
+        if (e != hipSuccess) return hip_fail(e, "score pass 2 launch");
+      }
+      hipError_t e = launch_stream_pool(q, t, st);
+      if (e != hipSuccess) return hip_fail(e, "streaming pool launch");
+      return KVSEL_OK;
+    });
+    if (s != KVSEL_OK) return s;
+    // The step's selection: one candidate row per segment, budget
+    // min(k, keys seen so far), no pool (the row holds pooled values), no
+    // reserve (reserved positions carry +inf).
+    Plan V = P;
+    V.pool = KVSEL_POOL_NONE;
+    V.pool_kernel = 1;
+    V.sink = 0;
+    V.recent = 0;
+    V.Lmax = P.lv;
+    for (int b = 0; b <= P.B; ++b) V.seq_off[b] = (int64_t)b * P.lv;
+    for (int b = 0; b < P.B; ++b) {
+      const int64_t seen = std::min<int64_t>(P.seq_off[b + 1] - P.seq_off[b], (int64_t)c0 + P.stream);
+      for (int h = 0; h < P.Hkv; ++h) {
+        const size_t sg = (size_t)b * P.Hkv + h;
+        V.keff[sg] = (int32_t)std::min<int64_t>(P.keff[sg], seen);
+        V.out_off[sg + 1] = V.out_off[sg] + V.keff[sg];
+      }
+    }
+    if (any_kept(V)) {
+      s = run_select(V, q.cand, reinterpret_cast<float *>(ws + P.off_candp), reinterpret_cast<int32_t *>(ws + P.off_selidx),
+                     ws, st);
+      if (s != KVSEL_OK) return s;
+    }
+    s = for_each_group(V, [&](const SegTable &vt, int64_t) {
+      hipError_t e = launch_stream_map(q, vt, st);
+      if (e != hipSuccess) return hip_fail(e, "streaming map launch");
+      return KVSEL_OK;
+    });
+    if (s != KVSEL_OK) return s;
+    cur ^= 1;
+  }
+  q.pos_in = reinterpret_cast<const int32_t *>(ws + P.off_pos[cur]);
+  s = for_each_group(P, [&](const SegTable &t, int64_t) {
+    hipError_t e = launch_stream_final(q, t, idx, st);
+    if (e != hipSuccess) return hip_fail(e, "streaming result launch");
+    return KVSEL_OK;
+  });
+  if (s != KVSEL_OK) return s;
+  return any_kept(P) ? run_gather(P, idx, K, V, K_out, V_out, st) : KVSEL_OK;
+}
+
+kvsel_status reject_streaming(const Plan &P, const char *fn) {
+  if (P.stream > 0)
+    return fail(KVSEL_EINVAL, std::string(fn) + " needs whole-prefix buffers; stream_keys applies to kvsel_compress only");
+  return KVSEL_OK;
+}
+
+}  // namespace
+
 KVSEL_API int kvsel_abi_version(void) { return KVSEL_ABI_VERSION; }
 
 KVSEL_API const char *kvsel_status_string(kvsel_status s) {
@@ -393,6 +604,7 @@ KVSEL_API kvsel_status kvsel_score(const kvsel_problem *p, const void *Q, const 
   g_last_error.clear();
   Plan P;
   kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = reject_streaming(P, "kvsel_score");
   if (s == KVSEL_OK) s = check_ptr(Q, "Q");
   if (s == KVSEL_OK) s = check_ptr(K, "K");
   if (s == KVSEL_OK) s = check_ptr(scores, "scores");
@@ -407,6 +619,7 @@ KVSEL_API kvsel_status kvsel_row_stats(const kvsel_problem *p, const void *Q, co
   g_last_error.clear();
   Plan P;
   kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = reject_streaming(P, "kvsel_row_stats");
   if (s == KVSEL_OK) s = check_ptr(Q, "Q");
   if (s == KVSEL_OK) s = check_ptr(K, "K");
   if (s == KVSEL_OK) s = check_ws(P, ws, ws_bytes);
@@ -420,6 +633,7 @@ KVSEL_API kvsel_status kvsel_score_from_stats(const kvsel_problem *p, const void
   g_last_error.clear();
   Plan P;
   kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = reject_streaming(P, "kvsel_score_from_stats");
   if (s == KVSEL_OK) s = check_ptr(Q, "Q");
   if (s == KVSEL_OK) s = check_ptr(K, "K");
   if (s == KVSEL_OK) s = check_ptr(scores, "scores");
@@ -434,6 +648,7 @@ KVSEL_API kvsel_status kvsel_pool_topk(const kvsel_problem *p, const float *scor
   g_last_error.clear();
   Plan P;
   kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = reject_streaming(P, "kvsel_pool_topk");
   if (s == KVSEL_OK) s = check_ptr(scores, "scores");
   if (s == KVSEL_OK && pooled) s = check_ptr(pooled, "pooled");
   if (s == KVSEL_OK && any_kept(P)) s = check_ptr(idx, "idx");
@@ -460,6 +675,7 @@ KVSEL_API kvsel_status kvsel_gather(const kvsel_problem *p, const int32_t *idx, 
   return run_gather(P, idx, K, V, K_out, V_out, reinterpret_cast<hipStream_t>(stream));
 }
 
+
 KVSEL_API kvsel_status kvsel_compress(const kvsel_problem *p, const void *Q, const void *K, const void *V,
                                       int32_t *idx, void *K_out, void *V_out, float *pooled, void *ws,
                                       size_t ws_bytes, kvsel_stream_t stream) {
@@ -473,11 +689,14 @@ KVSEL_API kvsel_status kvsel_compress(const kvsel_problem *p, const void *Q, con
   if (s == KVSEL_OK && any_kept(P)) s = check_ptr(K_out, "K_out");
   if (s == KVSEL_OK && any_kept(P)) s = check_ptr(V_out, "V_out");
   if (s == KVSEL_OK && pooled) s = check_ptr(pooled, "pooled");
+  if (s == KVSEL_OK && pooled && P.stream > 0)
+    s = fail(KVSEL_EINVAL, "pooled must be NULL with stream_keys (no whole-prefix pooled scores are kept)");
   if (s == KVSEL_OK) s = check_ws(P, ws, ws_bytes);
   if (s == KVSEL_OK) s = check_device();
   if (s != KVSEL_OK) return s;
   char *wsb = static_cast<char *>(ws);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (P.stream > 0) return run_compress_streaming(P, Q, K, V, idx, K_out, V_out, wsb, st);
   float *scores = reinterpret_cast<float *>(wsb + P.off_scores);
   float *pool_buf = pooled ? pooled : reinterpret_cast<float *>(wsb + P.off_pooled);
   s = run_score(P, Q, K, scores, wsb, st);
@@ -512,6 +731,7 @@ KVSEL_API kvsel_status kvsel_profile_layer(const kvsel_problem *p, const void *Q
   g_last_error.clear();
   Plan P;
   kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = reject_streaming(P, "kvsel_profile_layer");
   if (s == KVSEL_OK) s = check_ptr(Q, "Q");
   if (s == KVSEL_OK) s = check_ptr(K, "K");
   if (s == KVSEL_OK) s = check_ptr(profile, "profile");
@@ -541,6 +761,7 @@ KVSEL_API kvsel_status kvsel_tier_rank(const kvsel_problem *p, const float *prof
   g_last_error.clear();
   Plan P;
   kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = reject_streaming(P, "kvsel_tier_rank");
   if (s == KVSEL_OK) s = check_ptr(profile, "profile");
   if (s == KVSEL_OK) s = check_ptr(tier, "tier");
   if (s == KVSEL_OK && (n_fast < 0 || n_mid < 0)) s = fail(KVSEL_EINVAL, "n_fast and n_mid must be >= 0");
@@ -580,6 +801,7 @@ KVSEL_API kvsel_status kvsel_topk_mass(const kvsel_problem *p, const float *pool
   g_last_error.clear();
   Plan P;
   kvsel_status s = make_plan(p, P);
+  if (s == KVSEL_OK) s = reject_streaming(P, "kvsel_topk_mass");
   if (s == KVSEL_OK) s = check_ptr(pooled, "pooled");
   if (s == KVSEL_OK) s = check_ptr(mass, "mass");
   if (s == KVSEL_OK && (n_sizes < 1 || !sizes_h)) s = fail(KVSEL_EINVAL, "need n_sizes >= 1 candidate sizes");

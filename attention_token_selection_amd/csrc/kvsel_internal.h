@@ -48,6 +48,9 @@ struct ScoreParams {
   float log2norm;               // weighting 1: log2 of sum_r exp(lambda (r - r_max))
   int key_block;                // keys per workgroup in this pass (multiple of 32)
   int nblk1_max;                // pass 1 blocks per segment of the longest sequence
+  int key_begin, key_end;       // keys of each sequence this launch covers (0, INT_MAX: all)
+  int64_t out_stride;           // pass 2 output: 0 = the public layout; else floats per segment
+  int out_origin;               //   and the key stored first in each segment's window
 };
 
 // The mean query of every (sequence, observation row, KV head): the G query
@@ -96,6 +99,25 @@ struct MassParams {
   int j;                // the column written by this launch
 };
 
+// Streaming selection: per segment a candidate row of lv floats, the running
+// top-k values in [0, kslot) (ascending positions, -inf where unused) and
+// this step's pooled values in [kslot, kslot + stream).
+struct StreamParams {
+  const float *S;         // pass-2 window: [nseg][S_stride], element 0 is key S_origin
+  int64_t S_stride;
+  int S_origin;
+  float *cand;            // [nseg][lv]: this step's row (filled by init and pool, read by map)
+  float *cand_next;       // [nseg][lv]: the next step's row (running part written by map)
+  const int32_t *sel;     // selected slots of cand, per segment at the step plan's out_off
+  const int32_t *pos_in;  // [nseg][kslot] positions of the running slots
+  int32_t *pos_out;
+  int lv, kslot, stream;
+  int c0;                 // first key of this step
+  int Hkv;
+  int pool, pool_kernel;
+  int sink, recent;
+};
+
 struct GatherParams {
   const int32_t *idx;
   const uint4 *K;   // rows of d bf16 = 16 x uint4
@@ -113,6 +135,11 @@ hipError_t launch_tier_mark(const int32_t *idx, int8_t *tier, int label, const S
 hipError_t launch_score_pass1(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s);
 hipError_t launch_score_merge(const ScoreParams &p, const SegTable &t, hipStream_t s);  // key_block = pass 1's
 hipError_t launch_score_pass2(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s);
+hipError_t launch_stream_stats(const ScoreParams &p, const SegTable &t, float2 *run, int first, hipStream_t s);
+hipError_t launch_stream_init(const StreamParams &p, const SegTable &t, hipStream_t s);
+hipError_t launch_stream_pool(const StreamParams &p, const SegTable &t, hipStream_t s);
+hipError_t launch_stream_map(const StreamParams &p, const SegTable &vt, hipStream_t s);
+hipError_t launch_stream_final(const StreamParams &p, const SegTable &t, int32_t *idx, hipStream_t s);
 hipError_t launch_pool_topk(const SelectParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_gather(const GatherParams &p, const SegTable &t, hipStream_t s);
 

@@ -131,9 +131,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 4 
   const int sb = blockIdx.z;
   const int64_t key0 = t.key_off[sb];
   const int L = (int)(t.key_off[sb + 1] - key0);
-  const int kb0 = blk * p.key_block;
-  if (kb0 >= L) return;  // the whole workgroup leaves together
-  const int kb1 = min(L, kb0 + p.key_block);
+  // Keys key_begin + blk * key_block onwards, clipped to [key_begin,
+  // key_end) of the launch (the whole prefix unless streaming).
+  const int kend = min(L, p.key_end);
+  const int kb0 = p.key_begin + blk * p.key_block;
+  if (kb0 >= kend) return;  // the whole workgroup leaves together
+  const int kb1 = min(kend, kb0 + p.key_block);
   const int seg = t.seg0 + sb * p.Hkv + h;
   const int b = t.seq0 + sb;
 
@@ -326,7 +329,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 4 
   if constexpr (PASS == 2) {
     __syncthreads();
     const int n = kb1 - kb0;
-    float *out = p.scores + (int64_t)p.Hkv * key0 + (int64_t)h * L + kb0;
+    // The public layout, or (streaming) one window of out_stride floats per
+    // segment whose first element is key out_origin.
+    float *out = (p.out_stride > 0) ? p.scores + (int64_t)seg * p.out_stride + (kb0 - p.out_origin)
+                                    : p.scores + (int64_t)p.Hkv * key0 + (int64_t)h * L + kb0;
     for (int i = threadIdx.x; i < n; i += NT) {
       float v = red[i];
 #pragma unroll
@@ -357,13 +363,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 4 
 constexpr int MERGE_ROWS = 16;
 constexpr int MERGE_SPLIT = NT / MERGE_ROWS;
 
-__global__ __launch_bounds__(NT) void merge_kernel(ScoreParams p, SegTable t) {
+// FOLD (the streaming form, TideKV §4.2 with a bounded workspace): merge the
+// block states of the step's keys [key_begin, key_end) and the running
+// state `run` (unless this is the first step) back into `run` instead.
+template <bool FOLD>
+__global__ __launch_bounds__(NT) void merge_kernel(ScoreParams p, SegTable t, float2 *run, int first) {
   __shared__ float2 shares[MERGE_SPLIT][MERGE_ROWS];
   const int sl = blockIdx.y;  // local segment: sequence-major, head-minor
   const int sb = sl / p.Hkv;
   const int seg = t.seg0 + sl;
   const int L = (int)(t.key_off[sb + 1] - t.key_off[sb]);
-  const int nblk = (L + p.key_block - 1) / p.key_block;
+  const int kend = min(L, p.key_end);
+  const int nblk = FOLD ? ((kend > p.key_begin) ? (kend - p.key_begin + p.key_block - 1) / p.key_block : 0)
+                        : (L + p.key_block - 1) / p.key_block;
   const int lrow = threadIdx.x % MERGE_ROWS;
   const int sh = threadIdx.x / MERGE_ROWS;
   const int row = blockIdx.x * MERGE_ROWS + lrow;
@@ -386,6 +398,15 @@ __global__ __launch_bounds__(NT) void merge_kernel(ScoreParams p, SegTable t) {
   if (sh != 0 || row >= p.Rpad) return;
 #pragma unroll
   for (int k = 1; k < MERGE_SPLIT; ++k) lse_merge(r, z, shares[k][lrow].x, shares[k][lrow].y);
+  if constexpr (FOLD) {
+    float2 *mine = run + (int64_t)seg * p.Rpad + row;
+    if (!first) {
+      const float2 prev = *mine;
+      lse_merge(r, z, prev.x, prev.y);
+    }
+    *mine = make_float2(r, z);
+    return;
+  }
   const int wr = row / p.G;  // observation row: window rows 0 .. w-1, then the decode row
   float lc;                  // log2 of the row's weight c_r
   if (p.weighting == 1) {
@@ -423,7 +444,13 @@ hipError_t launch_score_pass1(const ScoreParams &p, const SegTable &t, int nblk,
 
 hipError_t launch_score_merge(const ScoreParams &p, const SegTable &t, hipStream_t s) {
   const dim3 grid((p.Rpad + MERGE_ROWS - 1) / MERGE_ROWS, t.nseq * p.Hkv);
-  hipLaunchKernelGGL(merge_kernel, grid, dim3(NT), 0, s, p, t);
+  hipLaunchKernelGGL(merge_kernel<false>, grid, dim3(NT), 0, s, p, t, (float2 *)nullptr, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_stats(const ScoreParams &p, const SegTable &t, float2 *run, int first, hipStream_t s) {
+  const dim3 grid((p.Rpad + MERGE_ROWS - 1) / MERGE_ROWS, t.nseq * p.Hkv);
+  hipLaunchKernelGGL(merge_kernel<true>, grid, dim3(NT), 0, s, p, t, run, first);
   return hipGetLastError();
 }
 

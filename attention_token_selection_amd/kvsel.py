@@ -55,6 +55,7 @@ class KvselProblem(ctypes.Structure):
         ("sink_tokens", ctypes.c_int32),
         ("recent_tokens", ctypes.c_int32),
         ("gqa", ctypes.c_int32),
+        ("stream_keys", ctypes.c_int32),
     ]
 
 
@@ -123,7 +124,7 @@ class Problem:
                  L: int = 0, batch: int = 1, has_decode: bool = False, alpha: float = 0.0, causal: bool = True,
                  scale: float = 0.0, pool: str = "none", pool_kernel: int = 1, k: int = 0,
                  budgets=None, key_chunk: int = 0, weighting: str = "alpha", lam: float = 0.0, sink: int = 0,
-                 recent: int = 0, gqa: str = "sum"):
+                 recent: int = 0, gqa: str = "sum", stream_keys: int = 0):
         if seq_lens is None:
             seq_lens = [int(L)] * int(batch)
         self.seq_lens = [int(x) for x in seq_lens]
@@ -159,6 +160,7 @@ class Problem:
         s.sink_tokens = int(sink)
         s.recent_tokens = int(recent)
         s.gqa = GQAS[gqa] if isinstance(gqa, str) else int(gqa)
+        s.stream_keys = int(stream_keys)
         self.struct = s
 
     @property

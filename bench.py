@@ -128,9 +128,10 @@ def _graph_ms(torch, stream, fn, reps):
 def time_variants(kv, W, spec, cases, outs, stream, reps):
     """The same 32 layers through the DeferKV variant (one decode-step row,
     exponential row weights with lambda 0.1, 16 sinks and 32 recent kept), the
-    same with the guide's mean query per group, and KVDrive's warm-up (profile
-    over all layers, then the three-tier ranking with 2048 fast and 8192
-    middle slots)."""
+    same with the guide's mean query per group, TideKV's bounded-memory
+    streaming form (8192 keys per step), and KVDrive's warm-up (profile over
+    all layers, then the three-tier ranking with 2048 fast and 8192 middle
+    slots)."""
     import torch
 
     dev = cases[0]["K"].device
@@ -161,6 +162,26 @@ def time_variants(kv, W, spec, cases, outs, stream, reps):
         res[name] = {"ms_per_step": ms, "tokens_per_s": L * spec.layers * spec.batch / (ms * 1e-3),
                      "what": "kvsel_compress per layer, 32 layers, w'=33 (decode row), k=2048"}
         del wsv
+    # TideKV's bounded-memory streaming form: the same selection in steps of
+    # 8192 keys, with a workspace that does not grow with the prefix
+    for C in (8192, 16384):
+        ps = kv.Problem(**dict(base, stream_keys=C))
+        wsb, _ = kv.kvsel_plan(ps)
+        wss = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        calls = [kv.bind_compress(ps, c["Q"], c["K"], c["V"], o["idx"], o["K_out"], o["V_out"], None, wss, stream)
+                 for c, o in zip(cases, outs)]
+
+        def run_s():
+            for call in calls:
+                call()
+
+        ms = _graph_ms(torch, stream, run_s, reps)
+        whole = kv.kvsel_plan(kv.Problem(**base))[0]
+        res[f"tidekv_streaming_{C}"] = {
+            "ms_per_step": ms, "tokens_per_s": L * spec.layers * spec.batch / (ms * 1e-3),
+            "workspace_MiB": wsb / 2 ** 20, "whole_prefix_workspace_MiB": whole / 2 ** 20,
+            "what": f"kvsel_compress with stream_keys={C}, 32 layers, k=2048"}
+        del wss
     pw = kv.Problem(**dict(base, pool="none"))
     wsb, _ = kv.kvsel_plan(pw)
     wsw = torch.empty(wsb, dtype=torch.uint8, device=dev)

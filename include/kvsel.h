@@ -142,6 +142,7 @@ typedef struct kvsel_problem {
   int32_t sink_tokens;           /* >= 0: positions 0 .. sink-1 of every sequence are always kept */
   int32_t recent_tokens;         /* >= 0: positions L_b-recent .. L_b-1 are always kept */
   int32_t gqa;                   /* a kvsel_gqa value; 0 is KVSEL_GQA_SUM */
+  int32_t stream_keys;           /* 0, or a multiple of 2048: kvsel_compress's streaming form (below) */
 } kvsel_problem;
 
 /* KVSEL_ABI_VERSION of the loaded library. */
@@ -206,6 +207,20 @@ kvsel_status kvsel_gather(const kvsel_problem *p, const int32_t *idx, const void
 /*
  * Steps 1-7 in one call: idx, K_out, V_out and (if not NULL) pooled; the
  * unpooled scores stay in the workspace.
+ *
+ * With p->stream_keys = C > 0 (a multiple of 2048) it takes TideKV's
+ * memory-bounded form instead (§4.2, two-pass blockwise streaming top-k):
+ * pass 1 visits the prefix C keys at a time, folding each step's row
+ * statistics into running ones; pass 2 visits it again C keys at a time
+ * (plus the pool's half width on each side), pools the step's scores and
+ * merges them into a running top-k of each (sequence, KV head).  The
+ * workspace (kvsel_plan's size) then depends on C, the budgets, B, Hkv and
+ * the rows, not on the prefix length; no whole-prefix score buffer exists,
+ * so `pooled` must be NULL, and the other workspace entry points reject
+ * such a problem (KVSEL_EINVAL).  C plus the largest budget must not exceed
+ * 2^20.  The kept positions are those of the whole-prefix form, up to
+ * positions whose pooled scores tie to within fp32 rounding (the row
+ * statistics are merged in another order).
  */
 kvsel_status kvsel_compress(const kvsel_problem *p, const void *Q, const void *K, const void *V,
                             int32_t *idx, void *K_out, void *V_out, float *pooled,

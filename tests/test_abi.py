@@ -76,6 +76,8 @@ BAD = {
     "sink_negative": dict(sink=-1),
     "recent_negative": dict(recent=-2),
     "gqa_unknown": dict(gqa=2),
+    "stream_not_2048": dict(stream_keys=1000),
+    "stream_negative": dict(stream_keys=-2048),
 }
 
 
@@ -171,7 +173,7 @@ def test_struct_layout_matches_c():
 #define F(x) printf("%s %zu\n", #x, offsetof(kvsel_problem, x));
 int main(void) { F(batch) F(Hq) F(Hkv) F(d) F(L) F(seq_offsets_h) F(w) F(has_decode) F(alpha) F(causal)
   F(scale) F(pool) F(pool_kernel) F(k) F(budgets_h) F(key_chunk) F(weighting) F(lambda) F(sink_tokens)
-  F(recent_tokens) F(gqa) printf("size %zu\n", sizeof(kvsel_problem)); return 0; }
+  F(recent_tokens) F(gqa) F(stream_keys) printf("size %zu\n", sizeof(kvsel_problem)); return 0; }
 '''
     import tempfile
 
@@ -215,3 +217,31 @@ def test_allocate_budgets_hand_and_validation():
     for bad in (([[0, 1]], [1, 1], 5), ([[0, 1]], [-1, 1], 5), ([[0, float("nan")]], [0, 1], 5)):
         with pytest.raises(kv.KvselError):
             kv.kvsel_allocate_budgets(*bad)
+
+
+def test_streaming_workspace_is_bounded():
+    """With stream_keys the workspace does not grow with the prefix length."""
+    sizes = []
+    for L in (4096, 65536, 1 << 20):
+        p = kv.Problem(Hq=32, Hkv=8, w=32, L=L, pool="max", pool_kernel=7, k=2048, stream_keys=32768)
+        sizes.append(kv.kvsel_plan(p)[0])
+    assert sizes[0] == sizes[1] == sizes[2]
+    whole = kv.kvsel_plan(kv.Problem(Hq=32, Hkv=8, w=32, L=1 << 20, pool="max", pool_kernel=7, k=2048))[0]
+    assert sizes[0] * 8 < whole
+    # budgets too large for one candidate row
+    p = kv.Problem(Hq=4, Hkv=1, w=1, L=1 << 20, k=1 << 20, stream_keys=2048)
+    assert _status(p) == kv.KVSEL_EUNSUPPORTED
+
+
+def test_streaming_rejected_by_whole_prefix_entry_points():
+    p = kv.Problem(Hq=4, Hkv=1, w=1, L=8, k=2, stream_keys=2048)
+    ws, _ = kv.kvsel_plan(p)
+    buf, a = _aligned_buffer(ws)
+    A = ctypes.c_void_p(a)
+    lib = kv._lib
+    sz = ctypes.c_size_t(ws)
+    for st in (lib.kvsel_score(p.ref(), A, A, A, A, sz, None), lib.kvsel_row_stats(p.ref(), A, A, A, sz, None),
+               lib.kvsel_pool_topk(p.ref(), A, A, A, A, sz, None),
+               lib.kvsel_compress(p.ref(), A, A, A, A, A, A, A, A, sz, None)):
+        assert st == kv.KVSEL_EINVAL
+    del buf
