@@ -1,14 +1,19 @@
 #!/usr/bin/env python3
 """Throughput of attention-score-based KV-cache selection on one MI355X.
 
-Workload: Llama-3.1-8B-shaped prefill compression, all 32 layers one after
-another, batch 1, L = 32768 prefix tokens, Hq = 32, Hkv = 8, d = 128, bf16,
+Workload: Llama-3.1-8B-shaped prefill compression of all 32 layers, batch 1, L = 32768 prefix tokens, Hq = 32, Hkv = 8, d = 128, bf16,
 observation window w = 32, max pool 7, budget k = 2048 per KV head; keys
 N(0,1)/sqrt(d) with 1% planted positions in runs of 1-16 tokens (seeded
 synthetic inputs, generated on the GPU before timing).
 
 A step is one kvsel_compress per layer (scores -> pool -> top-k -> gather)
-for all 32 layers, with every input resident in HBM.  Prints one JSON line.
+for all 32 layers, with every input resident in HBM.  The layers'
+compressions are independent of one another (each layer is compressed when
+its prefill ends, while the next layer's prefill runs), so a step spreads
+them over --streams streams (layer l on stream l mod S, each stream with its
+own workspace), forked from and joined to the timed stream; the small,
+latency-bound kernels of one layer then overlap with the score passes of
+another.  Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -209,6 +214,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle time the CPU baseline runs for, in whole layers (0: skip)")
     ap.add_argument("--stage-reps", type=int, default=3)
+    ap.add_argument("--streams", type=int, default=4,
+                    help="spread the layers' independent compressions over this many streams (layer l on "
+                         "stream l mod S, each with its own workspace), forked from and joined to the timed stream")
     ap.add_argument("--variants", type=int, default=1,
                     help="also time the DeferKV and KVDrive warm-up variants on the same layers (0: skip)")
     ap.add_argument("--variants-only", type=int, default=0,
@@ -255,12 +263,22 @@ def main():
     if args.variants_only:
         print(json.dumps({"variants": time_variants(kv, W, spec, cases, outs, stream, args.stage_reps)}), flush=True)
         return
-    calls = [kv.bind_compress(p, c["Q"], c["K"], c["V"], o["idx"], o["K_out"], o["V_out"], None, ws, stream)
-             for c, o in zip(cases, outs)]
+    n_streams = max(1, args.streams)
+    side = [stream] if n_streams == 1 else [torch.cuda.Stream(device=dev) for _ in range(n_streams)]
+    side_ws = [ws] + [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(n_streams - 1)]
+    calls = [kv.bind_compress(p, c["Q"], c["K"], c["V"], o["idx"], o["K_out"], o["V_out"], None,
+                              side_ws[l % n_streams], side[l % n_streams])
+             for l, (c, o) in enumerate(zip(cases, outs))]
 
     def step():
+        if n_streams > 1:
+            for st in side:
+                st.wait_stream(stream)
         for call in calls:
             call()
+        if n_streams > 1:
+            for st in side:
+                stream.wait_stream(st)
 
     with torch.cuda.stream(stream):
         step()
@@ -363,8 +381,10 @@ def main():
         "data": "synthetic (seeded, generated on the GPU)",
         "config": {
             "workload": "llama3.1-8b-shaped prefill KV selection: 32 layers, batch 1, L=32768, Hq=32, Hkv=8, "
-                        "d=128, w=32, max pool 7, k=2048 per KV head",
+                        "d=128, w=32, max pool 7, k=2048 per KV head; the layers' independent compressions "
+                        "spread over streams",
             "layers": spec.layers, "batch": spec.batch, "seq_len": L, "graph": bool(args.graph),
+            "streams": n_streams,
         },
         "hbm_frac_path": path_gbs / HBM_PEAK_GBS,
         "path_GBps": path_gbs,
