@@ -51,9 +51,12 @@ struct Plan {
 };
 
 int auto_key_block(int64_t head_keys, int64_t cap) {
-  // Aim for about 1024 workgroups (four per compute unit) over the launch,
-  // in whole 32-key tiles, at least two tiles per workgroup.
-  const int64_t wgs = 1024;
+  // Aim for about 512 workgroups (two per compute unit) over the launch,
+  // in whole 32-key tiles, at least two tiles per workgroup.  Larger blocks
+  // load each head's queries fewer times, and a launch then leaves room for
+  // another layer's kernels on other streams; 512 measured faster than 1024
+  // and 256 both alone and with four layers in flight.
+  const int64_t wgs = 512;
   int64_t kb = (head_keys + wgs - 1) / wgs;
   kb = (kb + kKeyTile - 1) / kKeyTile * kKeyTile;
   kb = std::max<int64_t>(kb, 2 * kKeyTile);

@@ -46,8 +46,9 @@ def algorithmic_bytes(spec, kept_rows: int):
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "score_pass1_traffic_llama8b_L32k.json")
+# The kernel's code, and the host code that picks its launch shape (block size).
 TRAFFIC_SOURCES = [os.path.join(ROOT, "attention_token_selection_amd", "csrc", f)
-                   for f in ("score.hip", "kvsel_internal.h")]
+                   for f in ("score.hip", "kvsel_internal.h", "kvsel_api.cpp")]
 
 
 def source_digest():
