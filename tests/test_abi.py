@@ -102,11 +102,17 @@ def test_plan_rejects_bad_offsets_and_batch():
     assert kv._lib.kvsel_plan(p.ref(), None, None) == kv.KVSEL_EINVAL
 
 
-@pytest.mark.parametrize("kw", [dict(d=64), dict(Hq=65 * 2, Hkv=65), dict(Hq=32, Hkv=2, w=33)])
+@pytest.mark.parametrize("kw", [dict(d=64), dict(Hq=65 * 2, Hkv=65), dict(Hq=32, Hkv=2, w=33),
+                                dict(L=(1 << 20) + 1), dict(seq_lens=[100, (1 << 20) + 1], L=0)])
 def test_plan_unsupported(kw):
     base = dict(Hq=4, Hkv=2, w=2, L=64, k=2)
     base.update(kw)
     assert _status(kv.Problem(**base)) == kv.KVSEL_EUNSUPPORTED
+
+
+def test_longest_supported_sequence_plans():
+    """2^20 keys is the longest sequence the selection supports."""
+    assert _status(kv.Problem(Hq=4, Hkv=2, w=2, L=1 << 20, k=2)) == kv.KVSEL_OK
 
 
 def test_budget_clamping():

@@ -404,3 +404,38 @@ def test_graph_replays_match_eager(kv):
             assert torch.equal(e["K_out"], o["K_out"]), f"replay {rep}: K_out"
             assert torch.equal(e["V_out"], o["V_out"]), f"replay {rep}: V_out"
             assert torch.equal(e["pooled"], o["pooled"]), f"replay {rep}: pooled"
+
+
+# ---------------------------------------------------------------- the longest supported sequence
+def test_longest_sequence(kv):
+    """One sequence of 2^20 keys (the documented limit: 512 selection chunks)
+    at the Llama-3.1-8B shape, k = 4096: exact selection and gather on every
+    head, and one head against the oracle (which scores that head alone)."""
+    L = 1 << 20
+    spec = W.Spec("longest_L1M_max7_k4096", [L], w=32, pool="max", pool_kernel=7, k=4096, recipe="plant",
+                  plant_frac=0.002)
+    _say(f"{spec.name}: generating")
+    case = W.make_case(spec, layer=0, device=DEV)
+    p = kv.Problem(**W.problem_kwargs(spec))
+    out = kv.compress(p, case["Q"], case["K"], case["V"])
+    torch.cuda.synchronize()
+    idx = out["idx"]
+    offs = out["out_offsets"]
+    pooled = out["pooled"].cpu().numpy()
+    for h in range(spec.Hkv):
+        seg = idx[offs[h]:offs[h + 1]].long()
+        assert torch.equal(out["K_out"][offs[h]:offs[h + 1]], case["K"][seg, h])
+        assert torch.equal(out["V_out"][offs[h]:offs[h + 1]], case["V"][seg, h])
+        check_select_exact(seg.cpu().numpy(), pooled[h * L:(h + 1) * L], offs[h + 1] - offs[h], where=f"head {h}")
+    h = 5
+    G = spec.Hq // spec.Hkv
+    _say(f"{spec.name}: oracle on head {h}")
+    Qg = to_np64(case["Q"][0, :, h * G:(h + 1) * G])
+    Kh = to_np64(case["K"][:, h:h + 1])
+    S = O.head_scores(Qg, Kh, 0, 1, w=spec.w, has_decode=False, alpha=0.0, causal=True, scale=1.0 / math.sqrt(128))
+    P = O.pool1d(S, "max", 7)
+    ref_idx = O.select_topk(P, spec.k)
+    st = check_scores(pooled[h * L:(h + 1) * L], P, f"pooled head {h}")
+    from parity import check_selection
+    d = check_selection(idx[offs[h]:offs[h + 1]].cpu().numpy(), ref_idx, P, spec.k, L)
+    _say(f"{spec.name}: head {h} max_rel {st['max_rel']:.2e}, near-tie differences {d}")
