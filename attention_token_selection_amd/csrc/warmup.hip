@@ -6,8 +6,8 @@
 //
 // profile_kernel: per sequence, out[i] = sum over heads h of S[h][i] (heads
 // in order 0, 1, ..., so the sum is reproducible), plus the previous value
-// when accumulating over layers.  Each thread handles 4 consecutive
-// positions of one sequence; the loads of a head are coalesced.
+// when accumulating over layers.  One thread per position, all of its heads'
+// loads in flight at once; the loads of a head are coalesced.
 //
 // tier_fill_kernel / tier_mark_kernel: the labels start at 2 (backing store
 // only); the positions of a selection (from the pool and top-k kernels, run
@@ -19,27 +19,25 @@ namespace kvsel {
 namespace {
 
 constexpr int NT = 256;
-constexpr int PER = 4;
+constexpr int HBATCH = 8;  // heads loaded before they are summed
 
 __global__ __launch_bounds__(NT) void profile_kernel(ProfileParams p, SegTable t) {
   const int sb = blockIdx.y;
   const int64_t key0 = t.key_off[sb];
   const int L = (int)(t.key_off[sb + 1] - key0);
-  const int i0 = (blockIdx.x * NT + threadIdx.x) * PER;
-  if (i0 >= L) return;
-  const float *S = p.scores + (int64_t)p.Hkv * key0;
-  float acc[PER] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int h = 0; h < p.Hkv; ++h) {
-    const float *Sh = S + (int64_t)h * L;
+  const int i = blockIdx.x * NT + threadIdx.x;
+  if (i >= L) return;
+  const float *S = p.scores + (int64_t)p.Hkv * key0 + i;
+  float acc = 0.0f;
+  for (int h0 = 0; h0 < p.Hkv; h0 += HBATCH) {
+    float v[HBATCH];
 #pragma unroll
-    for (int e = 0; e < PER; ++e)
-      if (i0 + e < L) acc[e] += Sh[i0 + e];
-  }
-  float *out = p.profile + key0;
+    for (int u = 0; u < HBATCH; ++u) v[u] = (h0 + u < p.Hkv) ? S[(int64_t)(h0 + u) * L] : 0.0f;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    if (i0 + e < L) out[i0 + e] = p.accumulate ? out[i0 + e] + acc[e] : acc[e];
+    for (int u = 0; u < HBATCH; ++u) acc += v[u];  // heads in order; the padding adds +0
   }
+  float *out = p.profile + key0 + i;
+  *out = p.accumulate ? *out + acc : acc;
 }
 
 __global__ __launch_bounds__(NT) void tier_fill_kernel(int8_t *tier, int64_t n) {
@@ -64,7 +62,7 @@ __global__ __launch_bounds__(NT) void tier_mark_kernel(const int32_t *idx, int8_
 
 hipError_t launch_profile(const ProfileParams &p, const SegTable &t, int64_t lmax, hipStream_t s) {
   if (lmax <= 0 || t.nseq <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((lmax + NT * PER - 1) / (NT * PER)), t.nseq);
+  const dim3 grid((unsigned)((lmax + NT - 1) / NT), t.nseq);
   hipLaunchKernelGGL(profile_kernel, grid, dim3(NT), 0, s, p, t);
   return hipGetLastError();
 }
