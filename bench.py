@@ -7,13 +7,14 @@ N(0,1)/sqrt(d) with 1% planted positions in runs of 1-16 tokens (seeded
 synthetic inputs, generated on the GPU before timing).
 
 A step is one kvsel_compress per layer (scores -> pool -> top-k -> gather)
-for all 32 layers, with every input resident in HBM.  The layers'
-compressions are independent of one another (each layer is compressed when
-its prefill ends, while the next layer's prefill runs), so a step spreads
-them over --streams streams (layer l on stream l mod S, each stream with its
-own workspace), forked from and joined to the timed stream; the small,
-latency-bound kernels of one layer then overlap with the score passes of
-another.  Prints one JSON line.
+for all 32 layers, with every input resident in HBM, the layers processed
+one after another on one stream.  The layers' compressions are independent
+of one another (each layer is compressed when its prefill ends, while the
+next layer's prefill runs), so the same step is also timed with the layers
+spread over --overlap-streams streams (layer l on stream l mod S, each with
+its own workspace, forked from and joined to the timed stream), where one
+layer's small latency-bound kernels overlap another's score passes; that
+figure is reported beside the main one.  Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -215,9 +216,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="oracle time the CPU baseline runs for, in whole layers (0: skip)")
     ap.add_argument("--stage-reps", type=int, default=3)
-    ap.add_argument("--streams", type=int, default=4,
+    ap.add_argument("--streams", type=int, default=1,
                     help="spread the layers' independent compressions over this many streams (layer l on "
-                         "stream l mod S, each with its own workspace), forked from and joined to the timed stream")
+                         "stream l mod S, each with its own workspace), forked from and joined to the timed "
+                         "stream; 1 (default) processes the layers one after another")
+    ap.add_argument("--overlap-streams", type=int, default=4,
+                    help="also time the same step with the layers spread over this many streams, reported "
+                         "beside the main figure (0: skip)")
     ap.add_argument("--variants", type=int, default=1,
                     help="also time the DeferKV and KVDrive warm-up variants on the same layers (0: skip)")
     ap.add_argument("--variants-only", type=int, default=0,
@@ -264,35 +269,38 @@ def main():
     if args.variants_only:
         print(json.dumps({"variants": time_variants(kv, W, spec, cases, outs, stream, args.stage_reps)}), flush=True)
         return
-    n_streams = max(1, args.streams)
-    side = [stream] if n_streams == 1 else [torch.cuda.Stream(device=dev) for _ in range(n_streams)]
-    side_ws = [ws] + [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(n_streams - 1)]
-    calls = [kv.bind_compress(p, c["Q"], c["K"], c["V"], o["idx"], o["K_out"], o["V_out"], None,
-                              side_ws[l % n_streams], side[l % n_streams])
-             for l, (c, o) in enumerate(zip(cases, outs))]
+    def make_step(n_streams):
+        """The 32 layers' kvsel_compress calls, on one stream or spread over
+        n_streams forked from (and joined back to) the timed stream."""
+        side = [stream] if n_streams == 1 else [torch.cuda.Stream(device=dev) for _ in range(n_streams)]
+        side_ws = [ws] + [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(n_streams - 1)]
+        calls = [kv.bind_compress(p, c["Q"], c["K"], c["V"], o["idx"], o["K_out"], o["V_out"], None,
+                                  side_ws[l % n_streams], side[l % n_streams])
+                 for l, (c, o) in enumerate(zip(cases, outs))]
 
-    def step():
-        if n_streams > 1:
-            for st in side:
-                st.wait_stream(stream)
-        for call in calls:
-            call()
-        if n_streams > 1:
-            for st in side:
-                stream.wait_stream(st)
+        def step():
+            if n_streams > 1:
+                for st in side:
+                    st.wait_stream(stream)
+            for call in calls:
+                call()
+            if n_streams > 1:
+                for st in side:
+                    stream.wait_stream(st)
 
-    with torch.cuda.stream(stream):
-        step()
-    torch.cuda.synchronize()
-    graph = None
-    if args.graph:
+        with torch.cuda.stream(stream):
+            step()
+        torch.cuda.synchronize()
+        if not args.graph:
+            return step, (side, side_ws, calls)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             step()
         torch.cuda.synchronize()
-        run = graph.replay
-    else:
-        run = step
+        return graph.replay, (side, side_ws, calls, graph)
+
+    n_streams = max(1, args.streams)
+    run, keep_alive = make_step(n_streams)
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             run()
@@ -316,6 +324,27 @@ def main():
     tokens_per_step = L * spec.layers * spec.batch
     value = tokens_per_step * args.steps / elapsed
     ms_per_step = elapsed / args.steps * 1e3
+
+    overlap = None
+    if args.overlap_streams > 1 and n_streams == 1:
+        run_o, keep_o = make_step(args.overlap_streams)
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                run_o()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            for _ in range(args.steps):
+                run_o()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms_o = a.elapsed_time(b) / args.steps
+        overlap = {"streams": args.overlap_streams, "ms_per_step": ms_o,
+                   "tokens_per_s": tokens_per_step / (ms_o * 1e-3),
+                   "what": "the same 32 layers with their independent compressions spread over streams"}
+        del run_o, keep_o
 
     ab = algorithmic_bytes(spec, kept)
     path_gbs = ab["path"] * spec.layers * args.steps / elapsed / 1e9
@@ -381,9 +410,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded, generated on the GPU)",
         "config": {
-            "workload": "llama3.1-8b-shaped prefill KV selection: 32 layers, batch 1, L=32768, Hq=32, Hkv=8, "
-                        "d=128, w=32, max pool 7, k=2048 per KV head; the layers' independent compressions "
-                        "spread over streams",
+            "workload": "llama3.1-8b-shaped prefill KV selection: 32 layers processed one after another, "
+                        "batch 1, L=32768, Hq=32, Hkv=8, d=128, w=32, max pool 7, k=2048 per KV head",
             "layers": spec.layers, "batch": spec.batch, "seq_len": L, "graph": bool(args.graph),
             "streams": n_streams,
         },
@@ -401,6 +429,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "variants": variants,
+        "overlapped_layers": overlap,
     }
     print(json.dumps(line), flush=True)
 
