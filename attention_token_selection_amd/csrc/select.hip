@@ -179,7 +179,9 @@ __device__ inline int chunk_len(int L, int c) { return min(CH, L - c * CH); }
 // ---------------------------------------------------------------- 1. pool + counting sort by first digit
 __global__ __launch_bounds__(NT) void pool_bucket_kernel(SelectParams p, SegTable t) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[NBIN];  // counts, then exclusive prefix
-  __shared__ __attribute__((aligned(16))) float stage[HOFF + CH + HOFF];  // pools wider than 9 only
+  // Dynamic: HOFF + CH + HOFF floats for pools wider than 2 FASTR + 1,
+  // nothing otherwise (the launch sizes it).
+  extern __shared__ __attribute__((aligned(16))) float stage[];
   __shared__ int tmp[NWAVE];
 
   const Segment g = segment_of(p, t, blockIdx.y, blockIdx.z);
@@ -290,12 +292,17 @@ __global__ __launch_bounds__(NT) void select_chunk_kernel(SelectParams p, SegTab
   __shared__ uint32_t candk[MAXC];       // keys of bin b1
   __shared__ uint16_t candc[MAXC];       // their chunks
   __shared__ uint32_t hist[2048];
-  __shared__ uint16_t win[MAXCH][WIN];   // per chunk: prefix entries 32 t0 .. 32 t0 + 32
-  __shared__ int ch_lo[MAXCH];           // per chunk: start of bin b1 in its bucket
-  __shared__ int ch_cb[MAXCH + 1];       // per chunk: first candidate index
-  __shared__ int ch_above[MAXCH];        // per chunk: keys in bins above b1
-  __shared__ int ch_gt[MAXCH];           // per chunk: candidates above tau
-  __shared__ int ch_eq[MAXCH];           // per chunk: candidates equal to tau
+  // Per-chunk arrays, in dynamic LDS sized for the launch's longest
+  // sequence (nch_cap chunks; select_lds_bytes): a launch of short
+  // sequences leaves room for several workgroups per compute unit.
+  extern __shared__ __attribute__((aligned(16))) int dyn[];
+  const int nch_cap = (int)gridDim.x / (GATHER ? 2 : 1);
+  int *ch_lo = dyn;                        // per chunk: start of bin b1 in its bucket
+  int *ch_cb = ch_lo + nch_cap;            // per chunk: first candidate index (nch_cap + 1)
+  int *ch_above = ch_cb + nch_cap + 1;     // per chunk: keys in bins above b1
+  int *ch_gt = ch_above + nch_cap;         // per chunk: candidates above tau
+  int *ch_eq = ch_gt + nch_cap;            // per chunk: candidates equal to tau
+  uint16_t (*win)[WIN] = reinterpret_cast<uint16_t (*)[WIN]>(ch_eq + nch_cap);  // per chunk: prefix entries 32 t0 .. 32 t0 + 32
   __shared__ int ge32[CSTEP];
   __shared__ uint16_t kept[CH];          // kept chunk-local positions, in output order
   __shared__ int tmp[NWAVE];
@@ -570,15 +577,26 @@ __global__ __launch_bounds__(NT) void select_chunk_kernel(SelectParams p, SegTab
 
 }  // namespace
 
+// Dynamic LDS of select_chunk_kernel for a launch whose longest sequence
+// has `nch` chunks: five int arrays (one with an extra entry) and the
+// prefix-entry windows.
+static size_t select_lds_bytes(int nch) {
+  return (size_t)(5 * nch + 1) * sizeof(int) + (size_t)nch * WIN * sizeof(uint16_t);
+}
+
 hipError_t launch_pool_topk(const SelectParams &p, const SegTable &t, hipStream_t s) {
   int64_t lmax = 0;
   for (int i = 0; i < t.nseq; ++i) lmax = std::max<int64_t>(lmax, t.key_off[i + 1] - t.key_off[i]);
-  const dim3 grid((unsigned)((lmax + CH - 1) / CH), p.Hkv, t.nseq);
-  hipLaunchKernelGGL(pool_bucket_kernel, grid, dim3(NT), 0, s, p, t);
+  const int nch = (int)((lmax + CH - 1) / CH);
+  if (nch < 1 || nch > MAXCH) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nch, p.Hkv, t.nseq);
+  const int r = (p.pool == 0) ? 0 : (p.pool_kernel - 1) / 2;
+  const size_t stage = (r > FASTR) ? (size_t)(HOFF + CH + HOFF) * sizeof(float) : 0;
+  hipLaunchKernelGGL(pool_bucket_kernel, grid, dim3(NT), stage, s, p, t);
   if (p.K_out)
-    hipLaunchKernelGGL(select_chunk_kernel<true>, dim3(2 * grid.x, grid.y, grid.z), dim3(NT), 0, s, p, t);
+    hipLaunchKernelGGL(select_chunk_kernel<true>, dim3(2 * grid.x, grid.y, grid.z), dim3(NT), select_lds_bytes(nch), s, p, t);
   else
-    hipLaunchKernelGGL(select_chunk_kernel<false>, grid, dim3(NT), 0, s, p, t);
+    hipLaunchKernelGGL(select_chunk_kernel<false>, grid, dim3(NT), select_lds_bytes(nch), s, p, t);
   return hipGetLastError();
 }
 
