@@ -207,6 +207,40 @@ def time_variants(kv, W, spec, cases, outs, stream, reps):
     return res
 
 
+def time_workloads(kv, W, stream, reps, skip):
+    """Every workload of the measurement plan other than the headline one
+    (index `skip`), each as one kvsel_compress call replayed from a graph:
+    milliseconds per call, prefix tokens per second, and the path's
+    algorithmic bytes (K once, Q, kept K/V read and written, indices) per
+    second against HBM peak.  Reported beside the headline figure."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    res = {}
+    for i in range(1, 6):
+        if i == skip:
+            continue
+        spec = W.config(i)
+        case = W.make_case(spec, device=dev)
+        p = kv.Problem(**W.problem_kwargs(spec))
+        out = kv.alloc_outputs(p, dev, pooled=False)
+        call = kv.bind_compress(p, case["Q"], case["K"], case["V"], out["idx"], out["K_out"], out["V_out"],
+                                None, out["ws"], stream)
+        ms = _graph_ms(torch, stream, call, reps)
+        kept = kv.kvsel_plan(p)[1][-1]
+        ab = algorithmic_bytes(spec, kept)
+        tokens = sum(spec.seq_lens)
+        res[spec.name] = {
+            "ms_per_call": ms, "tokens_per_s": tokens / (ms * 1e-3),
+            "path_GBps": ab["path"] / (ms * 1e-3) / 1e9, "hbm_frac_path": ab["path"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tokens": tokens, "kept_rows": kept,
+            "resident_in_infinity_cache": ab["K"] * 2 < 256 * 2 ** 20,
+        }
+        del case, out, call
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,6 +259,9 @@ def main():
                          "beside the main figure (0: skip)")
     ap.add_argument("--variants", type=int, default=1,
                     help="also time the DeferKV and KVDrive warm-up variants on the same layers (0: skip)")
+    ap.add_argument("--workloads", type=int, default=1,
+                    help="also time one kvsel_compress call of each other workload of the measurement plan "
+                         "(reported beside the main figure; 0: skip)")
     ap.add_argument("--variants-only", type=int, default=0,
                     help="only time the variants and print them (for a kernel trace of the variants alone)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -390,6 +427,7 @@ def main():
     traffic = counted_traffic()
 
     variants = time_variants(kv, W, spec, cases, outs, stream, args.stage_reps) if args.variants else None
+    workloads = time_workloads(kv, W, stream, args.stage_reps, skip=2) if args.workloads else None
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -429,6 +467,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "variants": variants,
+        "other_workloads": workloads,
         "overlapped_layers": overlap,
     }
     print(json.dumps(line), flush=True)
