@@ -81,7 +81,8 @@ kvsel_status plan_streaming(const kvsel_problem *p, Plan &P) {
   // A step has fewer keys than a whole prefix; blocks of at least 128 keys
   // keep each workgroup's query loads small next to its key loads.
   const int64_t step_keys = (int64_t)P.stream * P.B * P.Hkv;
-  P.kb1 = p->key_chunk > 0 ? p->key_chunk : std::max(128, auto_key_block(step_keys, 4096));
+  P.kb1 = std::max(128, auto_key_block(step_keys, 4096));
+  if (p->key_chunk > 0) P.kb1 = std::min(P.kb1, p->key_chunk);  // the caller's chunk bounds a block
   P.kb2 = std::max(128, auto_key_block(step_keys, 2048));
   P.nblk1_c = (P.stream + P.kb1 - 1) / P.kb1;
   P.nblk1_max = P.nblk1_c;
@@ -213,7 +214,10 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   P.nrt = (P.R + kRowTile - 1) / kRowTile;
   P.Rpad = P.nrt * kRowTile;
   const int64_t head_keys = P.seq_off[P.B] * P.Hkv;
-  P.kb1 = p->key_chunk > 0 ? p->key_chunk : auto_key_block(head_keys, 4096);
+  // A caller's key_chunk (TideKV's block size b_s) bounds a block; smaller
+  // blocks run the same blockwise procedure with more workgroups.
+  P.kb1 = auto_key_block(head_keys, 4096);
+  if (p->key_chunk > 0) P.kb1 = std::min(P.kb1, p->key_chunk);
   P.kb2 = auto_key_block(head_keys, 2048);
   P.nblk1_max = (int)((P.Lmax + P.kb1 - 1) / P.kb1);
   P.nblk2_max = (int)((P.Lmax + P.kb2 - 1) / P.kb2);

@@ -136,7 +136,9 @@ typedef struct kvsel_problem {
   int32_t pool_kernel;           /* odd, >= 1 (ignored for KVSEL_POOL_NONE) */
   int32_t k;                     /* uniform budget >= 0 when budgets_h is NULL */
   const int32_t *budgets_h;      /* host, B*Hkv budgets (>= 0, sequence-major), or NULL */
-  int32_t key_chunk;             /* keys per pass-1 statistics block (multiple of 32), 0 = library choice */
+  int32_t key_chunk;             /* most keys per pass-1 statistics block (multiple of 32; TideKV's b_s);
+                                    the library may use smaller blocks to fill the GPU (the result is
+                                    the same up to the rounding order of the block merge); 0 = library choice */
   int32_t weighting;             /* a kvsel_weighting value; 0 is KVSEL_WEIGHT_ALPHA */
   float lambda;                  /* KVSEL_WEIGHT_EXP: finite, >= 0 (0 gives equal weights) */
   int32_t sink_tokens;           /* >= 0: positions 0 .. sink-1 of every sequence are always kept */
