@@ -39,6 +39,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = kScoreThreads;        // 256 threads, 4 waves
 constexpr int NW = NT / 64;
@@ -116,8 +117,13 @@ __device__ inline float sum16(const float (&e)[16]) {
 }
 
 // RT: row tiles (of 32 rows) per wave.
-template <int PASS, int RT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 4 : 1))) void score_kernel(ScoreParams p, SegTable t) {
+// RT: full row tiles (of 32 rows) per wave.  SPLIT: there is one more row
+// tile (4 RT + 1 in all), split into four 16 x 16 blocks per key tile, one
+// per wave: wave v takes its rows 16 (v / 2) .. + 15 against the key tile's
+// keys 16 (v % 2) .. + 15, with v_mfma_f32_16x16x32_bf16, so that no wave
+// carries a whole extra tile (the slowest wave sets every step's pace).
+template <int PASS, int RT, bool SPLIT = false>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SPLIT ? 2 : RT == 1 ? 4 : 1))) void score_kernel(ScoreParams p, SegTable t) {
   // The LDS ring: one array per slot, so that the compiler can tell a
   // slot being read from the slots that loads are landing in.
   __shared__ __attribute__((aligned(16))) char tile0[TILE_BYTES];
@@ -186,6 +192,45 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 4 
     }
   }
 
+  // The split tile.  Lane l supplies, at k-step j (32 wide), row (or key)
+  // l % 16 of its block and the 16-byte chunk 4 j + l / 16 of it; the
+  // output holds entries 4 (l / 16) + i (i < 4) of the block's first
+  // operand against entry l % 16 of the second.  Pass 1: A = keys, B = rows,
+  // so a lane holds 4 keys of one row (sr); pass 2: A = rows, B = keys, so a
+  // lane holds 4 rows (sr4 + i) of one key.
+  const int s16 = lane & 15, s4 = lane >> 4;
+  const int srow = NW * RT * 32 + 16 * (wave >> 1);  // first row of this wave's block
+  const int skey = 16 * (wave & 1);                  // first key of this wave's block in a key tile
+  bf16x8 qs[4];
+  float ref5 = -INFINITY, zs5 = 0.0f, bias5[4];
+  int lim5 = 0;
+  if constexpr (SPLIT) {
+    const int row = srow + s16;
+    if (row < p.R) {
+      const int r = row / p.G;
+      const int gi = row - r * p.G;
+      const uint16_t *src = p.Q + ((int64_t)(b * p.wp + r) * p.Hq + h * p.G + gi) * (int64_t)kHeadDim + s4 * 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qs[j] = as_frag(*reinterpret_cast<const uint4 *>(src + 32 * j));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qs[j] = as_frag(make_uint4(0u, 0u, 0u, 0u));
+    }
+    lim5 = row_limit(row, p, L);
+    if constexpr (PASS == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bias5[i] = p.bias[(int64_t)seg * p.Rpad + srow + 4 * s4 + i];
+    }
+  }
+  // LDS byte offsets of this lane's split-tile key operand at k-step j: key
+  // skey + s16 of the tile, chunk 4 j + s4, swizzled like the 32-wide reads.
+  int srd[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int kr = skey + s16;
+    srd[j] = kr * ROWB + (((4 * j + s4) ^ (kr & 15)) << 4);
+  }
+
   const float cl2 = p.cl2;
   const int minlim = p.causal ? (L - p.w) : (L - 1);  // keys up to here are visible to every row
   const int ntile = (kb1 - kb0 + KT - 1) / KT;
@@ -239,6 +284,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 4 
         }
       }
     }
+    f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 kf = as_frag(*reinterpret_cast<const uint4 *>(slot + srd[j]));
+        if constexpr (PASS == 1)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qs[j], sacc, 0, 0, 0);
+        else
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qs[j], kf, sacc, 0, 0, 0);
+      }
+    }
     const bool need_mask = (i0 + KT - 1) > minlim;
 
     if constexpr (PASS == 1) {
@@ -263,7 +319,31 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 4 
         znew[k] = (k < my_rt) ? zs[k] + sum16(e) : 0.0f;
         bad |= (k < my_rt) && !(znew[k] <= kZLimit);
       }
+      // sacc[i]: key i0 + skey + 4 s4 + i, row srow + s16.
+      float znew5 = 0.0f;
+      if constexpr (SPLIT) {
+        float e5[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = fast_exp2(fmaf(sacc[i], cl2, -ref5));
+          e5[i] = (need_mask && (i0 + skey + 4 * s4 + i) > lim5) ? 0.0f : v;
+        }
+        znew5 = zs5 + ((e5[0] + e5[1]) + (e5[2] + e5[3]));
+        bad |= !(znew5 <= kZLimit);
+      }
       if (__builtin_expect(__ballot(bad) != 0ull, 0)) {
+        if constexpr (SPLIT) {
+          float m = ref5;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!need_mask || (i0 + skey + 4 * s4 + i) <= lim5) m = fmaxf(m, sacc[i] * cl2);
+          float z = (ref5 == -INFINITY || m == -INFINITY) ? 0.0f : zs5 * fast_exp2(ref5 - m);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!need_mask || (i0 + skey + 4 * s4 + i) <= lim5) z += fast_exp2(fmaf(sacc[i], cl2, -m));
+          ref5 = m;
+          zs5 = z;
+        }
         // Rare (always on a wave's first tile): move each reference up to
         // the largest logit seen so far and redo this tile's sum.
 #pragma unroll
@@ -287,6 +367,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 4 
       } else {
 #pragma unroll
         for (int k = 0; k < RT; ++k) zs[k] = znew[k];
+        if constexpr (SPLIT) zs5 = znew5;
       }
     } else {
       // acc[k][i]: row 8*(i/4) + 4*hf + i%4 of row tile k, key i0 + lr.
@@ -312,6 +393,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 4 
 #pragma unroll
       for (int k = 1; k < RT; ++k) s += part[k];
       s = sum_halves(s);
+      if constexpr (SPLIT) {
+        // sacc[i]: row srow + 4 s4 + i, key i0 + skey + s16.  Sum the rows,
+        // then over the four lane groups: every lane then holds the block's
+        // sum for key skey + s16, which lane lr adds when that is its key.
+        float s5 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = fast_exp2(fmaf(sacc[i], cl2, -bias5[i]));
+          s5 += (need_mask && (i0 + skey + s16) > row_limit(srow + 4 * s4 + i, p, L)) ? 0.0f : v;
+        }
+        s5 += __shfl_xor(s5, 16);
+        s5 += __shfl_xor(s5, 32);
+        s += ((lr >> 4) == (wave & 1)) ? s5 : 0.0f;
+      }
       if (hf == 0) red[wave * p.key_block + ti * KT + lr] = s;
     }
   };
@@ -350,6 +445,23 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 4 
       lse_merge(ref[k], zs[k], r2, z2);
       const int row = (wave + NW * k) * 32 + lr;
       if (hf == 0 && k < my_rt) part[row] = make_float2(ref[k], zs[k]);
+    }
+    if constexpr (SPLIT) {
+      // The four lanes of a row (s4 = 0..3), then the two waves of a row
+      // half (their key halves), in a fixed order.
+      float r2 = __shfl_xor(ref5, 16), z2 = __shfl_xor(zs5, 16);
+      lse_merge(ref5, zs5, r2, z2);
+      r2 = __shfl_xor(ref5, 32);
+      z2 = __shfl_xor(zs5, 32);
+      lse_merge(ref5, zs5, r2, z2);
+      __shared__ float2 xchg[NW / 2][16];
+      if ((wave & 1) && s4 == 0) xchg[wave >> 1][s16] = make_float2(ref5, zs5);
+      __syncthreads();
+      if (!(wave & 1) && s4 == 0) {
+        const float2 o = xchg[wave >> 1][s16];
+        lse_merge(ref5, zs5, o.x, o.y);
+        part[srow + s16] = make_float2(ref5, zs5);
+      }
     }
   }
 }
@@ -426,6 +538,10 @@ template <int PASS>
 hipError_t launch_pass(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s, size_t lds) {
   const dim3 grid(nblk, p.Hkv, t.nseq);
   const dim3 block(NT);
+  if (p.nrt == NW + 1) {  // one full row tile per wave plus a split one
+    hipLaunchKernelGGL((score_kernel<PASS, 1, true>), grid, block, lds, s, p, t);
+    return hipGetLastError();
+  }
   const int rt = (p.nrt + NW - 1) / NW;
   switch (rt) {
     case 1: hipLaunchKernelGGL((score_kernel<PASS, 1>), grid, block, lds, s, p, t); break;
