@@ -123,7 +123,7 @@ __device__ inline float sum16(const float (&e)[16]) {
 // keys 16 (v % 2) .. + 15, with v_mfma_f32_16x16x32_bf16, so that no wave
 // carries a whole extra tile (the slowest wave sets every step's pace).
 template <int PASS, int RT, bool SPLIT = false>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SPLIT ? 2 : RT == 1 ? 4 : 1))) void score_kernel(ScoreParams p, SegTable t) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SPLIT ? (RT > 2 ? 1 : 2) : RT > 1 ? 1 : 4))) void score_kernel(ScoreParams p, SegTable t) {
   // The LDS ring: one array per slot, so that the compiler can tell a
   // slot being read from the slots that loads are landing in.
   __shared__ __attribute__((aligned(16))) char tile0[TILE_BYTES];
@@ -538,8 +538,12 @@ template <int PASS>
 hipError_t launch_pass(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s, size_t lds) {
   const dim3 grid(nblk, p.Hkv, t.nseq);
   const dim3 block(NT);
-  if (p.nrt == NW + 1) {  // one full row tile per wave plus a split one
-    hipLaunchKernelGGL((score_kernel<PASS, 1, true>), grid, block, lds, s, p, t);
+  if (p.nrt % NW == 1 && p.nrt > NW) {  // whole row tiles per wave plus a split one
+    switch (p.nrt / NW) {
+      case 1: hipLaunchKernelGGL((score_kernel<PASS, 1, true>), grid, block, lds, s, p, t); break;
+      case 2: hipLaunchKernelGGL((score_kernel<PASS, 2, true>), grid, block, lds, s, p, t); break;
+      default: hipLaunchKernelGGL((score_kernel<PASS, 3, true>), grid, block, lds, s, p, t); break;
+    }
     return hipGetLastError();
   }
   const int rt = (p.nrt + NW - 1) / NW;
