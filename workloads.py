@@ -269,7 +269,7 @@ def small_cases():
         Spec("s_meanq_G1", [333], Hq=4, Hkv=4, w=5, pool="none", k=40, gqa="mean", recipe="plant"),
         # 4 n + 1 row tiles per KV head: n whole tiles per wave, the last one split into four 16 x 16
         # blocks (one per wave); five tiles (129 to 160 rows), nine (257 to 288), thirteen (385 to 416)
-        Spec("s_R160_spread", [517, 4100], Hq=32, Hkv=8, w=39, has_decode=True, alpha=0.2, pool="avg",
+        Spec("s_R160_split5", [517, 4100], Hq=32, Hkv=8, w=39, has_decode=True, alpha=0.2, pool="avg",
              pool_kernel=3, k=100, recipe="plant"),
         Spec("s_R130_G2_nocausal", [2049, 64], Hq=16, Hkv=8, w=64, has_decode=True, alpha=0.7, causal=False,
              pool="max", pool_kernel=5, k=77, recipe="decode_corr"),
