@@ -115,6 +115,18 @@ def test_longest_supported_sequence_plans():
     assert _status(kv.Problem(Hq=4, Hkv=2, w=2, L=1 << 20, k=2)) == kv.KVSEL_OK
 
 
+def test_key_chunk_caps_the_pass1_block():
+    """key_chunk bounds the pass-1 block (TideKV's b_s): a chunk above the
+    library's own block size changes nothing, a smaller one means more blocks
+    and so more per-block row records in the workspace."""
+    base = dict(Hq=32, Hkv=8, w=32, seq_lens=[4100, 2500], k=200)
+    ws0 = kv.kvsel_plan(kv.Problem(**base))[0]
+    assert kv.kvsel_plan(kv.Problem(**base, key_chunk=8192))[0] == ws0
+    ws64 = kv.kvsel_plan(kv.Problem(**base, key_chunk=64))[0]
+    ws32 = kv.kvsel_plan(kv.Problem(**base, key_chunk=32))[0]
+    assert ws0 < ws64 < ws32
+
+
 def test_budget_clamping():
     p = kv.Problem(Hq=4, Hkv=2, w=1, seq_lens=[5, 3], budgets=[[0, 9], [3, 2]])
     _, offs = kv.kvsel_plan(p)

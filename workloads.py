@@ -277,6 +277,12 @@ def small_cases():
              pool_kernel=5, k=100, recipe="decode_corr"),
         Spec("s_R388_split13", [900], Hq=16, Hkv=4, w=96, has_decode=True, alpha=0.4, pool="avg",
              pool_kernel=3, k=150, recipe="plant"),
+        # one KV head, G = 8: 8 x 18 = 144 rows, five row tiles
+        Spec("s_R144_G8_split5", [1500, 333], Hq=8, Hkv=1, w=17, has_decode=True, alpha=0.6, pool="max",
+             pool_kernel=3, k=120, recipe="decode_corr"),
+        # a caller's key_chunk below the library's own block size: the cap binds (64-key blocks)
+        Spec("s_chunk64_binds", [4100, 2500], Hq=32, Hkv=8, w=32, pool="avg", pool_kernel=5, k=200,
+             key_chunk=64, recipe="zipf"),
     ]
     return cases
 
