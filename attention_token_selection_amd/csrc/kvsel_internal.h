@@ -17,6 +17,15 @@ constexpr int kMaxPoolKernel = 255;  // widest pool supported
 constexpr int kSelectChunk = 2048;   // positions per pool / select workgroup
 constexpr int kSelectBins = 8192;    // bins of the first radix digit (top 13 bits of an order key)
 constexpr int kMaxChunks = 512;      // chunks per sequence, so L_b <= 2^20
+// Resident scoring (both passes of a key block in one workgroup, the block's
+// keys held in LDS between them).
+constexpr int kResThreads = 512;     // eight waves
+constexpr int kResBlock = 512;       // keys per workgroup (= threads: one position each in the epilogue)
+constexpr int kResHalo = 16;         // keys scored on each side of a block for the pool (pool radius <= 16)
+constexpr int kResMaxRows = 256;     // observation rows per KV head (16 row blocks of 16, two per wave)
+constexpr int kResBins = 2048;       // bins of the selection's first digit
+constexpr int kResDigitShift = 16;   // a bin spans 2^16 order-key steps (1/128 of a factor 2 in value)
+constexpr int kResSpinCap = 8192;    // polls of a block's wait for its segment before it computes what is missing
 
 // Per-launch description of the sequences and segments a kernel works on.
 // Travels by value in the kernel arguments, so no device-side tables are
@@ -62,6 +71,46 @@ struct QueryMeanParams {
   int items;       // B * w' * Hkv
 };
 
+// Words of the resident scoring's synchronisation area (64-bit):
+//   [0]                         T, the call token; the kernel that runs after
+//                               the scoring sets it to T + 1 for the next call
+//   [1]                         the T the last scoring ran with
+//   [2 + seg]                   == T + 1: segment seg's histogram lacks the
+//                               counts of blocks that stopped waiting
+//   [2 + nseg + sl * nblk + b]  == T + 1: block b of local segment sl has
+//                               published its row statistics
+// Flags from earlier calls hold smaller tokens, so nothing needs clearing.
+constexpr int kSyncIncomplete = 2;
+
+// The fused scoring of kvsel_compress: per block of kResBlock keys of one
+// (sequence, KV head) segment, pass 1, the segment's statistics merge,
+// pass 2 over the same keys (still in LDS), the pool and the block's
+// first-digit counting sort.
+struct ResidentParams {
+  const uint16_t *Q;     // bf16 [B][w'][Hq][d] (mean queries [B][w'][Hkv][d] with G = 1)
+  const uint16_t *K;     // bf16 [sum L][Hkv][d]
+  float *scores;         // optional: S in the public layout (nullptr: not written)
+  float *pooled;         // pooled scores, public layout
+  uint16_t *tab;         // [nseg][nblk_max][kResBins]: exclusive prefix of each block's digit histogram
+  uint32_t *bucket;      // [nseg][nblk_max][kResBlock]: each block's order keys grouped by digit
+  uint32_t *seg_hist;    // [nseg][kResBins]: each segment's digit histogram (its blocks clear it)
+  float *lse;            // [nseg][nblk_max][Rp]: per block and row, log2 of the sum of 2^(s log2 e)
+  uint64_t *sync;        // call tokens and flags (res_sync below)
+  int nseg;              // segments of the whole problem (global indices)
+  int Hq, Hkv, G, w, wp, R, Rp;  // Rp: rows rounded up to 16
+  int has_decode, causal;
+  float cl2, alpha;
+  int weighting;
+  float lam2, log2norm;
+  float wsum;            // sum of S over a segment's positions: G * sum_r c_r
+  int pool, pool_r;      // pool kind; half width (<= kResHalo)
+  float pool_width;
+  int sink, recent;
+  int nblk_max;          // blocks of the longest sequence
+  int spin_cap;          // polls before a block stops waiting (0: never wait)
+  int tables;            // 1: pool, pooled output and selection tables; 0: scores only
+};
+
 struct SelectParams {
   const float *scores;
   float *pooled;
@@ -70,6 +119,11 @@ struct SelectParams {
   uint16_t *tab_coarse;  // [nseg][nchunk_max][kSelectBins / 32]: every 32nd entry of tab_fine
   uint32_t *bucket;      // [nseg][nchunk_max][kSelectChunk]: each chunk's order keys grouped by first digit
   int nchunk_max;        // chunks of kSelectChunk positions in the longest sequence
+  // Tables of the resident scoring (launch_select_blocks): tab_fine and
+  // bucket then hold ResidentParams::tab and ::bucket.
+  const uint32_t *seg_hist;
+  uint64_t *sync;        // ResidentParams::sync
+  int nblk_max;
   int Hkv;
   int pool;              // 0 none, 1 avg, 2 max
   int pool_kernel;       // odd
@@ -141,6 +195,9 @@ hipError_t launch_stream_pool(const StreamParams &p, const SegTable &t, hipStrea
 hipError_t launch_stream_map(const StreamParams &p, const SegTable &vt, hipStream_t s);
 hipError_t launch_stream_final(const StreamParams &p, const SegTable &t, int32_t *idx, hipStream_t s);
 hipError_t launch_pool_topk(const SelectParams &p, const SegTable &t, hipStream_t s);
+hipError_t launch_resident_bump(uint64_t *sync, hipStream_t s);
+hipError_t launch_resident(const ResidentParams &p, const SegTable &t, int items, hipStream_t s);
+hipError_t launch_select_blocks(const SelectParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_gather(const GatherParams &p, const SegTable &t, hipStream_t s);
 
 }  // namespace kvsel

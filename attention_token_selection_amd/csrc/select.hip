@@ -35,6 +35,7 @@
 // unsigned key (-0 ranks as +0); reserved positions (DeferKV guide, Phase 3:
 // attention sinks and the recent window) take the largest key of all.
 #include "kvsel_internal.h"
+#include "kvsel_device.h"
 
 namespace kvsel {
 namespace {
@@ -58,19 +59,6 @@ static_assert(NBIN == 1 << (32 - DSHIFT), "first digit width");
 static_assert(NCOARSE == NT, "one coarse entry per thread");
 static_assert(HOFF >= HALO && HOFF % 4 == 0, "stage layout");
 static_assert(MAXCH <= 2 * NT, "chunk scans hold two chunks per thread");
-
-__device__ inline uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// The key a position competes with: reserved positions (the first `sink`
-// and the last `recent` of the sequence) take the largest key, above every
-// value's, so they are kept first (lowest position first among them).
-__device__ inline uint32_t select_key(float f, int pos, int L, int sink, int recent) {
-  return (pos < sink || pos >= L - recent) ? 0xffffffffu : order_key(f);
-}
 
 // N consecutive values of X from position `first` on (first may be
 // negative), `fill` outside [0, L); 16-byte loads where the run is in range
@@ -575,6 +563,331 @@ __global__ __launch_bounds__(NT) void select_chunk_kernel(SelectParams p, SegTab
   }
 }
 
+
+// ---------------------------------------------------------------- selection from the resident scoring's tables
+// The resident scoring leaves, per block of RBP = 512 positions, the
+// exclusive prefix of the block's first-digit histogram (a monotone
+// function of the order key; tab_fine, u16 [NB2]) and the block's keys
+// grouped by digit (bucket, u32 [RBP]), plus each segment's whole digit
+// histogram (seg_hist).  One workgroup per chunk of CH positions (CPB
+// blocks) takes the steps of select_chunk_kernel: b1 straight from the
+// segment's histogram; the keys of bin b1 from every block's bucket; their
+// whole 32-bit keys in three radix rounds (11 + 11 + 10 bits) over those
+// candidates; per-block kept counts; the chunk's ordered compaction and,
+// with K_out, the copy.  The digit function itself is never needed here.
+constexpr int RBP = kResBlock;
+constexpr int CPB = CH / RBP;            // blocks per chunk
+constexpr int NB2 = kResBins;
+static_assert(CPB == 4 && NB2 == 8 * NT, "four blocks per chunk; eight bins per thread");
+
+template <bool GATHER>
+__global__ __launch_bounds__(NT) void select_block_kernel(SelectParams p, SegTable t) {
+  __shared__ uint32_t candk[MAXC];       // keys of bin b1
+  __shared__ uint16_t candb[MAXC];       // their blocks
+  __shared__ uint32_t hist[2048];
+  // Per-block arrays in dynamic LDS, sized for the launch's longest sequence.
+  extern __shared__ __attribute__((aligned(16))) int dyn[];
+  const int nb_cap = (int)gridDim.x / (GATHER ? 2 : 1) * CPB;
+  int *b_lo = dyn;                        // per block: start of bin b1 in its bucket
+  int *b_cb = b_lo + nb_cap;              // per block: first candidate index (nb_cap + 1)
+  int *b_above = b_cb + nb_cap + 1;       // per block: keys in bins above b1
+  int *b_gt = b_above + nb_cap;           // per block: candidates above tau
+  int *b_eq = b_gt + nb_cap;              // per block: candidates equal to tau
+  __shared__ uint16_t kept[CH];           // kept chunk-local positions, in output order
+  __shared__ int tmp[NWAVE];
+  __shared__ int sh[4];
+
+  // The next call's token (the scoring that ran before has finished).
+  if ((blockIdx.x | blockIdx.y | blockIdx.z) == 0 && threadIdx.x == 0) p.sync[0] = p.sync[1] + 1;
+  const Segment g = segment_of(p, t, blockIdx.y, blockIdx.z);
+  const int c = GATHER ? (blockIdx.x >> 1) : blockIdx.x;
+  const int half = GATHER ? (blockIdx.x & 1) : 0;
+  const int p0 = c * CH;
+  if (p0 >= g.L) return;  // the whole workgroup leaves together
+  if (g.keff <= 0) return;
+  const int tid = threadIdx.x;
+  const int nb = (g.L + RBP - 1) / RBP;
+  const int n_me = chunk_len(g.L, c);
+  const int first = p0 + tid * PER;
+
+  int base = 0;   // first output slot of this chunk
+  int nkept = 0;  // kept positions of this chunk
+  if (g.keff >= g.L) {
+    base = p0;
+    nkept = n_me;
+    for (int i = tid; i < n_me; i += NT) {
+      if (half == 0) g.out[p0 + i] = p0 + i;
+      kept[i] = (uint16_t)i;
+    }
+  } else {
+    float v[PER];
+    load_run<PER>(g.P, g.L, first, g.vec_out, 0.0f, v);
+
+    const int64_t tab0 = (int64_t)g.seg * p.nblk_max;
+    const uint16_t *TF = p.tab_fine + tab0 * NB2;
+    const uint32_t *BK = p.bucket + tab0 * RBP;
+
+    // ---- b1: the digit b with ge(b) >= keff > ge(b + 1), where ge(b)
+    // counts the segment's keys whose digit is >= b.
+    if (tid == 0) {
+      sh[0] = 0;
+      sh[1] = 0;
+    }
+    {
+      uint32_t cnt[8];
+      if (p.sync[kSyncIncomplete + g.seg] != p.sync[1] + 1) {
+        const uint4 *SH = reinterpret_cast<const uint4 *>(p.seg_hist + (int64_t)g.seg * NB2);
+        const uint4 a0 = SH[2 * tid], a1 = SH[2 * tid + 1];
+        cnt[0] = a0.x; cnt[1] = a0.y; cnt[2] = a0.z; cnt[3] = a0.w;
+        cnt[4] = a1.x; cnt[5] = a1.y; cnt[6] = a1.z; cnt[7] = a1.w;
+      } else {
+        // Some block stopped waiting for its segment and left the histogram
+        // incomplete: rebuild it from every block's exclusive prefix table.
+#pragma unroll
+        for (int u = 0; u < 8; ++u) cnt[u] = 0u;
+        for (int j = 0; j < nb; ++j) {
+          const int len = min(RBP, g.L - j * RBP);
+          const uint16_t *row = TF + (int64_t)j * NB2 + 8 * tid;
+          uint32_t e[9];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) e[u] = row[u];
+          e[8] = (8 * tid + 8 < NB2) ? (uint32_t)row[8] : (uint32_t)len;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) cnt[u] += e[u + 1] - e[u];
+        }
+      }
+      int own = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) own += (int)cnt[u];
+      int tot;
+      int below = block_exscan(own, tmp, tot);  // keys in lower bins; tot = L
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int ge = tot - below;
+        const int gn = ge - (int)cnt[u];
+        if (ge >= g.keff && gn < g.keff) {
+          sh[0] = 8 * tid + u;
+          sh[1] = gn;
+        }
+        below += (int)cnt[u];
+      }
+      __syncthreads();
+    }
+    const int b1 = sh[0];
+    const int need = g.keff - sh[1];  // keys of bin b1 to keep, >= 1
+
+    // ---- per-block extent of bin b1, and candidate offsets
+    for (int j = tid; j < nb; j += NT) {
+      const int len = min(RBP, g.L - j * RBP);
+      const int lo = TF[(int64_t)j * NB2 + b1];
+      const int hi = (b1 + 1 < NB2) ? (int)TF[(int64_t)j * NB2 + b1 + 1] : len;
+      b_lo[j] = lo;
+      b_above[j] = len - hi;
+      b_cb[j] = hi - lo;
+      b_gt[j] = 0;
+      b_eq[j] = 0;
+    }
+    __syncthreads();
+    {
+      int a[8], s = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = 8 * tid + u;
+        a[u] = (j < nb) ? b_cb[j] : 0;
+        s += a[u];
+      }
+      int tot;
+      int ex = block_exscan(s, tmp, tot);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = 8 * tid + u;
+        if (j < nb) b_cb[j] = ex;
+        ex += a[u];
+      }
+      if (tid == 0) b_cb[nb] = tot;
+    }
+    __syncthreads();
+    const int m = b_cb[nb];  // keys in bin b1, >= need
+
+    // Candidate i lives in block j (the largest j with b_cb[j] <= i).
+    auto cand_block = [&](int i) {
+      int lo = 0, hi = nb - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (b_cb[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      return lo;
+    };
+    auto cand_addr = [&](int i, int j) { return (int64_t)j * RBP + b_lo[j] + (i - b_cb[j]); };
+    const bool in_lds = m <= MAXC;
+    if (in_lds) {
+      for (int i0 = 0; i0 < m; i0 += 4 * NT) {
+        uint32_t k[4];
+        int jb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * NT + tid;
+          jb[u] = (i < m) ? cand_block(i) : 0;
+          k[u] = (i < m) ? BK[cand_addr(i, jb[u])] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * NT + tid;
+          if (i < m) {
+            candk[i] = k[u];
+            candb[i] = (uint16_t)jb[u];
+          }
+        }
+      }
+      __syncthreads();
+    }
+    auto visit = [&](auto &&fn) {
+      for (int i = tid; i < m; i += NT) {
+        if (in_lds) {
+          fn(candk[i], (int)candb[i]);
+        } else {
+          const int j = cand_block(i);
+          fn(BK[cand_addr(i, j)], j);
+        }
+      }
+    };
+
+    // ---- radix rounds over the candidates' keys: bits [21, 32), [10, 21), [0, 10)
+    int rest = need;
+    uint32_t pre = 0u;
+    for (int hi = 32, lo = 21;; hi = lo, lo = (lo > 11) ? lo - 11 : 0) {
+      for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
+      __syncthreads();
+      const uint32_t dmask = (1u << (hi - lo)) - 1u;
+      visit([&](uint32_t k, int) {
+        if (hi == 32 || (k >> hi) == pre) atomicAdd(&hist[(k >> lo) & dmask], 1u);
+      });
+      __syncthreads();
+      // The bin holding the rest-th largest: thread tid owns bins [8 tid, 8 tid + 8).
+      uint32_t hc[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) hc[u] = hist[8 * tid + u];
+      int own = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) own += (int)hc[u];
+      int tot;
+      const int ex = block_exscan(own, tmp, tot);
+      int ab = tot - ex - own;  // keys in bins above this thread's
+#pragma unroll
+      for (int u = 7; u >= 0; --u) {
+        if (ab < rest && ab + (int)hc[u] >= rest) {
+          sh[2] = 8 * tid + u;
+          sh[3] = ab;
+        }
+        ab += (int)hc[u];
+      }
+      __syncthreads();
+      rest -= sh[3];
+      pre = (pre << (hi - lo)) | (uint32_t)sh[2];
+      __syncthreads();
+      if (lo == 0) break;
+    }
+    const uint32_t tau = pre;
+    const int take_eq = rest;  // keys equal to tau to keep (the lowest-positioned), >= 1
+
+    // ---- per-block kept counts; this chunk's first output slot and its
+    // share of the keys equal to tau
+    visit([&](uint32_t k, int j) {
+      if (k > tau) atomicAdd(&b_gt[j], 1);
+      else if (k == tau) atomicAdd(&b_eq[j], 1);
+    });
+    __syncthreads();
+    {
+      int e[8], es = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = 8 * tid + u;
+        e[u] = (j < nb) ? b_eq[j] : 0;
+        es += e[u];
+      }
+      int tot;
+      int eb = block_exscan(es, tmp, tot);  // equal keys in earlier blocks
+      int tk[8], sk[8], ss = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = 8 * tid + u;
+        tk[u] = min(e[u], max(0, take_eq - eb));
+        eb += e[u];
+        sk[u] = (j < nb) ? b_above[j] + b_gt[j] + tk[u] : 0;
+        ss += sk[u];
+      }
+      int sb = block_exscan(ss, tmp, tot);
+      // The chunk's blocks CPB c .. CPB c + CPB - 1 sit in one thread's eight.
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = 8 * tid + u;
+        if (j == CPB * c) {
+          sh[2] = sb;
+          sh[3] = tk[u] + ((u + 1 < 8) ? tk[u + 1] : 0) + ((u + 2 < 8) ? tk[u + 2] : 0) + ((u + 3 < 8) ? tk[u + 3] : 0);
+        }
+        sb += sk[u];
+      }
+      __syncthreads();
+    }
+    base = sh[2];
+    const int take_me = sh[3];  // keys equal to tau that this chunk keeps
+
+    // ---- ordered compaction of this chunk
+    uint32_t k[PER];
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const bool valid = first + e < g.L;
+      k[e] = select_key(v[e], first + e, g.L, p.sink, p.recent);
+      gt += (valid && k[e] > tau) ? 1 : 0;
+      eq += (valid && k[e] == tau) ? 1 : 0;
+    }
+    int tot;
+    const int packed = block_exscan((gt << 16) | eq, tmp, tot);
+    int eb = packed & 0xffff;  // keys equal to tau before this thread's, in this chunk
+    int slot = (packed >> 16) + min(eb, take_me);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const bool valid = first + e < g.L;
+      const bool is_eq = valid && k[e] == tau;
+      const bool keep = (valid && k[e] > tau) || (is_eq && eb < take_me);
+      if (keep && base + slot < g.keff) {  // always true; keeps every store inside the segment
+        if (half == 0) g.out[base + slot] = first + e;
+        kept[slot] = (uint16_t)(tid * PER + e);
+      }
+      slot += keep ? 1 : 0;
+      eb += is_eq ? 1 : 0;
+    }
+    nkept = min((tot >> 16) + min(tot & 0xffff, take_me), g.keff - base);
+  }
+
+  if constexpr (GATHER) {
+    // Copy this workgroup's half of the kept rows (rows 2 r + half), as in
+    // select_chunk_kernel.
+    __syncthreads();
+    const int part = tid & 15;
+    const int nmine = (nkept - half + 1) / 2;
+    constexpr int GR = NT / 16;
+    auto row_of = [&](int r) { return 2 * min(r, nmine - 1) + half; };
+    auto src = [&](int r) { return ((g.key0 + p0 + kept[row_of(r)]) * p.Hkv + g.h) * 16 + part; };
+    auto dst = [&](int r) { return (g.out0 + base + row_of(r)) * 16 + part; };
+    for (int r0 = tid >> 4; r0 < nmine; r0 += 4 * GR) {
+      const int64_t s0 = src(r0), s1 = src(r0 + GR), s2 = src(r0 + 2 * GR), s3 = src(r0 + 3 * GR);
+      const uint4 k0 = p.K[s0], k1 = p.K[s1], k2 = p.K[s2], k3 = p.K[s3];
+      const uint4 v0 = p.V[s0], v1 = p.V[s1], v2 = p.V[s2], v3 = p.V[s3];
+      p.K_out[dst(r0)] = k0;
+      p.V_out[dst(r0)] = v0;
+      p.K_out[dst(r0 + GR)] = k1;
+      p.V_out[dst(r0 + GR)] = v1;
+      p.K_out[dst(r0 + 2 * GR)] = k2;
+      p.V_out[dst(r0 + 2 * GR)] = v2;
+      p.K_out[dst(r0 + 3 * GR)] = k3;
+      p.V_out[dst(r0 + 3 * GR)] = v3;
+    }
+  }
+}
+
 }  // namespace
 
 // Dynamic LDS of select_chunk_kernel for a launch whose longest sequence
@@ -597,6 +910,24 @@ hipError_t launch_pool_topk(const SelectParams &p, const SegTable &t, hipStream_
     hipLaunchKernelGGL(select_chunk_kernel<true>, dim3(2 * grid.x, grid.y, grid.z), dim3(NT), select_lds_bytes(nch), s, p, t);
   else
     hipLaunchKernelGGL(select_chunk_kernel<false>, grid, dim3(NT), select_lds_bytes(nch), s, p, t);
+  return hipGetLastError();
+}
+
+}  // namespace kvsel
+
+namespace kvsel {
+
+hipError_t launch_select_blocks(const SelectParams &p, const SegTable &t, hipStream_t s) {
+  int64_t lmax = 0;
+  for (int i = 0; i < t.nseq; ++i) lmax = std::max<int64_t>(lmax, t.key_off[i + 1] - t.key_off[i]);
+  const int nch = (int)((lmax + CH - 1) / CH);
+  if (nch < 1 || nch > MAXCH) return hipErrorInvalidValue;
+  const size_t lds = (size_t)(5 * nch * CPB + 1) * sizeof(int);
+  const dim3 grid((unsigned)nch, p.Hkv, t.nseq);
+  if (p.K_out)
+    hipLaunchKernelGGL(select_block_kernel<true>, dim3(2 * grid.x, grid.y, grid.z), dim3(NT), lds, s, p, t);
+  else
+    hipLaunchKernelGGL(select_block_kernel<false>, grid, dim3(NT), lds, s, p, t);
   return hipGetLastError();
 }
 
