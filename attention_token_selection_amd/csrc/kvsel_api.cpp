@@ -55,7 +55,7 @@ struct Plan {
   bool res = false;
   int res_Rp = 0, res_nblk = 0, res_nsegl = 0, spin_cap = kResSpinCap;
   int64_t res_sync_words = 0;
-  size_t off_rsync = 0, off_rhist = 0, off_rlse = 0, off_rtab = 0, off_rbucket = 0;
+  size_t off_rsync = 0, off_rhist = 0, off_rlse = 0, off_rref = 0, off_rbias = 0, off_rtab = 0, off_rbucket = 0;
 };
 
 // Test hooks read from the environment: KVSEL_FORCE_TWO_PASS=1 sends
@@ -267,8 +267,8 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   off = align_up(off + nchunks * kSelectChunk * sizeof(uint32_t), 256);
   P.off_qmean = off;
   if (P.gqa == KVSEL_GQA_MEAN_QUERY) off = align_up(off + (size_t)P.B * P.wp * P.Hkv * p->d * sizeof(uint16_t), 256);
-  // The resident scoring: up to 256 rows, pools up to 33 wide, and blocks of
-  // 512 keys within the caller's key_chunk.
+  // The resident scoring: up to 128 rows, pools up to 33 wide, and blocks of
+  // 256 keys within the caller's key_chunk.
   const int pool_r = (P.pool == KVSEL_POOL_NONE) ? 0 : (P.pool_kernel - 1) / 2;
   P.res = P.R <= kResMaxRows && pool_r <= kResHalo && (p->key_chunk == 0 || p->key_chunk >= kResBlock) &&
           !env_force_two_pass();
@@ -277,13 +277,17 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
     P.res_Rp = 32 * ((P.R + 31) / 32);
     P.res_nblk = (int)((P.Lmax + kResBlock - 1) / kResBlock);
     P.res_nsegl = (int)std::min<size_t>(kMaxSeg, nseg);
-    P.res_sync_words = kSyncIncomplete + (int64_t)nseg + (int64_t)P.res_nsegl * P.res_nblk;
+    P.res_sync_words = kSyncFlags + 3 * (int64_t)nseg + (int64_t)P.res_nsegl * P.res_nblk;
     P.off_rsync = off;
     off = align_up(off + (size_t)P.res_sync_words * sizeof(uint64_t), 256);
     P.off_rhist = off;
     off = align_up(off + nseg * kResBins * sizeof(uint32_t), 256);
     P.off_rlse = off;
     off = align_up(off + nseg * P.res_nblk * P.res_Rp * sizeof(float), 256);
+    P.off_rref = off;
+    off = align_up(off + nseg * P.res_nblk * P.res_Rp * sizeof(float), 256);
+    P.off_rbias = off;
+    off = align_up(off + nseg * P.res_Rp * sizeof(float), 256);
     P.off_rtab = off;
     off = align_up(off + nseg * P.res_nblk * kResBins * sizeof(uint16_t), 256);
     P.off_rbucket = off;
@@ -501,6 +505,8 @@ ResidentParams resident_params(const Plan &P, const void *Q, const void *K, floa
   rp.bucket = reinterpret_cast<uint32_t *>(ws + P.off_rbucket);
   rp.seg_hist = reinterpret_cast<uint32_t *>(ws + P.off_rhist);
   rp.lse = reinterpret_cast<float *>(ws + P.off_rlse);
+  rp.biasg = reinterpret_cast<float *>(ws + P.off_rbias);
+  rp.refg = reinterpret_cast<float *>(ws + P.off_rref);
   rp.sync = reinterpret_cast<uint64_t *>(ws + P.off_rsync);
   rp.nseg = P.B * P.Hkv;
   rp.Hq = P.Hq;

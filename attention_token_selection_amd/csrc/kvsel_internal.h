@@ -19,10 +19,10 @@ constexpr int kSelectBins = 8192;    // bins of the first radix digit (top 13 bi
 constexpr int kMaxChunks = 512;      // chunks per sequence, so L_b <= 2^20
 // Resident scoring (both passes of a key block in one workgroup, the block's
 // keys held in LDS between them).
-constexpr int kResThreads = 512;     // eight waves
-constexpr int kResBlock = 512;       // keys per workgroup (= threads: one position each in the epilogue)
+constexpr int kResThreads = 256;     // four waves
+constexpr int kResBlock = 256;       // keys per workgroup (= threads: one position each in the epilogue)
 constexpr int kResHalo = 16;         // keys scored on each side of a block for the pool (pool radius <= 16)
-constexpr int kResMaxRows = 256;     // observation rows per KV head (16 row blocks of 16, two per wave)
+constexpr int kResMaxRows = 128;     // observation rows per KV head (a row tile of 32 per wave)
 constexpr int kResBins = 2048;       // bins of the selection's first digit
 constexpr int kResDigitShift = 16;   // a bin spans 2^16 order-key steps (1/128 of a factor 2 in value)
 constexpr int kResSpinCap = 8192;    // polls of a block's wait for its segment before it computes what is missing
@@ -72,15 +72,21 @@ struct QueryMeanParams {
 };
 
 // Words of the resident scoring's synchronisation area (64-bit):
-//   [0]                         T, the call token; the kernel that runs after
-//                               the scoring sets it to T + 1 for the next call
-//   [1]                         the T the last scoring ran with
-//   [2 + seg]                   == T + 1: segment seg's histogram lacks the
-//                               counts of blocks that stopped waiting
-//   [2 + nseg + sl * nblk + b]  == T + 1: block b of local segment sl has
-//                               published its row statistics
-// Flags from earlier calls hold smaller tokens, so nothing needs clearing.
-constexpr int kSyncIncomplete = 2;
+//   [0]                           T, the call token; the kernel that runs
+//                                 after the scoring sets it to T + 1 for
+//                                 the next call
+//   [1]                           the T the last scoring ran with
+//   [2 + seg]                     == T + 1: segment seg's histogram lacks the
+//                                 counts of blocks that stopped waiting
+//   [2 + nseg + seg]              == T + 1: segment seg's row biases are
+//                                 published
+//   [2 + 2 nseg + seg]            == T + 1: ... by a merger that saw every
+//                                 block publish
+//   [2 + 3 nseg + sl * nblk + b]  == T + 1: block b of local segment sl has
+//                                 published its row statistics
+// Flags from earlier calls hold other tokens, so nothing needs clearing.
+constexpr int kSyncFlags = 2;
+constexpr int kSyncIncomplete = kSyncFlags;
 
 // The fused scoring of kvsel_compress: per block of kResBlock keys of one
 // (sequence, KV head) segment, pass 1, the segment's statistics merge,
@@ -95,6 +101,8 @@ struct ResidentParams {
   uint32_t *bucket;      // [nseg][nblk_max][kResBlock]: each block's order keys grouped by digit
   uint32_t *seg_hist;    // [nseg][kResBins]: each segment's digit histogram (its blocks clear it)
   float *lse;            // [nseg][nblk_max][Rp]: per block and row, log2 of the sum of 2^(s log2 e)
+  float *biasg;          // [nseg][Rp]: the row biases, published by each segment's first block
+  float *refg;           // [nseg][nblk][Rp]: each block's reference logit per row (its e = 2^(x - ref))
   uint64_t *sync;        // call tokens and flags (res_sync below)
   int nseg;              // segments of the whole problem (global indices)
   int Hq, Hkv, G, w, wp, R, Rp;  // Rp: rows rounded up to 16

@@ -1,27 +1,38 @@
-// Resident scoring: TideKV's two-pass blockwise procedure ("Delayed KV
-// Eviction via Layer-Wise Chunked Prefill", §4.2) with each key block read
-// from memory once.
+// Fused scoring: TideKV's two-pass blockwise procedure ("Delayed KV Eviction
+// via Layer-Wise Chunked Prefill", §4.2) in one launch, with each key read
+// from memory once and each exponential computed once.
 //
-// Work unit: one workgroup of eight waves per block of 512 keys of one
-// (sequence, KV head) segment.  The block's keys (128 KiB) are loaded
-// straight from memory into LDS (global_load_lds, 16 bytes per lane, every
-// tile's loads issued up front) and stay there for both passes:
+// Work unit: one workgroup of four waves per block of 256 keys of one
+// (sequence, KV head) segment; two such workgroups share a compute unit, so
+// one's waits overlap the other's arithmetic.  The block's keys (64 KiB,
+// plus a halo tile for the pool) are loaded straight from memory into LDS
+// (global_load_lds, 16 bytes per lane, every tile's loads issued up front).
 //
-//  1. pass 1: the logits of the block against the segment's observation rows
-//     and, per row, log2 of the block's sum of exponentials (online, with a
-//     lazily raised reference);
-//  2. the per-row results are published, and the workgroup waits until every
-//     block of its segment has published, then merges them in block order
-//     into each row's normaliser;
-//  3. pass 2 over the same LDS-resident keys, plus a halo tile (the 16 keys
-//     before and after the block, for the pool): c_r * p_r summed over the
-//     rows of the group (TideKV §4.2 aggregation; DeferKV guide, Phase 2 row
-//     weights);
-//  4. the 1-D pool of the block's positions, the pooled scores written out,
+//  1. Pass 1: the logits of the block against the segment's observation
+//     rows.  For every (row, key) the lane keeps e = 2^(x - ref_row) in
+//     registers, where x = s * scale * log2(e) and ref_row is the row's
+//     largest logit in the block's first tile, and the row's block sum
+//     Z = sum of e.  Published per row: log2 of the block's sum, ref + log2 Z.
+//  2. The segment's first block waits until every block has published,
+//     merges the per-block results into each row's normaliser and weight,
+//     bias_r = log2(sum over blocks) - log2(c_r), and publishes the biases;
+//     the other blocks wait for them.
+//  3. Pass 2 without recomputing anything: the normalised, weighted
+//     probability of (row, key) is e * 2^(ref_row - bias_row), so each key's
+//     score S = sum over the group's rows (TideKV §4.2 aggregation; DeferKV
+//     guide, Phase 2 row weights) is one FMA per row.  Only the halo tile
+//     (16 keys each side of the block, for the pool) takes the MFMA and the
+//     exponential again.
+//  4. The 1-D pool of the block's positions, the pooled scores written out,
 //     and the block's counting sort by a first digit of each pooled value's
 //     order key: the exclusive prefix of the block's digit histogram, the
 //     keys grouped by digit, and the histogram added to the segment's.  The
 //     selection kernel finishes the top-k from these.
+//
+// Overflow: e stays below 2^100 as long as no logit of a row exceeds that
+// row's first-tile maximum by 100 (in log2 units).  A wave whose block sums
+// go past that bound (or are not finite) finds each row's true maximum over
+// the block first and computes e again, so e <= 1.
 //
 // The first digit.  A segment's scores sum to W = G * sum_r c_r, so they
 // centre near the mean W / L; the digit counts steps of 2^16 in the order
@@ -37,31 +48,26 @@
 // workgroups, which start together.  A block publishes its row results,
 // then a flag holding this call's token (one more than the token the
 // previous call saw, so flags left by earlier calls never match and nothing
-// needs clearing), and polls its segment's flags.  The wait is bounded:
-// after spin_cap polls the block computes pass 1 of the blocks that have
-// not published yet itself (the same code on the same keys, so the same
-// bits) and goes on, so the kernel ends whatever else shares the GPU and in
-// whatever order its workgroups run.  Such a block leaves the segment's
-// histogram alone and marks it incomplete; the selection then rebuilds it
-// from the blocks' tables.  Before publishing, every block clears its slice
-// of the segment histogram, so the histogram is clear before any block
-// that saw all flags adds to it.  Cross-workgroup data moves with
-// device-scope atomic loads and stores (coherent across the chip's L2s
-// without cache write-backs); a block's results are complete before its
-// flag is set.
+// needs clearing).  Every wait is bounded: after spin_cap polls a block
+// computes pass 1 of the blocks that have not published yet itself (the
+// same code on the same keys, so the same bits) and merges on its own, so
+// the kernel ends whatever else shares the GPU and in whatever order its
+// workgroups run.  Such a block leaves the segment's histogram alone and
+// marks it incomplete (the selection then rebuilds it from the blocks'
+// tables).  Before publishing, every block clears its slice of the segment
+// histogram, so the histogram is clear before any block that saw all flags
+// adds to it.  Cross-workgroup data moves with device-scope atomic loads
+// and stores (coherent across the chip's L2s without cache write-backs); a
+// block's results are complete before its flag is set.
 //
-// Rows and keys: the R = G * w' observation rows of the KV head (row =
-// window row * G + query head of the group) are split into row tiles of 32.
-// With at most four row tiles, waves 0-3 own row tiles 0-3 over the even
-// key tiles of the block and waves 4-7 the same rows over the odd ones
-// (two key groups, so that each key tile is read from LDS by four waves,
-// not eight); with five to eight, wave v owns row tile v over every key
-// tile.  Contraction: v_mfma_f32_32x32x16_bf16 over d = 128 in 8 k-steps;
-// lane l supplies, at k-step j, the 16-byte chunk 2 j + l / 32 of entry
-// l % 32 of each operand (the same permutation of the contraction index on
-// both operands leaves the products unchanged).  Pass 1 puts keys in the
-// first operand (a lane holds 16 keys of one row), pass 2 rows (a lane
-// holds 16 rows of one key).
+// Rows: the R = G * w' <= 128 observation rows of the KV head (row = window
+// row * G + query head of the group) are split into row tiles of 32; wave v
+// owns row tile v over every key tile.  Contraction: v_mfma_f32_32x32x16_bf16
+// over d = 128 in 8 k-steps, rows in the first operand and keys in the
+// second, so a lane holds 16 rows (8 (i / 4) + 4 (l / 32) + i % 4) of one
+// key (l % 32); lane l supplies, at k-step j, the 16-byte chunk 2 j + l / 32
+// of entry l % 32 of each operand (the same permutation of the contraction
+// index on both operands leaves the products unchanged).
 #include <algorithm>
 
 #include "kvsel_internal.h"
@@ -73,21 +79,21 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int NT = kResThreads;        // 512 threads
-constexpr int NW = NT / 64;            // 8 waves
+constexpr int NT = kResThreads;        // 256 threads
+constexpr int NW = NT / 64;            // 4 waves
 constexpr int KT = kKeyTile;           // 32 keys per tile
-constexpr int BLK = kResBlock;         // 512 keys per workgroup
-constexpr int NTILE = BLK / KT;        // 16 tiles
+constexpr int BLK = kResBlock;         // 256 keys per workgroup
+constexpr int NTILE = BLK / KT;        // 8 tiles
 constexpr int ROWB = kHeadDim * 2;     // 256 bytes per key row
 constexpr int TILE_BYTES = KT * ROWB;  // 8 KiB
 constexpr int HALO = kResHalo;         // 16
-constexpr int SIDX = BLK + 2 * HALO;   // per-wave key sums: block keys, then the halo tile's
+constexpr int SIDX = BLK + 2 * HALO;   // per-row-tile key sums: block keys, then the halo tile's
 constexpr int NBIN = kResBins;         // 2048
-constexpr int DSHIFT = kResDigitShift; // 21
-constexpr float kZLimit = 0x1p100f;    // a lane's running sum stays below this
-static_assert(TILE_BYTES == NT * 16, "one 16-byte chunk per lane and tile");
+constexpr int DSHIFT = kResDigitShift; // 16
+constexpr float kZLimit = 0x1p100f;
+static_assert(TILE_BYTES == 2 * NT * 16, "two 16-byte chunks per lane and tile");
 static_assert(NT == BLK, "one thread per position of a block in the epilogue");
-static_assert(NBIN == 4 * NT, "four bins per thread in the block scan");
+static_assert(NBIN == 8 * NT, "eight bins per thread in the block scan");
 static_assert(NBIN == 2048, "digits centre on bin 1024");
 static_assert(kResMaxRows == NW * 32, "one row tile of 32 per wave");
 
@@ -95,7 +101,7 @@ static_assert(kResMaxRows == NW * 32, "one row tile of 32 per wave");
 // pair's array, so the compiler waits only for that pair's loads (an array
 // it cannot tell apart from the others would make it wait for all of them).
 #define KVSEL_PAIR(n) __shared__ __attribute__((aligned(16))) char g_pair##n[2 * TILE_BYTES];
-KVSEL_PAIR(0) KVSEL_PAIR(1) KVSEL_PAIR(2) KVSEL_PAIR(3) KVSEL_PAIR(4) KVSEL_PAIR(5) KVSEL_PAIR(6) KVSEL_PAIR(7)
+KVSEL_PAIR(0) KVSEL_PAIR(1) KVSEL_PAIR(2) KVSEL_PAIR(3)
 #undef KVSEL_PAIR
 __shared__ __attribute__((aligned(16))) char g_halo[TILE_BYTES];
 
@@ -104,15 +110,11 @@ __device__ __forceinline__ char *pair_at(int i) {
     case 0: return g_pair0;
     case 1: return g_pair1;
     case 2: return g_pair2;
-    case 3: return g_pair3;
-    case 4: return g_pair4;
-    case 5: return g_pair5;
-    case 6: return g_pair6;
-    default: return g_pair7;
+    default: return g_pair3;
   }
 }
 
-// Key tile t (0 .. 15), or the halo tile (t = 16).
+// Key tile t (0 .. 7), or the halo tile (t = 8).
 __device__ __forceinline__ char *tile_at(int t) {
   return (t >= NTILE) ? g_halo : pair_at(t >> 1) + (t & 1) * TILE_BYTES;
 }
@@ -132,21 +134,13 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void wait_vm_upto(int n) {
   switch (n) {
     case 0: wait_vm<0>(); break;
-    case 1: wait_vm<1>(); break;
     case 2: wait_vm<2>(); break;
-    case 3: wait_vm<3>(); break;
     case 4: wait_vm<4>(); break;
-    case 5: wait_vm<5>(); break;
     case 6: wait_vm<6>(); break;
-    case 7: wait_vm<7>(); break;
     case 8: wait_vm<8>(); break;
-    case 9: wait_vm<9>(); break;
     case 10: wait_vm<10>(); break;
-    case 11: wait_vm<11>(); break;
     case 12: wait_vm<12>(); break;
-    case 13: wait_vm<13>(); break;
     case 14: wait_vm<14>(); break;
-    case 15: wait_vm<15>(); break;
     default: wait_vm<16>(); break;
   }
 }
@@ -157,8 +151,7 @@ __device__ __forceinline__ void barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// (r, z) <- merge of two partial log-sum-exp states in base 2.  Symmetric in
-// its operands bit for bit, so exchange partners agree exactly.
+// (r, z) <- merge of two partial log-sum-exp states in base 2.
 __device__ inline void lse_merge(float &r, float &z, float r2, float z2) {
   const float m = fmaxf(r, r2);
   if (m == -INFINITY) return;
@@ -174,7 +167,47 @@ __device__ inline float sum_halves(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+// Sum and maximum over the 32 lanes of a half-wave (l % 32), with the same
+// bits in all of them: partners within quads (DPP quad permutations), then
+// mirrored lanes of each 8 and of each 16 (DPP row mirrors), then the two
+// 16-lane rows (permlane16 swap).  Every step combines two lanes' values
+// with a commutative operation, so both partners hold the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within 8
+constexpr int kDppMirror = 0x140;      // lane i <- 15 - i within 16
+__device__ inline float other_row16(float x, float &mine) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  mine = __uint_as_float(sw[0]);
+  return __uint_as_float(sw[1]);
+}
+__device__ inline float sum32(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  x += dpp<kDppMirror>(x);
+  float a;
+  const float b = other_row16(x, a);
+  return a + b;
+}
+__device__ inline float max32(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppMirror>(x));
+  float a;
+  const float b = other_row16(x, a);
+  return fmaxf(a, b);
+}
+
 __device__ inline uint64_t ld_agent(const uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float ld_agent(const float *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline void st_agent(uint64_t *p, uint64_t v) {
@@ -187,15 +220,24 @@ __device__ inline void st_agent(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Observation row -> last key it sees.
-__device__ inline int row_limit(int row, const ResidentParams &p, int L) {
-  const int r = row / p.G;
-  if (!p.causal || r >= p.w) return L - 1;
-  return L - p.w + r;
+// Which of a lane's rows see a key.  Rows see every key up to
+// minlim = L - w (causal) or L - 1; past that, window row r sees keys up to
+// L - w + r and the decode row sees all.  With rows numbered r * G + g, row
+// x sees key k > L - w exactly when x >= (k - (L - w)) * G.  For the lane's
+// rows base + c (c = out_row's offset), row base + c sees the key iff
+// c >= the returned threshold; keys at or past kend (or before 0) are seen
+// by none.
+__device__ inline int vis_thr(int key, int kend, int minlim, int Lw, int G, int base) {
+  if (key < 0 || key >= kend) return INT_MAX;
+  if (key <= minlim) return INT_MIN;
+  return (key - Lw) * G - base;
 }
 
-// Exclusive prefix sum over the 512 threads; also returns the total.
-__device__ __forceinline__ int block_exscan512(int v, int *tmp, int &total) {
+// Offset of this lane's i-th output row from its first (4 l / 32 + 32 tile).
+__device__ __forceinline__ constexpr int row_off(int i) { return 8 * (i >> 2) + (i & 3); }
+
+// Exclusive prefix sum over the workgroup; also returns the total.
+__device__ __forceinline__ int block_exscan(int v, int *tmp, int &total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -217,61 +259,71 @@ __device__ __forceinline__ int block_exscan512(int v, int *tmp, int &total) {
   return before + x - v;
 }
 
-// Issues this wave's share of the block's 16 key tiles and of the halo tile
-// into LDS: 16-byte position P = 64 wave + lane of a tile receives chunk
-// (P & 15) ^ (key & 15) of key row P >> 4, which leaves the tile swizzled
-// (chunk c of key r at position c ^ (r & 15)), so the operand reads below
-// are free of bank conflicts.  Keys past the block's end re-read its last
-// key and halo keys outside the sequence are clamped into it, so every load
-// is in bounds; such keys are masked or never used.  Exactly 17 loads per
-// wave, in tile order.
+// Issues this wave's share of the block's 8 key tiles and of the halo tile
+// into LDS: 16-byte position P = 128 wave + 64 u + lane of a tile receives
+// chunk (P & 15) ^ (key & 15) of key row P >> 4, which leaves the tile
+// swizzled (chunk c of key r at position c ^ (r & 15)), so the operand reads
+// below are free of bank conflicts.  Keys past the block's end re-read its
+// last key and halo keys outside the sequence are clamped into it, so every
+// load is in bounds; such keys are masked or never used.  Exactly 18 loads
+// per wave, two per tile, in tile order (the halo tile last).
 __device__ inline void issue_block(const uint16_t *Kh, int64_t key0, int rowstride, int kb0, int kb1, int L,
                                    int wave, int lane) {
-  const int P = 64 * wave + lane;
-  const int row = P >> 4;
-  const int csrc = (P & 15) ^ (row & 15);
-  const uint16_t *base = Kh + key0 * (int64_t)rowstride + csrc * 8;
   typedef __attribute__((address_space(3))) void lds_void;
   typedef __attribute__((address_space(1))) void glb_void;
 #pragma unroll
-  for (int t = 0; t < NTILE; ++t) {
-    const int key = min(kb0 + t * KT + row, kb1 - 1);
-    __builtin_amdgcn_global_load_lds((glb_void *)(base + (int64_t)key * rowstride),
-                                     (lds_void *)(tile_at(t) + wave * 1024), 16, 0, 0);
-  }
-  int hk = (row < HALO) ? kb0 - HALO + row : kb1 + (row - HALO);
-  hk = min(max(hk, 0), L - 1);
-  __builtin_amdgcn_global_load_lds((glb_void *)(base + (int64_t)hk * rowstride),
-                                   (lds_void *)(g_halo + wave * 1024), 16, 0, 0);
-}
-
-// This lane's operand fragments of a tile (8 k-steps): entry l % 32, chunk
-// 2 j + l / 32, swizzled.
-__device__ __forceinline__ void read_tile(bf16x8 (&kf)[8], const char *tl, int lr, int hf) {
+  for (int t = 0; t <= NTILE; ++t) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    kf[j] = as_frag(*reinterpret_cast<const uint4 *>(tl + lr * ROWB + (((2 * j + hf) ^ (lr & 15)) << 4)));
+    for (int u = 0; u < 2; ++u) {
+      const int P = 128 * wave + 64 * u + lane;
+      const int row = P >> 4;
+      const int csrc = (P & 15) ^ (row & 15);
+      int key;
+      if (t < NTILE) {
+        key = min(kb0 + t * KT + row, kb1 - 1);
+      } else {
+        key = (row < HALO) ? kb0 - HALO + row : kb1 + (row - HALO);
+        key = min(max(key, 0), L - 1);
+      }
+      const uint16_t *src = Kh + (key0 + key) * (int64_t)rowstride + csrc * 8;
+      __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)(tile_at(t) + (128 * wave + 64 * u) * 16), 16, 0, 0);
+    }
+  }
 }
 
-// KG: key groups (2: up to four row tiles, the two groups taking alternate
-// key tiles; 1: five to eight row tiles, each wave every key tile).
-template <int KG>
-__global__ __launch_bounds__(NT) void resident_kernel(ResidentParams p, SegTable t) {
-  constexpr int NRTW = NW / KG;  // row tiles one key group covers
-  __shared__ __attribute__((aligned(16))) float red[NW * SIDX];  // pass 2: per-row-tile key sums; also scratch
+// The 32 x 32 logits of this wave's row tile against key tile tl: the
+// key fragments are read KSTEP k-steps at a time, to keep registers free.
+constexpr int KSTEP = 2;
+__device__ __forceinline__ f32x16 logits(const bf16x8 (&qf)[8], const char *tl, int lr, int hf) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int j0 = 0; j0 < 8; j0 += KSTEP) {
+    bf16x8 kf[KSTEP];
+#pragma unroll
+    for (int j = 0; j < KSTEP; ++j)
+      kf[j] = as_frag(*reinterpret_cast<const uint4 *>(tl + lr * ROWB + (((2 * (j0 + j) + hf) ^ (lr & 15)) << 4)));
+#pragma unroll
+    for (int j = 0; j < KSTEP; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[j0 + j], kf[j], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// Row of this lane's i-th output entry within its row tile.
+__device__ __forceinline__ int out_row(int i, int hf) { return 8 * (i >> 2) + 4 * hf + (i & 3); }
+
+__global__ __launch_bounds__(NT, 2) void resident_kernel(ResidentParams p, SegTable t) {
+  __shared__ __attribute__((aligned(16))) float red[NW * SIDX];  // pass 2: per-row-tile key sums; merge scratch
   __shared__ __attribute__((aligned(16))) float sbuf[SIDX];      // S by position: [HALO + x], x in [-HALO, n + HALO)
   __shared__ float bias_s[kResMaxRows];
-  __shared__ float2 xch[kResMaxRows];                             // pass 1: the odd key group's row states
   __shared__ int tmp[NW];
   __shared__ int s_misc[4];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int lr = lane & 31;  // entry of a 32-wide operand
+  const int lr = lane & 31;  // key of a tile
   const int hf = lane >> 5;  // chunk parity, and output rows 4 hf + ...
-  const int rt = wave % NRTW;
-  const int kg = wave / NRTW;
+  const int rt = wave;       // row tile
 
   // ---- this call's token (used only once pass 1 is done; set by the kernel
   // that ran after the previous scoring launch, so a plain, scalar load),
@@ -299,226 +351,266 @@ __global__ __launch_bounds__(NT) void resident_kernel(ResidentParams p, SegTable
   const int n = kb1 - kb0;
   const int rowstride = p.Hkv * kHeadDim;
   const uint16_t *Kh = p.K + (int64_t)h * kHeadDim;
-  const int nrt = p.Rp >> 5;        // row tiles of 32
-  const bool active = rt < nrt;     // this wave owns rows (wave-uniform)
+  const int nrt = p.Rp >> 5;     // row tiles of 32
+  const bool active = rt < nrt;  // this wave owns rows (wave-uniform)
 
-  // ---- query fragments of this wave's rows, issued before the key tiles so
-  // that every wait for a tile below also covers them.  Rows past R load
-  // row R - 1 instead (no branch, so nothing waits for these loads before
-  // the tiles are issued): their statistics are never used and their
-  // weight in pass 2 is 0.
-  bf16x8 qf[8];
+  // ---- query fragments of this wave's rows (loaded again wherever they are
+  // needed after the key tiles' logits, so they hold no registers across the
+  // waits).  Rows past R load row R - 1 instead: their statistics are never
+  // used and their weight in pass 2 is 0.
+  const uint16_t *qsrc;
   {
     const int row = min(rt * 32 + lr, p.R - 1);
     const int r = row / p.G;
     const int gi = row - r * p.G;
-    const uint16_t *src = p.Q + ((int64_t)(b * p.wp + r) * p.Hq + h * p.G + gi) * (int64_t)kHeadDim + hf * 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qf[j] = as_frag(*reinterpret_cast<const uint4 *>(src + 16 * j));
+    qsrc = p.Q + ((int64_t)(b * p.wp + r) * p.Hq + h * p.G + gi) * (int64_t)kHeadDim + hf * 8;
   }
-
+  auto load_q = [&](bf16x8 (&qf)[8]) {
+    const uint16_t *src = qsrc;
+    asm volatile("" : "+v"(src));  // a fresh load each time, not registers held from the last
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qf[j] = __builtin_bit_cast(bf16x8, *(g_u32x4 *)(src + 16 * j));
+  };
   const float cl2 = p.cl2;
   const int minlim = p.causal ? (L - p.w) : (L - 1);  // keys up to here are visible to every row
-  const int lim1 = row_limit(rt * 32 + lr, p, L);
-  float *lse_seg = p.lse + (int64_t)seg * p.nblk_max * p.Rp;
+  const int Lw = L - p.w;
+  const int rbase = rt * 32 + 4 * hf;  // this lane's first row
 
-  // Pass 1 of block ob (keys c0 .. c1 - 1): loads it into LDS, then log2 of
-  // each row's sum of exponentials over the block, published to lse.
-  //
-  // Pairs of tiles whose keys every row sees run first, in an unrolled loop
-  // that waits for each pair's own loads: a wave's first tile gives each
-  // lane its reference (its largest logit there), later tiles only add.
-  // The other tiles (past the block's end, or inside the window's causal
-  // triangle) run once every load has landed, with masks and a reference
-  // raised whenever the running sum would pass 2^100.  A wave whose quick
-  // sums passed that bound redoes the whole block the careful way.
-  auto pass1 = [&](int ob, int c0, int c1) {
-    issue_block(Kh, key0, rowstride, c0, c1, L, wave, lane);
-    const int nc = c1 - c0;
-    const int nvis = (min(c1 - 1, minlim) - c0 + 1) / KT;  // leading tiles all rows see in full
-    const int nfp = max(0, min(nvis, NTILE)) >> 1;          // ... as pairs
-    float ref = -INFINITY, zs = 0.0f;
-#pragma unroll
-    for (int tp = 0; tp < NTILE; tp += 2) {
-      if ((tp >> 1) < nfp) {
-        // This wave's parts of tiles tp and tp + 1 have landed (17 loads in
-        // tile order: tiles tp + 2 .. 16 may still be in flight), then everyone's.
-        wait_vm_upto(NTILE - (tp + 1));
-        barrier();
-        if (active) {
-#pragma unroll
-          for (int u = 0; u < 2 / KG; ++u) {
-            bf16x8 kf[8];
-            read_tile(kf, pair_at(tp >> 1) + ((KG == 2) ? kg : u) * TILE_BYTES, lr, hf);
-            f32x16 acc = {};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[j], acc, 0, 0, 0);
-            // acc[i]: key 8 (i / 4) + 4 hf + i % 4 of the tile, row rt * 32 + lr.
-            if (tp == 0 && u == 0) {
-              float m = -INFINITY;
-#pragma unroll
-              for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[i] * cl2);
-              ref = m;
-            }
-            float e[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) e[i] = fast_exp2(fmaf(acc[i], cl2, -ref));
-            const float a = ((e[0] + e[8]) + (e[4] + e[12])) + ((e[1] + e[9]) + (e[5] + e[13]));
-            const float c = ((e[2] + e[10]) + (e[6] + e[14])) + ((e[3] + e[11]) + (e[7] + e[15]));
-            zs += a + c;
-          }
-        }
-      }
-    }
-    wait_vm<0>();
-    barrier();
-    // The rest, and a redo by a wave whose quick sums went past the bound.
-    int g0 = 2 * nfp;
-    if (__ballot(active && !(zs <= kZLimit)) != 0ull) {
-      g0 = 0;
-      ref = -INFINITY;
-      zs = 0.0f;
-    }
-    const int ntl = (nc + KT - 1) / KT;
-    if (active) {
-      for (int tt = g0 + ((KG == 2) ? kg : 0); tt < ntl; tt += KG) {
-        bf16x8 kf[8];
-        read_tile(kf, tile_at(tt), lr, hf);
-        f32x16 acc = {};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[j], acc, 0, 0, 0);
-        const int kbase = c0 + tt * KT;
-        const bool need_mask = (kbase + KT - 1 > minlim) || (kbase + KT - 1 >= c1);
-        float e[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float v = fast_exp2(fmaf(acc[i], cl2, -ref));
-          const int key = kbase + 8 * (i >> 2) + 4 * hf + (i & 3);
-          e[i] = (need_mask && (key > lim1 || key >= c1)) ? 0.0f : v;
-        }
-        const float a = ((e[0] + e[8]) + (e[4] + e[12])) + ((e[1] + e[9]) + (e[5] + e[13]));
-        const float c = ((e[2] + e[10]) + (e[6] + e[14])) + ((e[3] + e[11]) + (e[7] + e[15]));
-        const float znew = zs + (a + c);
-        if (__builtin_expect(__ballot(!(znew <= kZLimit)) != 0ull, 0)) {
-          // Raise the reference to the largest visible logit seen so far and
-          // redo this tile's sum (always on a careful pass's first tile).
-          float m = ref;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kbase + 8 * (i >> 2) + 4 * hf + (i & 3);
-            if (!need_mask || (key <= lim1 && key < c1)) m = fmaxf(m, acc[i] * cl2);
-          }
-          float z = (ref == -INFINITY || m == -INFINITY) ? 0.0f : zs * fast_exp2(ref - m);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kbase + 8 * (i >> 2) + 4 * hf + (i & 3);
-            if (!need_mask || (key <= lim1 && key < c1)) z += fast_exp2(fmaf(acc[i], cl2, -m));
-          }
-          ref = m;
-          zs = z;
-        } else {
-          zs = znew;
-        }
-      }
-    }
-    // The two lanes of a row hold different keys: merge them (the same bits
-    // in both); then the key groups, in order; publish log2 of the row's
-    // block sum.
-    {
-      float r2 = __shfl_xor(ref, 32), z2 = __shfl_xor(zs, 32);
-      lse_merge(ref, zs, r2, z2);
-    }
-    const int row = rt * 32 + lr;
-    if (KG == 2) {
-      if (active && kg == 1 && hf == 0) xch[row] = make_float2(ref, zs);
-      __syncthreads();
-      if (active && kg == 0) lse_merge(ref, zs, xch[row].x, xch[row].y);
-    }
-    if (active && kg == 0 && hf == 0) {
-      const float l2 = (zs > 0.0f) ? ref + __log2f(zs) : -INFINITY;
-      st_agent(lse_seg + (int64_t)ob * p.Rp + row, l2);
-    }
-  };
-
-  // ---- pass 1 of our block, publish, wait for the segment's other blocks.
-  // After a wait that times out: pass 1 of every block of the segment that
-  // has not published (its owner writes the same bits when it gets to it),
-  // then our own keys again.
-  uint64_t *flags = p.sync + kSyncIncomplete + p.nseg + (int64_t)segl * p.nblk_max;
+  uint64_t *flags = p.sync + kSyncFlags + 3 * p.nseg + (int64_t)segl * p.nblk_max;
+  uint64_t *bflag = p.sync + kSyncFlags + p.nseg + seg;       // the segment's biases are published
+  uint64_t *bclean = p.sync + kSyncFlags + 2 * p.nseg + seg;  // ... by a merger that saw every block
   uint32_t *hist_seg = p.seg_hist + (int64_t)seg * NBIN;
+  float *lse_seg = p.lse + (int64_t)seg * p.nblk_max * p.Rp;
+  float *bias_seg = p.biasg + (int64_t)seg * p.Rp;
+  float *ref_seg = p.refg + (int64_t)seg * p.nblk_max * p.Rp;
+  const bool merger = blk == 0;
+
+  bf16x8 qf[8];
+  load_q(qf);  // issued before the key tiles: every wait for a tile covers it
+  issue_block(Kh, key0, rowstride, kb0, kb1, L, wave, lane);
   if (p.tables) {
     // this block's slice of the segment histogram, cleared before its flag
     const int z0 = (int)((int64_t)blk * NBIN / nb), z1 = (int)((int64_t)(blk + 1) * NBIN / nb);
     for (int i = z0 + tid; i < z1; i += NT) st_agent(hist_seg + i, 0u);
   }
-  int ob = blk;
-  int scan = 0;  // next block the late path looks at
-  bool late = false;
-  for (;;) {
-    const int c0 = ob * BLK;
-    pass1(ob, c0, min(L, c0 + BLK));
-    wait_vm<0>();  // this thread's stores (and the halo tile) are done
+
+  // Pass 1 (e for every (row, key) of the block, in registers), then the
+  // row biases: block 0 of the segment merges every block's results once
+  // they are all published and publishes the biases; the others wait for
+  // them.  The loop body computes pass 1 for the block whose keys are in
+  // LDS (cb): it runs again (same keys, same bits) after the block's sums
+  // overflowed, with each row's true block maximum as its reference; after
+  // a timed-out wait, for each block of the segment that has not published
+  // (its keys loaded here, its results published for it by the same code,
+  // so with the same bits it would publish itself); and at last for this
+  // block again, whose e the waits' detour overwrote.
+  const bool want_halo = p.pool_r > 0 && p.tables;
+  float e[NTILE][16];
+  float ref[16];
+  int cb = blk;            // the block whose keys are in LDS
+  bool true_max = false;   // ref holds each row's largest logit over block cb
+  bool published = false;  // this block's results are out
+  bool synced = false;     // waiting is over
+  bool late = false;       // the segment histogram must not be added to
+  int got = 0;             // 1 or 2: biases read from the merger (2: it saw some block late)
+  bool missing = false;    // some block's results were computed here
+  // The next block of the segment (from `from` on, ours excluded) that has
+  // not published, or -1; the whole workgroup gets the same answer.
+  auto next_missing = [&](int from) -> int {
+    if (tid == 0) {
+      int ob = from;
+      while (ob < nb && (ob == blk || ld_agent(flags + ob) == tok)) ++ob;
+      s_misc[3] = (ob < nb) ? ob : -1;
+    }
     __syncthreads();
-    if (!late) {
-      if (tid == 0) {
-        st_agent(flags + blk, tok);
-        if (blockIdx.x == 0) st_agent(p.sync + 1, T);
+    const int r = s_misc[3];
+    __syncthreads();
+    return r;
+  };
+  // Keys of block c into LDS (after every wave is done with the last ones).
+  auto load_block = [&](int c) {
+    int c0 = c * BLK;
+    asm volatile("" : "+s"(c0));  // addresses computed here, not held from the first issue
+    __syncthreads();
+    issue_block(Kh, key0, rowstride, c0, min(L, c0 + BLK), L, wave, lane);
+    wait_vm<0>();
+  };
+#pragma unroll 1
+  for (int round = 0;; ++round) {
+    const int c0 = cb * BLK;
+    const int c1 = min(L, c0 + BLK);
+    const bool quick = (c1 - 1 <= minlim) && c1 - c0 == BLK;  // no key of the block is masked
+    // The visibility thresholds are formed per tile, from a copy of the
+    // block start that the compiler cannot see through: otherwise it
+    // computes every tile's masks up front and holds them all.
+    int kbr = c0;
+    asm volatile("" : "+v"(kbr));
+    if (round > 0) {
+      load_q(qf);
+      __syncthreads();  // every wave's key loads (waited for) have landed
+    }
+#pragma unroll
+    for (int tt = 0; tt < NTILE; ++tt) {
+      if (round == 0) {
+        // This wave's loads of tile tt have landed (tiles tt + 1 .. 8 may
+        // still be in flight), then everyone's.
+        wait_vm_upto(2 * (NTILE - tt));
+        barrier();
       }
-      if (wave == 0) {
-        // poll the segment's flags, 64 per load, until all carry the token
-        int it = 0;
-        bool give_up = false;
-        for (;;) {
-          bool all = true;
-          for (int b0 = 0; b0 < nb; b0 += 64) {
-            const int bb = b0 + lane;
-            const bool ok = bb >= nb || ld_agent(flags + bb) == tok;
-            all = all && (__ballot(!ok) == 0ull);
+      // Every wave computes every tile, also a wave past the last row tile
+      // (its rows repeat row R - 1) and a tile past the block's end (its
+      // keys repeat the last one): the values are masked or never used, and
+      // straight-line code keeps e in registers.
+      const f32x16 acc = logits(qf, pair_at(tt >> 1) + (tt & 1) * TILE_BYTES, lr, hf);
+      // acc[i]: row rt * 32 + out_row(i), key c0 + tt * 32 + lr.
+      const int thr = vis_thr(kbr + tt * KT + lr, c1, minlim, Lw, p.G, rbase);
+      if (tt == 0 && !true_max) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x = acc[i] * cl2;
+          if (!quick) x = (row_off(i) >= thr) ? x : -INFINITY;
+          ref[i] = max32(x);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) e[tt][i] = fast_exp2(fmaf(acc[i], cl2, -ref[i]));
+      if (!quick) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) e[tt][i] = (row_off(i) >= thr) ? e[tt][i] : 0.0f;
+      }
+    }
+    // Each row's block sum; a sum past 2^100 (or not finite) anywhere in the
+    // block is an overflow (rare): then every wave takes its rows' true
+    // block maxima and the body runs again.
+    float zr[16];
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float z = e[0][i];
+#pragma unroll
+      for (int tt = 1; tt < NTILE; ++tt) z += e[tt][i];
+      zr[i] = sum32(z);
+      bad |= !(zr[i] <= kZLimit);
+    }
+    if (tid == 0) s_misc[0] = 0;
+    __syncthreads();
+    if (active && __ballot(bad) != 0ull && lane == 0) s_misc[0] = 1;
+    __syncthreads();
+    if (s_misc[0] && !true_max) {
+      float m[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m[i] = -INFINITY;
+#pragma unroll 1
+      for (int tt = 0; tt < NTILE; ++tt) {
+        const f32x16 acc = logits(qf, tile_at(tt), lr, hf);
+        const int thr = vis_thr(c0 + tt * KT + lr, c1, minlim, Lw, p.G, rbase);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (row_off(i) >= thr) m[i] = fmaxf(m[i], acc[i] * cl2);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ref[i] = max32(m[i]);
+      true_max = true;
+      continue;
+    }
+
+    if (cb != blk || !published) {
+      // ---- publish log2 of each row's block sum (for block cb)
+      if (active) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float l2 = (zr[i] > 0.0f) ? ref[i] + __log2f(zr[i]) : -INFINITY;
+          const int64_t at = (int64_t)cb * p.Rp + rt * 32 + out_row(i, hf);
+          if (lr == 0) {
+            st_agent(lse_seg + at, l2);
+            st_agent(ref_seg + at, ref[i]);  // for the neighbours' halo keys
           }
-          if (all) break;
-          if (++it > p.spin_cap) {
-            give_up = true;
+        }
+      }
+      wait_vm<0>();  // this thread's stores are done
+      __syncthreads();
+      if (cb == blk) {
+        if (tid == 0) {
+          st_agent(flags + blk, tok);
+          if (blockIdx.x == 0) st_agent(p.sync + 1, T);
+        }
+        published = true;
+      }
+    }
+    if (cb != blk) {
+      // on to the next block that has not published, else back to ours
+      const int ob = next_missing(cb + 1);
+      cb = (ob >= 0) ? ob : blk;
+      true_max = false;
+      load_block(cb);
+      continue;
+    }
+    if (synced) break;
+
+    // ---- wait: a non-merger for the merger's biases
+    if (!merger) {
+      if (wave == 0) {
+        int it = 0, ok = 0;
+        for (;;) {
+          if (ld_agent(bflag) == tok) {
+            ok = (ld_agent(bclean) == tok) ? 1 : 2;
             break;
           }
-          __builtin_amdgcn_s_sleep(8);
+          if (++it > p.spin_cap) break;
+          __builtin_amdgcn_s_sleep(2);
         }
-        if (lane == 0) s_misc[1] = give_up ? 1 : 0;
+        if (lane == 0) s_misc[1] = ok;
       }
       __syncthreads();
-      late = s_misc[1] != 0;
-      if (!late) break;
-      if (tid == 0 && p.tables) st_agent(p.sync + kSyncIncomplete + seg, tok);
-    }
-    int next = -1;
-    while (scan < nb) {
-      const int cand = scan++;
-      if (cand == blk) continue;
-      if (tid == 0) s_misc[2] = (ld_agent(flags + cand) == tok) ? 1 : 0;
-      __syncthreads();
-      const int done = s_misc[2];
-      __syncthreads();
-      if (!done) {
-        next = cand;
+      got = s_misc[1];
+      if (got) {
+        late = got == 2;
+        if (tid < p.Rp) bias_s[tid] = ld_agent(bias_seg + tid);
+        __syncthreads();
+        synced = true;
         break;
       }
+      late = true;  // merging on its own: the histogram is not ours to add to
     }
-    if (next < 0) {
-      issue_block(Kh, key0, rowstride, kb0, kb1, L, wave, lane);
-      wait_vm<0>();
-      __syncthreads();
-      break;
+    // ---- wait for every block's flag; past the bound, compute the blocks
+    // that have not published here
+    if (wave == 0) {
+      int it = 0, give_up = 0;
+      for (;;) {
+        bool all = true;
+        for (int b0 = 0; b0 < nb; b0 += 64) {
+          const int bb = b0 + lane;
+          const bool okb = bb >= nb || ld_agent(flags + bb) == tok;
+          all = all && (__ballot(!okb) == 0ull);
+        }
+        if (all) break;
+        if (++it > p.spin_cap) {
+          give_up = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (lane == 0) s_misc[2] = give_up;
     }
-    ob = next;
+    __syncthreads();
+    synced = true;
+    if (s_misc[2] == 0) break;
+    late = true;
+    const int ob = next_missing(0);
+    if (ob < 0) break;  // every block published after all
+    missing = true;
+    cb = ob;
+    true_max = false;
+    load_block(cb);
   }
 
-  // ---- merge: per row, log2 of the sum over the segment's blocks, minus
-  // log2 of the row's weight.  The blocks' results are read with
-  // device-scope loads (coherent across the chip's L2s), two rows per 8-byte
-  // load; tpr threads share a row pair, each taking every tpr-th block: the
-  // largest value, then the sum of 2^(value - largest), in block order;
-  // then the threads' partial results in thread order (a fixed order, so
-  // every block of the segment gets the same bits).
-  {
+  if (got == 0) {
+    // ---- merge: per row, log2 of the sum over the segment's blocks (the
+    // largest value, then the sum of 2^(value - largest), in block order per
+    // thread; the threads' partial results in thread order), minus log2 of
+    // the row's weight.  Two rows per 8-byte device-scope load.
     const int npair = p.Rp >> 1;
     const int tpr = NT / npair;  // >= 4
     const int q = tid / tpr;
@@ -526,10 +618,12 @@ __global__ __launch_bounds__(NT) void resident_kernel(ResidentParams p, SegTable
     float m0 = -INFINITY, s0 = 0.0f, m1 = -INFINITY, s1 = 0.0f;
     if (q < npair) {
       const uint64_t *src = reinterpret_cast<const uint64_t *>(lse_seg) + q;
-      for (int b0 = sub; b0 < nb; b0 += 16 * tpr) {
-        float v0[16], v1[16];
+      constexpr int MB = 16;  // loads in flight per thread
+#pragma unroll 1
+      for (int b0 = sub; b0 < nb; b0 += MB * tpr) {
+        float v0[MB], v1[MB];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+        for (int u = 0; u < MB; ++u) {
           const int bb = b0 + u * tpr;
           const uint64_t w = (bb < nb) ? ld_agent(src + (int64_t)bb * npair) : 0xff800000ff800000ull;  // -inf, -inf
           v0[u] = __uint_as_float((uint32_t)w);
@@ -537,18 +631,18 @@ __global__ __launch_bounds__(NT) void resident_kernel(ResidentParams p, SegTable
         }
         float a0 = v0[0], a1 = v1[0];
 #pragma unroll
-        for (int u = 1; u < 16; ++u) {
+        for (int u = 1; u < MB; ++u) {
           a0 = fmaxf(a0, v0[u]);
           a1 = fmaxf(a1, v1[u]);
         }
         float t0 = 0.0f, t1 = 0.0f;
         if (a0 > -INFINITY) {
 #pragma unroll
-          for (int u = 0; u < 16; ++u) t0 += fast_exp2(v0[u] - a0);
+          for (int u = 0; u < MB; ++u) t0 += fast_exp2(v0[u] - a0);
         }
         if (a1 > -INFINITY) {
 #pragma unroll
-          for (int u = 0; u < 16; ++u) t1 += fast_exp2(v1[u] - a1);
+          for (int u = 0; u < MB; ++u) t1 += fast_exp2(v1[u] - a1);
         }
         lse_merge(m0, s0, a0, t0);
         lse_merge(m1, s1, a1, t1);
@@ -582,72 +676,66 @@ __global__ __launch_bounds__(NT) void resident_kernel(ResidentParams p, SegTable
       }
     }
     __syncthreads();
-  }
-
-  // ---- pass 2 over the resident keys (and the halo tile when pooling)
-  {
-    float bia[16];
-    int lim2[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = rt * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-      bia[i] = active ? bias_s[row] : INFINITY;
-      lim2[i] = row_limit(row, p, L);
+    if (merger) {
+      if (tid < p.Rp) st_agent(bias_seg + tid, bias_s[tid]);
+      wait_vm<0>();
+      __syncthreads();
+      if (tid == 0) {
+        if (!missing) st_agent(bclean, tok);
+        wait_vm<0>();
+        st_agent(bflag, tok);
+      }
     }
-    const int nbt = (n + KT - 1) / KT;  // block tiles in use
-    const bool halo_on = p.pool_r > 0 && p.tables;
-    // leading tiles that every row sees in full, as pairs: no masks
-    const int nfp = max(0, min((min(kb1 - 1, minlim) - kb0 + 1) / KT, nbt)) >> 1;
-    if (active) {
-      for (int st = 0; st < nfp; ++st) {
+  }
+  if (tid == 0 && p.tables && late) st_agent(p.sync + kSyncFlags + seg, tok);  // the histogram is incomplete
+
+  // ---- pass 2: S per key from the stored e; the halo tile's logits afresh
+  // (its keys are still in LDS; the query fragments are loaded again, which
+  // kept them out of registers while e was held)
+  if (active) {
+    // the halo's loads first, so that they land while the block's sums run
+    const int hpos = (lr < HALO) ? kb0 - HALO + lr : kb1 + lr - HALO;
+    const int hthr = vis_thr(hpos, L, minlim, Lw, p.G, rbase);
+    float href[16];  // reference logits of the block that holds the halo key
+    if (want_halo) {
+      load_q(qf);
+      const int ob = (lr < HALO) ? blk - 1 : blk + 1;  // the block that holds hpos, if hpos is in the sequence
+      const float *oref = ref_seg + (int64_t)min(max(ob, 0), nb - 1) * p.Rp + rt * 32;
 #pragma unroll
-        for (int u = 0; u < 2 / KG; ++u) {
-          const int tt = 2 * st + ((KG == 2) ? kg : u);
-          bf16x8 kf[8];
-          read_tile(kf, pair_at(st) + (tt & 1) * TILE_BYTES, lr, hf);
-          f32x16 acc = {};
+      for (int i = 0; i < 16; ++i) href[i] = (hthr == INT_MAX) ? 0.0f : ld_agent(oref + out_row(i, hf));
+    }
+    float f[16];  // 2^(ref - bias): e times f is the row's weighted probability
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[j], kf[j], acc, 0, 0, 0);
-          // acc[i]: row rt * 32 + 8 (i / 4) + 4 hf + i % 4, key tt * 32 + lr.
-          float e[16];
+    for (int i = 0; i < 16; ++i) f[i] = fast_exp2(ref[i] - bias_s[rt * 32 + out_row(i, hf)]);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) e[i] = fast_exp2(fmaf(acc[i], cl2, -bia[i]));
-          const float a = ((e[0] + e[8]) + (e[4] + e[12])) + ((e[1] + e[9]) + (e[5] + e[13]));
-          const float c = ((e[2] + e[10]) + (e[6] + e[14])) + ((e[3] + e[11]) + (e[7] + e[15]));
-          const float sk = sum_halves(a + c);
-          if (hf == 0) red[rt * SIDX + tt * KT + lr] = sk;
-        }
+    for (int tt = 0; tt < NTILE; ++tt) {
+      float s = e[tt][0] * f[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) s = fmaf(e[tt][i], f[i], s);
+      s = sum_halves(s);
+      if (hf == 0) red[rt * SIDX + tt * KT + lr] = s;
+    }
+    if (want_halo) {
+      // The halo keys' S exactly as the blocks they belong to compute it:
+      // with that block's reference logits (published with its sums), the
+      // same masking, products and order of summation.
+      const f32x16 acc = logits(qf, g_halo, lr, hf);
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float ev = (row_off(i) >= hthr) ? fast_exp2(fmaf(acc[i], cl2, -href[i])) : 0.0f;
+        const float fv = fast_exp2(href[i] - bias_s[rt * 32 + out_row(i, hf)]);
+        s = (i == 0) ? ev * fv : fmaf(ev, fv, s);
       }
-      // the remaining block tiles, then the halo tile (key group 0), with masks
-      const int nend = nbt + (halo_on ? 1 : 0);
-      for (int tt0 = 2 * nfp; tt0 < nend; ++tt0) {
-        const bool halo = tt0 >= nbt;
-        if (KG == 2 && (halo ? 0 : (tt0 & 1)) != kg) continue;
-        bf16x8 kf[8];
-        read_tile(kf, tile_at(halo ? NTILE : tt0), lr, hf);
-        f32x16 acc = {};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[j], kf[j], acc, 0, 0, 0);
-        const int pos = halo ? ((lr < HALO) ? kb0 - HALO + lr : kb1 + lr - HALO) : kb0 + tt0 * KT + lr;
-        float e[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float v = fast_exp2(fmaf(acc[i], cl2, -bia[i]));
-          e[i] = (pos > lim2[i]) ? 0.0f : v;
-        }
-        const float a = ((e[0] + e[8]) + (e[4] + e[12])) + ((e[1] + e[9]) + (e[5] + e[13]));
-        const float c = ((e[2] + e[10]) + (e[6] + e[14])) + ((e[3] + e[11]) + (e[7] + e[15]));
-        const float sk = sum_halves(a + c);
-        if (hf == 0) red[rt * SIDX + (halo ? BLK : tt0 * KT) + lr] = sk;
-      }
+      s = sum_halves(s);
+      if (hf == 0) red[rt * SIDX + BLK + lr] = s;
     }
   }
   __syncthreads();
 
-  // ---- S by position (the sum over the waves' rows in wave order)
+  // ---- S by position (the sum over the row tiles in order)
   const bool is_max = p.pool == 2;
   const float fill = is_max ? -INFINITY : 0.0f;  // the pool's value outside the sequence
-  const int nwr = nrt;                            // row tiles with partial sums
   const int64_t segbase = (int64_t)p.Hkv * key0 + (int64_t)h * L;
   {
     const int nx = (p.pool_r > 0 && p.tables) ? SIDX : BLK;
@@ -662,7 +750,7 @@ __global__ __launch_bounds__(NT) void resident_kernel(ResidentParams p, SegTable
         pos = kb1 + (x - BLK - HALO);
       }
       float v = 0.0f;
-      for (int w2 = 0; w2 < nwr; ++w2) v += red[w2 * SIDX + x];
+      for (int r2 = 0; r2 < nrt; ++r2) v += red[r2 * SIDX + x];
       if (x < BLK && p.scores) p.scores[segbase + pos] = v;
       if (pos < 0 || pos >= L) v = fill;
       sbuf[HALO + pos - kb0] = v;
@@ -692,8 +780,10 @@ __global__ __launch_bounds__(NT) void resident_kernel(ResidentParams p, SegTable
   }
 
   // ---- counting sort of the block by first digit; the segment histogram
-  uint32_t *hist = reinterpret_cast<uint32_t *>(red);
-  reinterpret_cast<uint4 *>(hist)[tid] = make_uint4(0u, 0u, 0u, 0u);
+  // (the key tiles are no longer needed: the histogram lives in their LDS)
+  uint32_t *hist = reinterpret_cast<uint32_t *>(g_pair0);
+  reinterpret_cast<uint4 *>(hist)[2 * tid] = make_uint4(0u, 0u, 0u, 0u);
+  reinterpret_cast<uint4 *>(hist)[2 * tid + 1] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
   uint32_t key = 0u, dg = 0u, rank = 0u;
   if (x < n) {
@@ -703,20 +793,34 @@ __global__ __launch_bounds__(NT) void resident_kernel(ResidentParams p, SegTable
     rank = atomicAdd(&hist[dg], 1u);
   }
   __syncthreads();
-  const uint4 c4 = reinterpret_cast<const uint4 *>(hist)[tid];
-  int total;
-  const int ex = block_exscan512((int)(c4.x + c4.y + c4.z + c4.w), tmp, total);  // its barriers end the reads above
-  const uint32_t p0 = (uint32_t)ex, p1 = p0 + c4.x, p2 = p1 + c4.y, p3 = p2 + c4.z;
-  const int64_t tabi = (int64_t)seg * p.nblk_max + blk;
-  reinterpret_cast<uint2 *>(p.tab + tabi * NBIN)[tid] = make_uint2(p0 | (p1 << 16), p2 | (p3 << 16));
-  if (!late) {  // a block that stopped waiting has marked the histogram incomplete instead
-    uint32_t *sh = hist_seg + 4 * tid;
-    if (c4.x) atomicAdd(sh, c4.x);
-    if (c4.y) atomicAdd(sh + 1, c4.y);
-    if (c4.z) atomicAdd(sh + 2, c4.z);
-    if (c4.w) atomicAdd(sh + 3, c4.w);
+  uint32_t cnt[8], pre[8];
+  {
+    const uint4 a0 = reinterpret_cast<const uint4 *>(hist)[2 * tid];
+    const uint4 a1 = reinterpret_cast<const uint4 *>(hist)[2 * tid + 1];
+    cnt[0] = a0.x; cnt[1] = a0.y; cnt[2] = a0.z; cnt[3] = a0.w;
+    cnt[4] = a1.x; cnt[5] = a1.y; cnt[6] = a1.z; cnt[7] = a1.w;
   }
-  reinterpret_cast<uint4 *>(hist)[tid] = make_uint4(p0, p1, p2, p3);
+  int own = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) own += (int)cnt[u];
+  int total;
+  uint32_t run = (uint32_t)block_exscan(own, tmp, total);  // its barriers end the reads above
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    pre[u] = run;
+    run += cnt[u];
+  }
+  const int64_t tabi = (int64_t)seg * p.nblk_max + blk;
+  reinterpret_cast<uint4 *>(p.tab + tabi * NBIN)[tid] =
+      make_uint4(pre[0] | (pre[1] << 16), pre[2] | (pre[3] << 16), pre[4] | (pre[5] << 16), pre[6] | (pre[7] << 16));
+  if (!late) {  // a block that did not see every block publish marked the histogram incomplete instead
+    uint32_t *sh = hist_seg + 8 * tid;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (cnt[u]) atomicAdd(sh + u, cnt[u]);
+  }
+  reinterpret_cast<uint4 *>(hist)[2 * tid] = make_uint4(pre[0], pre[1], pre[2], pre[3]);
+  reinterpret_cast<uint4 *>(hist)[2 * tid + 1] = make_uint4(pre[4], pre[5], pre[6], pre[7]);
   __syncthreads();
   if (x < n) p.bucket[tabi * BLK + hist[dg] + rank] = key;
 }
@@ -736,10 +840,7 @@ hipError_t launch_resident_bump(uint64_t *sync, hipStream_t s) {
 
 hipError_t launch_resident(const ResidentParams &p, const SegTable &t, int items, hipStream_t s) {
   if (items < 1) return hipSuccess;
-  if (p.Rp > 128)
-    hipLaunchKernelGGL(resident_kernel<1>, dim3(items), dim3(NT), 0, s, p, t);
-  else
-    hipLaunchKernelGGL(resident_kernel<2>, dim3(items), dim3(NT), 0, s, p, t);
+  hipLaunchKernelGGL(resident_kernel, dim3(items), dim3(NT), 0, s, p, t);
   return hipGetLastError();
 }
 

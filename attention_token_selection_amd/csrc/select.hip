@@ -578,7 +578,11 @@ __global__ __launch_bounds__(NT) void select_chunk_kernel(SelectParams p, SegTab
 constexpr int RBP = kResBlock;
 constexpr int CPB = CH / RBP;            // blocks per chunk
 constexpr int NB2 = kResBins;
-static_assert(CPB == 4 && NB2 == 8 * NT, "four blocks per chunk; eight bins per thread");
+constexpr int BPT = 16;                  // blocks per thread in the per-block scans
+constexpr int MAXB = BPT * NT;           // blocks per segment: 4096, so up to 2^20 positions
+static_assert(CPB == 8 && BPT == 2 * CPB, "a chunk's blocks are one half of a thread's share");
+static_assert(NB2 == 8 * NT, "eight bins per thread");
+static_assert((int64_t)MAXB * RBP >= (int64_t)MAXCH * CH, "every supported sequence fits the per-block scans");
 
 template <bool GATHER>
 __global__ __launch_bounds__(NT) void select_block_kernel(SelectParams p, SegTable t) {
@@ -689,18 +693,20 @@ __global__ __launch_bounds__(NT) void select_block_kernel(SelectParams p, SegTab
     }
     __syncthreads();
     {
-      int a[8], s = 0;
+      // exclusive prefix over the blocks: thread tid owns blocks
+      // [BPT tid, BPT tid + BPT)
+      int a[BPT], s = 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = 8 * tid + u;
+      for (int u = 0; u < BPT; ++u) {
+        const int j = BPT * tid + u;
         a[u] = (j < nb) ? b_cb[j] : 0;
         s += a[u];
       }
       int tot;
       int ex = block_exscan(s, tmp, tot);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = 8 * tid + u;
+      for (int u = 0; u < BPT; ++u) {
+        const int j = BPT * tid + u;
         if (j < nb) b_cb[j] = ex;
         ex += a[u];
       }
@@ -799,34 +805,37 @@ __global__ __launch_bounds__(NT) void select_block_kernel(SelectParams p, SegTab
     });
     __syncthreads();
     {
-      int e[8], es = 0;
+      int e[BPT], es = 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = 8 * tid + u;
+      for (int u = 0; u < BPT; ++u) {
+        const int j = BPT * tid + u;
         e[u] = (j < nb) ? b_eq[j] : 0;
         es += e[u];
       }
       int tot;
       int eb = block_exscan(es, tmp, tot);  // equal keys in earlier blocks
-      int tk[8], sk[8], ss = 0;
+      int tk[BPT], sk[BPT], ss = 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = 8 * tid + u;
+      for (int u = 0; u < BPT; ++u) {
+        const int j = BPT * tid + u;
         tk[u] = min(e[u], max(0, take_eq - eb));
         eb += e[u];
         sk[u] = (j < nb) ? b_above[j] + b_gt[j] + tk[u] : 0;
         ss += sk[u];
       }
       int sb = block_exscan(ss, tmp, tot);
-      // The chunk's blocks CPB c .. CPB c + CPB - 1 sit in one thread's eight.
+      // The chunk's blocks CPB c .. CPB c + CPB - 1 are one half of thread
+      // c / 2's share: its first half for even c, its second for odd c.
+      if (tid == (c >> 1)) {
+        const int h0 = (c & 1) * CPB;
+        int tm = 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = 8 * tid + u;
-        if (j == CPB * c) {
-          sh[2] = sb;
-          sh[3] = tk[u] + ((u + 1 < 8) ? tk[u + 1] : 0) + ((u + 2 < 8) ? tk[u + 2] : 0) + ((u + 3 < 8) ? tk[u + 3] : 0);
+        for (int u = 0; u < BPT; ++u) {
+          sb += (u < h0) ? sk[u] : 0;
+          tm += (u >= h0 && u < h0 + CPB) ? tk[u] : 0;
         }
-        sb += sk[u];
+        sh[2] = sb;
+        sh[3] = tm;
       }
       __syncthreads();
     }
