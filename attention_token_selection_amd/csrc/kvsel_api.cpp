@@ -47,31 +47,23 @@ struct Plan {
   int64_t Lmax = 0;
   int kb1 = 0, kb2 = 0, nblk1_max = 0, nblk2_max = 0;
   int nchunk_max = 0;
-  size_t off_partials = 0, off_bias = 0, off_scores = 0, off_pooled = 0, ws_bytes = 0;
+  size_t off_partials = 0, off_scores = 0, off_pooled = 0, ws_bytes = 0;
   size_t off_tfine = 0, off_tcoarse = 0, off_bucket = 0;
-  // Resident scoring (kvsel_compress when the problem fits it): per block of
-  // kResBlock keys the row statistics, the first-digit tables, and the
-  // per-segment histograms and wait counters cleared before each launch.
-  bool res = false;
-  int res_Rp = 0, res_nblk = 0, res_nsegl = 0, spin_cap = kResSpinCap;
-  int64_t res_sync_words = 0;
-  size_t off_rsync = 0, off_rhist = 0, off_rlse = 0, off_rref = 0, off_rbias = 0, off_rtab = 0, off_rbucket = 0;
+  // kvsel_compress with the pool and the selection's first steps fused into
+  // pass 2 (pools up to 33 wide): pass 2's key blocks in whole table blocks
+  // of kTabBlock positions, the tables and the per-segment histograms.
+  bool fused = false;
+  int kb2t = 0, ntab_max = 0;
+  size_t off_thist = 0, off_ttab = 0, off_tbucket = 0;
 };
 
-// Test hooks read from the environment: KVSEL_FORCE_TWO_PASS=1 sends
-// kvsel_compress down the two-launch scoring path; KVSEL_SPIN_CAP=n bounds
-// the resident scoring's wait for the other blocks of a segment at n polls
-// (0: compute whatever has not been published instead of waiting).
-bool env_force_two_pass() {
-  const char *e = std::getenv("KVSEL_FORCE_TWO_PASS");
+// Test hook read from the environment: KVSEL_UNFUSED=1 sends kvsel_compress
+// through pass 2 without tables, then the separate pool and selection
+// launches (the path of pools wider than 33), so that tests can compare the
+// two.
+bool env_unfused() {
+  const char *e = std::getenv("KVSEL_UNFUSED");
   return e && e[0] == '1';
-}
-
-int env_spin_cap() {
-  const char *e = std::getenv("KVSEL_SPIN_CAP");
-  if (!e || !e[0]) return kResSpinCap;
-  const long v = std::strtol(e, nullptr, 10);
-  return (int)std::max(0L, std::min(v, 1L << 24));
 }
 
 int auto_key_block(int64_t head_keys, int64_t cap) {
@@ -119,7 +111,6 @@ kvsel_status plan_streaming(const kvsel_problem *p, Plan &P) {
   };
   P.off_partials = take(nseg * P.nblk1_c * P.Rpad * sizeof(float2));
   P.off_run = take(nseg * P.Rpad * sizeof(float2));
-  P.off_bias = take(nseg * P.Rpad * sizeof(float));
   P.off_sbuf = take(nseg * ((size_t)P.stream + 2 * P.halo) * sizeof(float));
   P.off_cand[0] = take(nseg * P.lv * sizeof(float));
   P.off_cand[1] = take(nseg * P.lv * sizeof(float));
@@ -251,8 +242,6 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   size_t off = 0;
   P.off_partials = off;
   off = align_up(off + nseg * P.nblk1_max * P.Rpad * sizeof(float2), 256);
-  P.off_bias = off;
-  off = align_up(off + nseg * P.Rpad * sizeof(float), 256);
   P.off_scores = off;
   off = align_up(off + (size_t)head_keys * sizeof(float), 256);
   P.off_pooled = off;
@@ -267,31 +256,19 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   off = align_up(off + nchunks * kSelectChunk * sizeof(uint32_t), 256);
   P.off_qmean = off;
   if (P.gqa == KVSEL_GQA_MEAN_QUERY) off = align_up(off + (size_t)P.B * P.wp * P.Hkv * p->d * sizeof(uint16_t), 256);
-  // The resident scoring: up to 128 rows, pools up to 33 wide, and blocks of
-  // 256 keys within the caller's key_chunk.
+  // The fused pass 2 of kvsel_compress: pools up to 2 kPoolHalo + 1 wide;
+  // its blocks are pass 2's, rounded up to whole table blocks.
   const int pool_r = (P.pool == KVSEL_POOL_NONE) ? 0 : (P.pool_kernel - 1) / 2;
-  P.res = P.R <= kResMaxRows && pool_r <= kResHalo && (p->key_chunk == 0 || p->key_chunk >= kResBlock) &&
-          !env_force_two_pass();
-  if (P.res) {
-    P.spin_cap = env_spin_cap();
-    P.res_Rp = 32 * ((P.R + 31) / 32);
-    P.res_nblk = (int)((P.Lmax + kResBlock - 1) / kResBlock);
-    P.res_nsegl = (int)std::min<size_t>(kMaxSeg, nseg);
-    P.res_sync_words = kSyncFlags + 3 * (int64_t)nseg + (int64_t)P.res_nsegl * P.res_nblk;
-    P.off_rsync = off;
-    off = align_up(off + (size_t)P.res_sync_words * sizeof(uint64_t), 256);
-    P.off_rhist = off;
-    off = align_up(off + nseg * kResBins * sizeof(uint32_t), 256);
-    P.off_rlse = off;
-    off = align_up(off + nseg * P.res_nblk * P.res_Rp * sizeof(float), 256);
-    P.off_rref = off;
-    off = align_up(off + nseg * P.res_nblk * P.res_Rp * sizeof(float), 256);
-    P.off_rbias = off;
-    off = align_up(off + nseg * P.res_Rp * sizeof(float), 256);
-    P.off_rtab = off;
-    off = align_up(off + nseg * P.res_nblk * kResBins * sizeof(uint16_t), 256);
-    P.off_rbucket = off;
-    off = align_up(off + nseg * P.res_nblk * kResBlock * sizeof(uint32_t), 256);
+  P.fused = pool_r <= kPoolHalo && !env_unfused();
+  if (P.fused) {
+    P.kb2t = (P.kb2 + kTabBlock - 1) / kTabBlock * kTabBlock;
+    P.ntab_max = (int)((P.Lmax + kTabBlock - 1) / kTabBlock);
+    P.off_thist = off;
+    off = align_up(off + nseg * kTabHistCopies * kTabBins * sizeof(uint32_t), 256);
+    P.off_ttab = off;
+    off = align_up(off + nseg * P.ntab_max * kTabBins * sizeof(uint16_t), 256);
+    P.off_tbucket = off;
+    off = align_up(off + nseg * P.ntab_max * kTabBlock * sizeof(uint32_t), 256);
   }
   P.ws_bytes = off;
   return KVSEL_OK;
@@ -368,7 +345,6 @@ ScoreParams score_params(const Plan &P, const void *Q, const void *K, float *sco
   sp.K = static_cast<const uint16_t *>(K);
   sp.scores = scores;
   sp.partials = reinterpret_cast<float2 *>(ws + P.off_partials);
-  sp.bias = reinterpret_cast<float *>(ws + P.off_bias);
   sp.Hq = P.Hq;
   sp.Hkv = P.Hkv;
   sp.G = P.G;
@@ -385,6 +361,7 @@ ScoreParams score_params(const Plan &P, const void *Q, const void *K, float *sco
   sp.lam2 = P.lam2;
   sp.log2norm = P.log2norm;
   sp.nblk1_max = P.nblk1_max;
+  sp.stat_block = P.kb1;
   sp.key_begin = 0;
   sp.key_end = INT_MAX;
   sp.out_stride = 0;
@@ -393,7 +370,9 @@ ScoreParams score_params(const Plan &P, const void *Q, const void *K, float *sco
 }
 
 // Pass 1: per-block row statistics into the workspace.
-kvsel_status run_row_stats(const Plan &P, const void *Q, const void *K, char *ws, hipStream_t st) {
+// seg_hist (kvsel_compress's fused pass 2): the histograms pass 1 clears.
+kvsel_status run_row_stats(const Plan &P, const void *Q, const void *K, char *ws, hipStream_t st,
+                           uint32_t *seg_hist = nullptr) {
   if (P.gqa == KVSEL_GQA_MEAN_QUERY) {
     QueryMeanParams qp;
     qp.Q = static_cast<const uint4 *>(Q);
@@ -406,6 +385,7 @@ kvsel_status run_row_stats(const Plan &P, const void *Q, const void *K, char *ws
     if (e != hipSuccess) return hip_fail(e, "query mean launch");
   }
   ScoreParams sp = score_params(P, Q, K, nullptr, ws);
+  sp.seg_hist = seg_hist;
   return for_each_group(P, [&](const SegTable &t, int64_t lmax) {
     sp.key_block = P.kb1;
     hipError_t e = launch_score_pass1(sp, t, (int)((lmax + P.kb1 - 1) / P.kb1), st);
@@ -414,15 +394,12 @@ kvsel_status run_row_stats(const Plan &P, const void *Q, const void *K, char *ws
   });
 }
 
-// Merge of the block statistics into per-row biases, then pass 2.
+// Pass 2 (which starts by merging the block statistics into per-row biases).
 kvsel_status run_from_stats(const Plan &P, const void *Q, const void *K, float *scores, char *ws, hipStream_t st) {
   ScoreParams sp = score_params(P, Q, K, scores, ws);
   return for_each_group(P, [&](const SegTable &t, int64_t lmax) {
-    sp.key_block = P.kb1;
-    hipError_t e = launch_score_merge(sp, t, st);
-    if (e != hipSuccess) return hip_fail(e, "row statistics merge launch");
     sp.key_block = P.kb2;
-    e = launch_score_pass2(sp, t, (int)((lmax + P.kb2 - 1) / P.kb2), st);
+    hipError_t e = launch_score_pass2(sp, t, (int)((lmax + P.kb2 - 1) / P.kb2), st);
     if (e != hipSuccess) return hip_fail(e, "score pass 2 launch");
     return KVSEL_OK;
   });
@@ -479,128 +456,56 @@ kvsel_status run_gather(const Plan &P, const int32_t *idx, const void *K, const 
 
 bool any_kept(const Plan &P) { return P.out_off.back() > 0; }
 
-kvsel_status run_query_mean(const Plan &P, const void *Q, char *ws, hipStream_t st) {
-  if (P.gqa != KVSEL_GQA_MEAN_QUERY) return KVSEL_OK;
-  QueryMeanParams qp;
-  qp.Q = static_cast<const uint4 *>(Q);
-  qp.Qm = reinterpret_cast<uint4 *>(ws + P.off_qmean);
-  qp.Hq = P.Hq_in;
-  qp.Hkv = P.Hkv;
-  qp.G = P.G_in;
-  qp.items = P.B * P.wp * P.Hkv;
-  hipError_t e = launch_query_mean(qp, st);
-  if (e != hipSuccess) return hip_fail(e, "query mean launch");
-  return KVSEL_OK;
-}
 
-ResidentParams resident_params(const Plan &P, const void *Q, const void *K, float *scores, float *pooled, char *ws) {
-  ResidentParams rp;
-  std::memset(&rp, 0, sizeof(rp));
-  rp.Q = (P.gqa == KVSEL_GQA_MEAN_QUERY) ? reinterpret_cast<const uint16_t *>(ws + P.off_qmean)
-                                          : static_cast<const uint16_t *>(Q);
-  rp.K = static_cast<const uint16_t *>(K);
-  rp.scores = scores;
-  rp.pooled = pooled;
-  rp.tab = reinterpret_cast<uint16_t *>(ws + P.off_rtab);
-  rp.bucket = reinterpret_cast<uint32_t *>(ws + P.off_rbucket);
-  rp.seg_hist = reinterpret_cast<uint32_t *>(ws + P.off_rhist);
-  rp.lse = reinterpret_cast<float *>(ws + P.off_rlse);
-  rp.biasg = reinterpret_cast<float *>(ws + P.off_rbias);
-  rp.refg = reinterpret_cast<float *>(ws + P.off_rref);
-  rp.sync = reinterpret_cast<uint64_t *>(ws + P.off_rsync);
-  rp.nseg = P.B * P.Hkv;
-  rp.Hq = P.Hq;
-  rp.Hkv = P.Hkv;
-  rp.G = P.G;
-  rp.w = P.w;
-  rp.wp = P.wp;
-  rp.R = P.R;
-  rp.Rp = P.res_Rp;
-  rp.has_decode = P.has_decode;
-  rp.causal = P.causal;
-  rp.cl2 = P.cl2;
-  rp.alpha = P.alpha;
-  rp.weighting = P.weighting;
-  rp.lam2 = P.lam2;
-  rp.log2norm = P.log2norm;
+kvsel_status run_compress_fused(const Plan &P, const void *Q, const void *K, const void *V, int32_t *idx, void *K_out,
+                                void *V_out, float *pooled, char *ws, hipStream_t st) {
+  uint32_t *seg_hist = reinterpret_cast<uint32_t *>(ws + P.off_thist);
+  kvsel_status s = run_row_stats(P, Q, K, ws, st, seg_hist);
+  if (s != KVSEL_OK) return s;
+  ScoreParams sp = score_params(P, Q, K, nullptr, ws);
+  sp.pooled = pooled;
+  sp.tab = reinterpret_cast<uint16_t *>(ws + P.off_ttab);
+  sp.bucket = reinterpret_cast<uint32_t *>(ws + P.off_tbucket);
+  sp.seg_hist = seg_hist;
+  sp.ntab_max = P.ntab_max;
+  sp.pool = P.pool;
+  sp.pool_r = (P.pool == KVSEL_POOL_NONE) ? 0 : (P.pool_kernel - 1) / 2;
+  sp.pool_width = (float)P.pool_kernel;
+  sp.sink = P.sink;
+  sp.recent = P.recent;
   {
     // sum of the row weights: 1 each, or 1 - alpha and alpha with a decode
     // row, or the exponential weights normalised to 1
     double cw = P.w;
     if (P.weighting == KVSEL_WEIGHT_EXP) cw = 1.0;
     else if (P.has_decode) cw = (1.0 - P.alpha) * P.w + P.alpha;
-    rp.wsum = (float)(P.G * cw);
+    sp.wsum = (float)(P.G * cw);
   }
-  rp.pool = P.pool;
-  rp.pool_r = (P.pool == KVSEL_POOL_NONE) ? 0 : (P.pool_kernel - 1) / 2;
-  rp.pool_width = (float)P.pool_kernel;
-  rp.sink = P.sink;
-  rp.recent = P.recent;
-  rp.nblk_max = P.res_nblk;
-  rp.spin_cap = P.spin_cap;
-  rp.tables = pooled ? 1 : 0;
-  return rp;
-}
 
-int64_t resident_items(const Plan &P, const SegTable &t) {
-  int64_t items = 0;
-  for (int i = 0; i < t.nseq; ++i) items += (int64_t)P.Hkv * ((t.key_off[i + 1] - t.key_off[i] + kResBlock - 1) / kResBlock);
-  return items;
-}
-
-// kvsel_score through the resident scoring (no pool, no tables), then the
-// next call's token.
-kvsel_status run_score_resident(const Plan &P, const void *Q, const void *K, float *scores, char *ws, hipStream_t st) {
-  kvsel_status s = run_query_mean(P, Q, ws, st);
-  if (s != KVSEL_OK) return s;
-  const ResidentParams rp = resident_params(P, Q, K, scores, nullptr, ws);
-  return for_each_group(P, [&](const SegTable &t, int64_t) {
-    const int64_t items = resident_items(P, t);
-    if (items > INT_MAX) return fail(KVSEL_EUNSUPPORTED, "too many key blocks in one launch");
-    hipError_t e = launch_resident(rp, t, (int)items, st);
-    if (e != hipSuccess) return hip_fail(e, "resident scoring launch");
-    e = launch_resident_bump(rp.sync, st);
-    if (e != hipSuccess) return hip_fail(e, "resident token launch");
-    return KVSEL_OK;
-  });
-}
-
-// kvsel_compress through the resident scoring: per group of sequences, the
-// fused scoring (both passes of TideKV §4.2, the pool and the first-digit
-// tables), then the selection and the gather, which also sets the next
-// call's token.
-kvsel_status run_compress_resident(const Plan &P, const void *Q, const void *K, const void *V, int32_t *idx,
-                                   void *K_out, void *V_out, float *pooled, char *ws, hipStream_t st) {
-  kvsel_status s = run_query_mean(P, Q, ws, st);
-  if (s != KVSEL_OK) return s;
-  const ResidentParams rp = resident_params(P, Q, K, nullptr, pooled, ws);
-
-  SelectParams sp;
-  std::memset(&sp, 0, sizeof(sp));
-  sp.pooled = pooled;
-  sp.idx = idx;
-  sp.tab_fine = rp.tab;
-  sp.bucket = rp.bucket;
-  sp.seg_hist = rp.seg_hist;
-  sp.sync = rp.sync;
-  sp.nblk_max = P.res_nblk;
-  sp.Hkv = P.Hkv;
-  sp.pool = P.pool;
-  sp.pool_kernel = P.pool_kernel;
-  sp.sink = P.sink;
-  sp.recent = P.recent;
+  SelectParams sel;
+  std::memset(&sel, 0, sizeof(sel));
+  sel.pooled = pooled;
+  sel.idx = idx;
+  sel.tab_fine = sp.tab;
+  sel.bucket = sp.bucket;
+  sel.seg_hist = sp.seg_hist;
+  sel.nblk_max = P.ntab_max;
+  sel.Hkv = P.Hkv;
+  sel.pool = P.pool;
+  sel.pool_kernel = P.pool_kernel;
+  sel.sink = P.sink;
+  sel.recent = P.recent;
   if (any_kept(P)) {
-    sp.K = static_cast<const uint4 *>(K);
-    sp.V = static_cast<const uint4 *>(V);
-    sp.K_out = static_cast<uint4 *>(K_out);
-    sp.V_out = static_cast<uint4 *>(V_out);
+    sel.K = static_cast<const uint4 *>(K);
+    sel.V = static_cast<const uint4 *>(V);
+    sel.K_out = static_cast<uint4 *>(K_out);
+    sel.V_out = static_cast<uint4 *>(V_out);
   }
-  return for_each_group(P, [&](const SegTable &t, int64_t) {
-    const int64_t items = resident_items(P, t);
-    if (items > INT_MAX) return fail(KVSEL_EUNSUPPORTED, "too many key blocks in one launch");
-    hipError_t e = launch_resident(rp, t, (int)items, st);
-    if (e != hipSuccess) return hip_fail(e, "resident scoring launch");
-    e = launch_select_blocks(sp, t, st);  // also when nothing is kept: it sets the next token
+  return for_each_group(P, [&](const SegTable &t, int64_t lmax) {
+    sp.key_block = P.kb2t;
+    hipError_t e = launch_score_pass2_tables(sp, t, (int)((lmax + P.kb2t - 1) / P.kb2t), st);
+    if (e != hipSuccess) return hip_fail(e, "score pass 2 launch");
+    e = launch_select_blocks(sel, t, st);
     if (e != hipSuccess) return hip_fail(e, "selection launch");
     return KVSEL_OK;
   });
@@ -649,19 +554,11 @@ kvsel_status run_compress_streaming(const Plan &P, const void *Q, const void *K,
     });
   }
   if (s != KVSEL_OK) return s;
-  // Biases from the running states: the merge over a single "block".
-  {
-    ScoreParams mp = sp;
-    mp.partials = run;
-    mp.nblk1_max = 1;
-    mp.key_block = 1 << 30;
-    s = for_each_group(P, [&](const SegTable &t, int64_t) {
-      hipError_t e = launch_score_merge(mp, t, st);
-      if (e != hipSuccess) return hip_fail(e, "row statistics merge launch");
-      return KVSEL_OK;
-    });
-    if (s != KVSEL_OK) return s;
-  }
+  // Pass 2 takes its biases from the running states: one block state per
+  // row and segment.
+  sp.partials = run;
+  sp.nblk1_max = 1;
+  sp.stat_block = 1 << 30;
   // Pass 2 and the running selection, step by step.
   StreamParams q;
   q.S = reinterpret_cast<const float *>(ws + P.off_sbuf);
@@ -795,7 +692,6 @@ KVSEL_API kvsel_status kvsel_score(const kvsel_problem *p, const void *Q, const 
   if (s == KVSEL_OK) s = check_ws(P, ws, ws_bytes);
   if (s == KVSEL_OK) s = check_device();
   if (s != KVSEL_OK) return s;
-  if (P.res) return run_score_resident(P, Q, K, scores, static_cast<char *>(ws), reinterpret_cast<hipStream_t>(stream));
   return run_score(P, Q, K, scores, static_cast<char *>(ws), reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -884,7 +780,7 @@ KVSEL_API kvsel_status kvsel_compress(const kvsel_problem *p, const void *Q, con
   if (P.stream > 0) return run_compress_streaming(P, Q, K, V, idx, K_out, V_out, wsb, st);
   float *scores = reinterpret_cast<float *>(wsb + P.off_scores);
   float *pool_buf = pooled ? pooled : reinterpret_cast<float *>(wsb + P.off_pooled);
-  if (P.res) return run_compress_resident(P, Q, K, V, idx, K_out, V_out, pool_buf, wsb, st);
+  if (P.fused) return run_compress_fused(P, Q, K, V, idx, K_out, V_out, pool_buf, wsb, st);
   s = run_score(P, Q, K, scores, wsb, st);
   if (s != KVSEL_OK) return s;
   if (any_kept(P)) return run_select(P, scores, pool_buf, idx, wsb, st, K, V, K_out, V_out);
@@ -928,7 +824,7 @@ KVSEL_API kvsel_status kvsel_profile_layer(const kvsel_problem *p, const void *Q
   char *wsb = static_cast<char *>(ws);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   float *scores = reinterpret_cast<float *>(wsb + P.off_scores);
-  s = P.res ? run_score_resident(P, Q, K, scores, wsb, st) : run_score(P, Q, K, scores, wsb, st);
+  s = run_score(P, Q, K, scores, wsb, st);
   if (s != KVSEL_OK) return s;
   ProfileParams pp;
   pp.scores = scores;

@@ -1,4 +1,4 @@
-// Device helpers shared by the selection kernels and the resident scoring.
+// Device helpers shared by the selection kernels and pass 2 with tables.
 // Included by HIP sources only.
 #pragma once
 

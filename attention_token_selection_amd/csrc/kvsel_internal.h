@@ -17,15 +17,16 @@ constexpr int kMaxPoolKernel = 255;  // widest pool supported
 constexpr int kSelectChunk = 2048;   // positions per pool / select workgroup
 constexpr int kSelectBins = 8192;    // bins of the first radix digit (top 13 bits of an order key)
 constexpr int kMaxChunks = 512;      // chunks per sequence, so L_b <= 2^20
-// Resident scoring (both passes of a key block in one workgroup, the block's
-// keys held in LDS between them).
-constexpr int kResThreads = 256;     // four waves
-constexpr int kResBlock = 256;       // keys per workgroup (= threads: one position each in the epilogue)
-constexpr int kResHalo = 16;         // keys scored on each side of a block for the pool (pool radius <= 16)
-constexpr int kResMaxRows = 128;     // observation rows per KV head (a row tile of 32 per wave)
-constexpr int kResBins = 2048;       // bins of the selection's first digit
-constexpr int kResDigitShift = 16;   // a bin spans 2^16 order-key steps (1/128 of a factor 2 in value)
-constexpr int kResSpinCap = 8192;    // polls of a block's wait for its segment before it computes what is missing
+// Selection tables built by pass 2 of kvsel_compress (pool and first-digit
+// counting sort fused into the scoring): per block of kTabBlock positions,
+// the exclusive prefix of the block's digit histogram and its order keys
+// grouped by digit, plus each segment's whole histogram.
+constexpr int kTabBlock = 256;       // positions per table block
+constexpr int kTabBins = 2048;       // bins of the first digit
+constexpr int kTabDigitShift = 16;   // a bin spans 2^16 order-key steps (1/128 of a factor 2 in value)
+constexpr int kPoolHalo = 16;        // keys scored past each end of a pass-2 block for the pool (radius <= 16)
+constexpr int kTabHistCopies = 8;    // copies of each segment's histogram (workgroup w adds to copy w mod 8, the
+                                     // compute die it runs on, so that no count is contended across dies)
 
 // Per-launch description of the sequences and segments a kernel works on.
 // Travels by value in the kernel arguments, so no device-side tables are
@@ -45,7 +46,6 @@ struct ScoreParams {
   const uint16_t *K;            // bf16 [sum L][Hkv][d]
   float *scores;                // pass 2 output (layout of the public ABI)
   float2 *partials;             // pass 1 per-block (ref, Z), [nseg][nblk1_max][Rpad]
-  float *bias;                  // pass 1 result per row, [nseg][Rpad]
   int Hq, Hkv, G, w, wp, R;
   int nrt;                      // row tiles of 32 rows
   int Rpad;                     // nrt * 32
@@ -57,9 +57,23 @@ struct ScoreParams {
   float log2norm;               // weighting 1: log2 of sum_r exp(lambda (r - r_max))
   int key_block;                // keys per workgroup in this pass (multiple of 32)
   int nblk1_max;                // pass 1 blocks per segment of the longest sequence
+  int stat_block;               // pass 2: keys per pass-1 block state it merges (ceil(L / stat_block) per segment)
   int key_begin, key_end;       // keys of each sequence this launch covers (0, INT_MAX: all)
   int64_t out_stride;           // pass 2 output: 0 = the public layout; else floats per segment
   int out_origin;               //   and the key stored first in each segment's window
+  // Pass 2 with selection tables (kvsel_compress): the pool of S over the
+  // block (and kPoolHalo keys past each end), the pooled output and the
+  // tables of each kTabBlock positions; `scores` may then be null.
+  float *pooled;                // public layout
+  uint16_t *tab;                // [nseg][ntab_max][kTabBins]: exclusive prefix of each block's digit histogram
+  uint32_t *bucket;             // [nseg][ntab_max][kTabBlock]: each block's order keys grouped by digit
+  uint32_t *seg_hist;           // [nseg][kTabHistCopies][kTabBins]: each segment's digit histogram, in
+                                //   copies that add up to it (cleared by pass 1)
+  int ntab_max;                 // table blocks of the longest sequence
+  int pool, pool_r;             // pool kind (0 none, 1 avg, 2 max); half width (<= kPoolHalo)
+  float pool_width;
+  int sink, recent;
+  float wsum;                   // sum of S over a segment's positions: G * sum_r c_r
 };
 
 // The mean query of every (sequence, observation row, KV head): the G query
@@ -71,54 +85,6 @@ struct QueryMeanParams {
   int items;       // B * w' * Hkv
 };
 
-// Words of the resident scoring's synchronisation area (64-bit):
-//   [0]                           T, the call token; the kernel that runs
-//                                 after the scoring sets it to T + 1 for
-//                                 the next call
-//   [1]                           the T the last scoring ran with
-//   [2 + seg]                     == T + 1: segment seg's histogram lacks the
-//                                 counts of blocks that stopped waiting
-//   [2 + nseg + seg]              == T + 1: segment seg's row biases are
-//                                 published
-//   [2 + 2 nseg + seg]            == T + 1: ... by a merger that saw every
-//                                 block publish
-//   [2 + 3 nseg + sl * nblk + b]  == T + 1: block b of local segment sl has
-//                                 published its row statistics
-// Flags from earlier calls hold other tokens, so nothing needs clearing.
-constexpr int kSyncFlags = 2;
-constexpr int kSyncIncomplete = kSyncFlags;
-
-// The fused scoring of kvsel_compress: per block of kResBlock keys of one
-// (sequence, KV head) segment, pass 1, the segment's statistics merge,
-// pass 2 over the same keys (still in LDS), the pool and the block's
-// first-digit counting sort.
-struct ResidentParams {
-  const uint16_t *Q;     // bf16 [B][w'][Hq][d] (mean queries [B][w'][Hkv][d] with G = 1)
-  const uint16_t *K;     // bf16 [sum L][Hkv][d]
-  float *scores;         // optional: S in the public layout (nullptr: not written)
-  float *pooled;         // pooled scores, public layout
-  uint16_t *tab;         // [nseg][nblk_max][kResBins]: exclusive prefix of each block's digit histogram
-  uint32_t *bucket;      // [nseg][nblk_max][kResBlock]: each block's order keys grouped by digit
-  uint32_t *seg_hist;    // [nseg][kResBins]: each segment's digit histogram (its blocks clear it)
-  float *lse;            // [nseg][nblk_max][Rp]: per block and row, log2 of the sum of 2^(s log2 e)
-  float *biasg;          // [nseg][Rp]: the row biases, published by each segment's first block
-  float *refg;           // [nseg][nblk][Rp]: each block's reference logit per row (its e = 2^(x - ref))
-  uint64_t *sync;        // call tokens and flags (res_sync below)
-  int nseg;              // segments of the whole problem (global indices)
-  int Hq, Hkv, G, w, wp, R, Rp;  // Rp: rows rounded up to 16
-  int has_decode, causal;
-  float cl2, alpha;
-  int weighting;
-  float lam2, log2norm;
-  float wsum;            // sum of S over a segment's positions: G * sum_r c_r
-  int pool, pool_r;      // pool kind; half width (<= kResHalo)
-  float pool_width;
-  int sink, recent;
-  int nblk_max;          // blocks of the longest sequence
-  int spin_cap;          // polls before a block stops waiting (0: never wait)
-  int tables;            // 1: pool, pooled output and selection tables; 0: scores only
-};
-
 struct SelectParams {
   const float *scores;
   float *pooled;
@@ -127,10 +93,9 @@ struct SelectParams {
   uint16_t *tab_coarse;  // [nseg][nchunk_max][kSelectBins / 32]: every 32nd entry of tab_fine
   uint32_t *bucket;      // [nseg][nchunk_max][kSelectChunk]: each chunk's order keys grouped by first digit
   int nchunk_max;        // chunks of kSelectChunk positions in the longest sequence
-  // Tables of the resident scoring (launch_select_blocks): tab_fine and
-  // bucket then hold ResidentParams::tab and ::bucket.
+  // Tables of the fused pass 2 (launch_select_blocks): tab_fine and bucket
+  // then hold ScoreParams::tab and ::bucket.
   const uint32_t *seg_hist;
-  uint64_t *sync;        // ResidentParams::sync
   int nblk_max;
   int Hkv;
   int pool;              // 0 none, 1 avg, 2 max
@@ -195,16 +160,16 @@ hipError_t launch_tier_fill(int8_t *tier, int64_t n, hipStream_t s);
 hipError_t launch_mass(const MassParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_tier_mark(const int32_t *idx, int8_t *tier, int label, const SegTable &t, hipStream_t s);
 hipError_t launch_score_pass1(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s);
-hipError_t launch_score_merge(const ScoreParams &p, const SegTable &t, hipStream_t s);  // key_block = pass 1's
 hipError_t launch_score_pass2(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s);
+// Pass 2 with the pool and the selection tables (p.pooled, p.tab, ...);
+// key_block a multiple of kTabBlock, pool radius <= kPoolHalo.
+hipError_t launch_score_pass2_tables(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s);
 hipError_t launch_stream_stats(const ScoreParams &p, const SegTable &t, float2 *run, int first, hipStream_t s);
 hipError_t launch_stream_init(const StreamParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_stream_pool(const StreamParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_stream_map(const StreamParams &p, const SegTable &vt, hipStream_t s);
 hipError_t launch_stream_final(const StreamParams &p, const SegTable &t, int32_t *idx, hipStream_t s);
 hipError_t launch_pool_topk(const SelectParams &p, const SegTable &t, hipStream_t s);
-hipError_t launch_resident_bump(uint64_t *sync, hipStream_t s);
-hipError_t launch_resident(const ResidentParams &p, const SegTable &t, int items, hipStream_t s);
 hipError_t launch_select_blocks(const SelectParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_gather(const GatherParams &p, const SegTable &t, hipStream_t s);
 

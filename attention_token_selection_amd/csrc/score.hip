@@ -25,14 +25,34 @@
 // moved when Z would leave a safe range (checked once per tile for the whole
 // wave), so the common path costs one FMA, one exp2 and one add per logit.
 // The two lanes of a row are merged with the log-sum-exp rule and each
-// block's per-row state is stored; a small merge launch then combines the
+// block's per-row state is stored; pass 2 starts by combining the
 // blocks, in a fixed order, into per row bias = r + log2(Z) - log2(c_r).
 //
 // Pass 2 puts the observation rows in M (A = Q, B = K), so each lane holds 16
 // rows of one key: it adds c_r * p = 2^(x - bias) over its rows in-lane, the
 // two lane halves are combined with one swap, the four waves in LDS, in a
 // fixed order (no floating-point atomics: results are bit-reproducible).
+//
+// For kvsel_compress, pass 2 goes on to the selection's first steps over its
+// block (TAB): it also scores the kPoolHalo keys past each end of the block
+// (one more tile; the same arithmetic in the same order as the block that
+// owns them, so the same bits), pools S over the block's positions (TideKV
+// §4.2 / DeferKV guide Phase 2 pooling), writes the pooled scores and, per
+// kTabBlock positions, counting-sorts the positions by a first digit of
+// their order key: the exclusive prefix of the digit histogram, the keys
+// grouped by digit, and the histogram added to the segment's.  The
+// selection launch finishes the top-k from these tables.
+//
+// The first digit.  A segment's scores sum to W = G * sum_r c_r, so they
+// centre near the mean W / L; the digit counts steps of 2^16 in the order
+// key (the fp32 bits, which grow like 2^23 log2 of the value) from the
+// mean's key, offset by 1024 and clamped to [0, 2047]: bins of 1/128 of a
+// factor 2, 8 factors of 2 either side of the mean.  It is a monotone
+// function of the key, so equal values share a bin and higher bins hold
+// larger keys, and it leaves a few hundred keys in the bin of the k-th
+// largest where a fixed slice of the key's top bits leaves thousands.
 #include "kvsel_internal.h"
+#include "kvsel_device.h"
 
 namespace kvsel {
 namespace {
@@ -50,7 +70,26 @@ static_assert(TILE_BYTES == 2 * 16 * NT, "each thread moves two 16-byte chunks p
 constexpr int PD = 4;                    // LDS ring slots; tiles in flight = PD - 1
 // s_waitcnt immediate for vmcnt(2 (PD - 2)) with the other counters left alone.
 constexpr int kWaitTile = 0x3F70 | (2 * (PD - 2));
-static_assert(PD == 4 && 2 * (PD - 2) < 16, "four named slots; vmcnt fits the low field");
+static_assert(PD >= 3 && PD <= 8 && 2 * (PD - 2) < 16, "at most eight named slots; vmcnt fits the low field");
+
+// The LDS ring: one array per slot, so that the compiler can tell a slot
+// being read from the slots that loads are landing in (ring(i) is only ever
+// called with an index known after unrolling).
+#define KVSEL_SLOT(n) __shared__ __attribute__((aligned(16))) char g_ring##n[TILE_BYTES];
+KVSEL_SLOT(0) KVSEL_SLOT(1) KVSEL_SLOT(2) KVSEL_SLOT(3) KVSEL_SLOT(4) KVSEL_SLOT(5) KVSEL_SLOT(6) KVSEL_SLOT(7)
+#undef KVSEL_SLOT
+__device__ __forceinline__ char *ring(int i) {
+  switch (i) {
+    case 0: return g_ring0;
+    case 1: return g_ring1;
+    case 2: return g_ring2;
+    case 3: return g_ring3;
+    case 4: return g_ring4;
+    case 5: return g_ring5;
+    case 6: return g_ring6;
+    default: return g_ring7;
+  }
+}
 constexpr float kZLimit = 0x1p100f;      // a lane's running sum stays below this
 
 __device__ inline bf16x8 as_frag(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -71,20 +110,55 @@ __device__ inline void lse_merge(float &r, float &z, float r2, float z2) {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-// Issues this wave's share of key tile i0 .. i0+31 (`kt` = its first key row
-// of this head) straight into the LDS slot: 16-byte position P = 128 * wave
-// + 64 * i + lane (i = 0, 1) of the slot receives chunk (P & 15) ^ (row & 15)
-// of key row = P >> 4, which leaves the slot in the swizzled layout.  Rows
-// past `rmax` (the block's last key minus i0) re-read that key, so every
-// load is in bounds; such keys are masked or never consumed.
-__device__ inline void issue_tile(char *slot, const uint16_t *kt, int rmax, int rowstride, int wave, int lane) {
+// Issues this wave's share of one key tile straight into an LDS slot:
+// 16-byte position P = 128 * wave + 64 * i + lane (i = 0, 1) of the slot
+// receives chunk (P & 15) ^ (row & 15) of tile row = P >> 4, which leaves
+// the slot in the swizzled layout.  kh points at key 0 of this sequence and
+// head.  Tile ti of the block [kb0, kb1) holds keys kb0 + 32 ti + row;
+// rows past the block re-read its last key, so every load is in bounds (such
+// keys are masked or never consumed).  The halo tile (hal) holds key kb1 +
+// row (row < HALO) or kb0 - 2 HALO + row, clamped into [0, L - 1] (a clamped
+// key's score is never used): each halo key thus sits in the half of the
+// tile it has in its own block's tile (key mod 32; block starts are
+// multiples of 32), so the split row tile's partial sums land in the same
+// waves and S comes out with the same bits.  The two layouts differ only
+// in the key index (a select, no branch: the compiler then still knows how
+// many loads each wait covers).
+__device__ inline void issue_keys(char *slot, const uint16_t *kh, bool hal, int ti, int kb0, int kb1, int L,
+                                  int rowstride, int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int P = 128 * wave + 64 * i + lane;
     const int row = P >> 4;
-    const uint16_t *src = kt + (int64_t)min(row, rmax) * rowstride + (((P & 15) ^ (row & 15)) * 8);
+    const int kt = min(kb0 + ti * kKeyTile + row, kb1 - 1);
+    const int khalo = min(max((row < kPoolHalo) ? kb1 + row : kb0 - 2 * kPoolHalo + row, 0), L - 1);
+    const int key = hal ? khalo : kt;
+    const uint16_t *src = kh + (int64_t)key * rowstride + (((P & 15) ^ (row & 15)) * 8);
     __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)(slot + (128 * wave + 64 * i) * 16), 16, 0, 0);
   }
+}
+
+// Exclusive prefix sum over the workgroup; also returns the total.
+__device__ inline int block_exscan(int v, int *tmp, int &total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) tmp[wid] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int s = tmp[i];
+    before += (i < wid) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return before + x - v;
 }
 
 // Row bookkeeping: observation row index -> causal limit (last visible key).
@@ -116,21 +190,209 @@ __device__ inline float sum16(const float (&e)[16]) {
   return (a + b) + (c + d);
 }
 
-// RT: row tiles (of 32 rows) per wave.
+// log2 of row `row`'s weight c_r (TideKV §4.2 / DeferKV guide Phase 2):
+// 1 per window row, 1 - alpha and alpha with a decode row, or the
+// normalised exponential weights.
+__device__ inline float row_log2_weight(const ScoreParams &p, int row) {
+  const int wr = row / p.G;  // observation row: window rows 0 .. w-1, then the decode row
+  if (p.weighting == 1) {
+    // c_r = 2^(lambda log2(e) (r - r_max)) / norm, relative position r = wr - (w - 1)
+    return p.lam2 * (float)(wr - (p.w - 1) - p.has_decode) - p.log2norm;
+  }
+  float c = 1.0f;
+  if (p.has_decode) c = (wr < p.w) ? (1.0f - p.alpha) : p.alpha;
+  return (c > 0.0f) ? log2f(c) : -INFINITY;
+}
+
+// The start of pass 2: every row's bias = r + log2(Z) - log2(c_r) from the
+// segment's nblk pass-1 block states (r, Z).  Two threads per row (row
+// row0 + tid / 2, share sh = tid % 2): share sh loads the states of blocks
+// sh, sh + 2, ... MB at a time, takes their largest r, m, then the sum of
+// Z 2^(r - m) in block order, and folds that into its running state; share
+// 0 then takes in share 1.  Every pass-2 workgroup of the segment computes
+// the same bits.  The first batch of loads is issued before the key tiles
+// (so that waiting for it does not mean waiting for them), by
+// MergeRows::load; MergeRows::finish does the rest.
+struct MergeRows {
+  static constexpr int MB = 16;
+  float2 v[MB];
+  int row, sh;
+  const float2 *all;
+
+  // Unconditional loads, clamped into the segment's states (all written by
+  // pass 1, so finite or (-inf, 0)); a state past the end becomes (-inf, 0)
+  // by arithmetic on the loaded value, which keeps every load outside any
+  // branch: loads under a branch would make the compiler wait for every
+  // load in flight, the key tiles' too.
+  __device__ void load_batch(const ScoreParams &p, int bb0, int nblk) {
+    const int rc = min(row, p.Rpad - 1);
+#pragma unroll
+    for (int u = 0; u < MB; ++u) {
+      const int bb = bb0 + 2 * u;
+      const float2 w = all[(int64_t)min(bb, nblk - 1) * p.Rpad + rc];
+      const bool ok = bb < nblk && row < p.R;
+      v[u] = make_float2(w.x + (ok ? 0.0f : -INFINITY), w.y * (ok ? 1.0f : 0.0f));
+    }
+  }
+  __device__ void fold(float &r, float &z) const {
+    float m = v[0].x;
+#pragma unroll
+    for (int u = 1; u < MB; ++u) m = fmaxf(m, v[u].x);
+    if (m > -INFINITY) {
+      float t = 0.0f;
+#pragma unroll
+      for (int u = 0; u < MB; ++u) t = fmaf(v[u].y, fast_exp2(v[u].x - m), t);
+      lse_merge(r, z, m, t);
+    }
+  }
+  // The first batch of rows row0 = 0.
+  __device__ void load(const ScoreParams &p, int seg, int nblk) {
+    all = p.partials + (int64_t)seg * p.nblk1_max * p.Rpad;
+    sh = threadIdx.x & 1;
+    row = (int)(threadIdx.x >> 1);
+    load_batch(p, sh, nblk);
+  }
+  // The rows of group `row` (its first batch loaded) into out.
+  __device__ void group(const ScoreParams &p, int nblk, float *out) {
+    float r = -INFINITY, z = 0.0f;
+    fold(r, z);
+    for (int bb0 = sh + 2 * MB; bb0 < nblk; bb0 += 2 * MB) {
+      load_batch(p, bb0, nblk);
+      fold(r, z);
+    }
+    const float r2 = __shfl_xor(r, 1), z2 = __shfl_xor(z, 1);
+    if (sh == 0 && row < p.Rpad) {
+      lse_merge(r, z, r2, z2);
+      const float lc = row_log2_weight(p, row);
+      float b = INFINITY;  // a row of weight 0 (or without visible keys) contributes nothing
+      if (row < p.R && lc > -INFINITY && z > 0.0f) b = r + log2f(z) - lc;
+      out[row] = b;
+    }
+  }
+  // Biases of rows [0, Rpad) into out.  The first group is outside the
+  // loop, so that its wait covers only its own loads.
+  __device__ void finish(const ScoreParams &p, int nblk, float *out) {
+    group(p, nblk, out);
+    for (int row0 = NT / 2; row0 < p.Rpad; row0 += NT / 2) {
+      row = row0 + (int)(threadIdx.x >> 1);
+      load_batch(p, sh, nblk);
+      group(p, nblk, out);
+    }
+  }
+};
+
+// The end of pass 2 with tables (see top).  red holds the waves' partial S
+// per key (rs floats per wave: the block's keys, then the halo tile's); hist
+// is 2048 words of LDS the key ring no longer needs.
+__device__ void tables_epilogue(const ScoreParams &p, float *red, int rs, uint32_t *hist, int seg, int h, int64_t key0,
+                                int L, int kb0, int kb1) {
+  static_assert(NT == kTabBlock, "one thread per position of a table block");
+  static_assert(kTabBins == 8 * NT, "eight bins per thread in the block scan");
+  constexpr int HALO = kPoolHalo;
+  __shared__ int tmp[NW];
+  const int tid = threadIdx.x;
+  const int n = kb1 - kb0;
+  const int r = p.pool_r;  // 0: no pool
+  const bool is_max = p.pool == 2;
+  const float fill = is_max ? -INFINITY : 0.0f;  // the pool's value outside the sequence
+  float *sbuf = red + NW * rs;                   // S of position kb0 + x at sbuf[HALO + x], x in [-HALO, n + HALO)
+  const int64_t segbase = (int64_t)p.Hkv * key0 + (int64_t)h * L;
+
+  // S by position: the sum over the waves in wave order, as pass 2 without
+  // tables stores it.
+  for (int x = tid - HALO; x < n + HALO; x += NT) {
+    const bool in_blk = x >= 0 && x < n;
+    if (!in_blk && r == 0) continue;
+    const int col = in_blk ? x : p.key_block + ((x < 0) ? 2 * HALO + x : x - n);
+    float v = red[col];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) v += red[w2 * rs + col];
+    if (in_blk && p.scores) p.scores[segbase + kb0 + x] = v;
+    const int pos = kb0 + x;
+    if (pos < 0 || pos >= L) v = fill;
+    sbuf[HALO + x] = v;
+  }
+  __syncthreads();
+
+  const uint32_t centre = order_key(p.wsum / (float)L);  // the key of the mean score
+  const int ntb = (n + kTabBlock - 1) / kTabBlock;
+  for (int tb = 0; tb < ntb; ++tb) {
+    // ---- pool, pooled output
+    const int x = tb * kTabBlock + tid;
+    float P = 0.0f;
+    if (x < n) {
+      const float *c = sbuf + HALO + x;
+      if (r == 0) {
+        P = c[0];
+      } else if (is_max) {
+        float m = c[0];
+        for (int j = -r; j <= r; ++j) m = fmaxf(m, c[j]);
+        P = m;
+      } else {
+        float sum = 0.0f;
+        for (int j = -r; j <= r; ++j) sum += c[j];
+        P = sum / p.pool_width;
+      }
+      p.pooled[segbase + kb0 + x] = P;
+    }
+
+    // ---- counting sort of the table block by first digit; the segment
+    // histogram
+    reinterpret_cast<uint4 *>(hist)[2 * tid] = make_uint4(0u, 0u, 0u, 0u);
+    reinterpret_cast<uint4 *>(hist)[2 * tid + 1] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    uint32_t key = 0u, dg = 0u, rank = 0u;
+    if (x < n) {
+      key = select_key(P, kb0 + x, L, p.sink, p.recent);
+      const int64_t rel = ((int64_t)key - (int64_t)centre) >> kTabDigitShift;
+      dg = (uint32_t)min<int64_t>(kTabBins - 1, max<int64_t>(0, rel + kTabBins / 2));
+      rank = atomicAdd(&hist[dg], 1u);
+    }
+    __syncthreads();
+    uint32_t cnt[8], pre[8];
+    {
+      const uint4 a0 = reinterpret_cast<const uint4 *>(hist)[2 * tid];
+      const uint4 a1 = reinterpret_cast<const uint4 *>(hist)[2 * tid + 1];
+      cnt[0] = a0.x; cnt[1] = a0.y; cnt[2] = a0.z; cnt[3] = a0.w;
+      cnt[4] = a1.x; cnt[5] = a1.y; cnt[6] = a1.z; cnt[7] = a1.w;
+    }
+    int own = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) own += (int)cnt[u];
+    int total;
+    uint32_t run = (uint32_t)block_exscan(own, tmp, total);  // its barriers end the reads above
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      pre[u] = run;
+      run += cnt[u];
+    }
+    const int64_t tabi = (int64_t)seg * p.ntab_max + kb0 / kTabBlock + tb;
+    reinterpret_cast<uint4 *>(p.tab + tabi * kTabBins)[tid] =
+        make_uint4(pre[0] | (pre[1] << 16), pre[2] | (pre[3] << 16), pre[4] | (pre[5] << 16), pre[6] | (pre[7] << 16));
+    // this workgroup's copy of the segment histogram: consecutive
+    // workgroups go to different compute dies, and so do the copies
+    const int copy = (int)((blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z)) % kTabHistCopies);
+    uint32_t *sh = p.seg_hist + ((int64_t)seg * kTabHistCopies + copy) * kTabBins + 8 * tid;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (cnt[u]) atomicAdd(sh + u, cnt[u]);
+    reinterpret_cast<uint4 *>(hist)[2 * tid] = make_uint4(pre[0], pre[1], pre[2], pre[3]);
+    reinterpret_cast<uint4 *>(hist)[2 * tid + 1] = make_uint4(pre[4], pre[5], pre[6], pre[7]);
+    __syncthreads();
+    if (x < n) p.bucket[tabi * kTabBlock + hist[dg] + rank] = key;
+    __syncthreads();  // hist is cleared for the next table block
+  }
+}
+
 // RT: full row tiles (of 32 rows) per wave.  SPLIT: there is one more row
 // tile (4 RT + 1 in all), split into four 16 x 16 blocks per key tile, one
 // per wave: wave v takes its rows 16 (v / 2) .. + 15 against the key tile's
 // keys 16 (v % 2) .. + 15, with v_mfma_f32_16x16x32_bf16, so that no wave
 // carries a whole extra tile (the slowest wave sets every step's pace).
-template <int PASS, int RT, bool SPLIT = false>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SPLIT ? (RT > 2 ? 1 : 2) : RT > 1 ? 1 : 4))) void score_kernel(ScoreParams p, SegTable t) {
-  // The LDS ring: one array per slot, so that the compiler can tell a
-  // slot being read from the slots that loads are landing in.
-  __shared__ __attribute__((aligned(16))) char tile0[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char tile1[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char tile2[TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char tile3[TILE_BYTES];
-  extern __shared__ float red[];  // pass 2: [NW][key_block] partial sums
+// TAB (pass 2 only): the halo tile, pool and selection tables (see top).
+template <int PASS, int RT, bool SPLIT = false, bool TAB = false>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT > 1 ? 1 : 2))) void score_kernel(ScoreParams p, SegTable t) {
+  extern __shared__ float red[];  // pass 2: [NW][rs] partial sums (TAB: then S by position)
 
   const int blk = blockIdx.x;
   const int h = blockIdx.y;
@@ -144,6 +406,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SPLIT ? (RT 
   if (kb0 >= kend) return;  // the whole workgroup leaves together
   const int kb1 = min(kend, kb0 + p.key_block);
   const int seg = t.seg0 + sb * p.Hkv + h;
+  if (PASS == 1 && p.seg_hist) {
+    // this block's slice of the segment's selection histogram (all its
+    // copies), cleared for the pass 2 that adds to it
+    constexpr int nw = kTabHistCopies * kTabBins;
+    const int nbs = (L + p.key_block - 1) / p.key_block;
+    const int z0 = (int)((int64_t)blk * nw / nbs), z1 = (int)((int64_t)(blk + 1) * nw / nbs);
+    for (int i = z0 + (int)threadIdx.x; i < z1; i += NT) p.seg_hist[(int64_t)seg * nw + i] = 0u;
+  }
   const int b = t.seq0 + sb;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -183,13 +453,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SPLIT ? (RT 
     ref[k] = -INFINITY;
     zs[k] = 0.0f;
     lim[k] = row_limit((wave + NW * k) * 32 + lr, p, L);
-    if constexpr (PASS == 2) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = (wave + NW * k) * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-        bias[k][i] = (k < my_rt) ? p.bias[(int64_t)seg * p.Rpad + row] : INFINITY;
-      }
-    }
   }
 
   // The split tile.  Lane l supplies, at k-step j (32 wide), row (or key)
@@ -217,10 +480,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SPLIT ? (RT 
       for (int j = 0; j < 4; ++j) qs[j] = as_frag(make_uint4(0u, 0u, 0u, 0u));
     }
     lim5 = row_limit(row, p, L);
-    if constexpr (PASS == 2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bias5[i] = p.bias[(int64_t)seg * p.Rpad + srow + 4 * s4 + i];
-    }
   }
   // LDS byte offsets of this lane's split-tile key operand at k-step j: key
   // skey + s16 of the tile, chunk 4 j + s4, swizzled like the 32-wide reads.
@@ -234,42 +493,60 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SPLIT ? (RT 
   const float cl2 = p.cl2;
   const int minlim = p.causal ? (L - p.w) : (L - 1);  // keys up to here are visible to every row
   const int ntile = (kb1 - kb0 + KT - 1) / KT;
+  // TAB with a pool: one more step scores the halo tile (its keys after the
+  // block's in red: rs floats per wave).
+  const bool halo = TAB && p.pool_r > 0;
+  const int nsteps = ntile + (halo ? 1 : 0);
+  const int rs = TAB ? p.key_block + 2 * kPoolHalo : p.key_block;
   const int rowstride = p.Hkv * kHeadDim;  // elements between consecutive keys of one head
-  const uint16_t *kblk = p.K + (key0 + kb0) * (int64_t)rowstride + (int64_t)h * kHeadDim;
-  const int last = kb1 - 1 - kb0;  // block-relative index of the block's last key
   // LDS byte offset of this lane's operand chunk for k-step j: row lr, chunk 2j + hf, swizzled.
   const int rd_base = lr * ROWB;
   const int sw = lr & 15;
 
-  // Tiles go straight from memory into a ring of PD = 4 LDS slots, three
+  // Tiles go straight from memory into a ring of PD LDS slots, PD - 1
   // tiles ahead of the one being consumed.  Every step issues exactly two
   // loads per wave (past the block they re-read its last key), so before
-  // step t this wave has tiles t .. t + 2 in flight, and waiting until at
-  // most 2 (PD - 2) loads remain means tile t has landed.
-  auto tile_src = [&](int ti) { return kblk + (int64_t)(ti * KT) * rowstride; };
-  issue_tile(tile0, tile_src(0), last, rowstride, wave, lane);
-  issue_tile(tile1, tile_src(1), last - KT, rowstride, wave, lane);
-  issue_tile(tile2, tile_src(2), last - 2 * KT, rowstride, wave, lane);
+  // step t this wave has tiles t .. t + PD - 2 in flight, and waiting until
+  // at most 2 (PD - 2) loads remain means tile t has landed.
+  const uint16_t *kh = p.K + key0 * (int64_t)rowstride + (int64_t)h * kHeadDim;
+  auto issue = [&](char *slot, int ti) { issue_keys(slot, kh, halo && ti == ntile, ti, kb0, kb1, L, rowstride, wave, lane); };
+  MergeRows mr;
+  const int nstat = (int)((L + (int64_t)p.stat_block - 1) / p.stat_block);  // pass-1 block states per row
+  if constexpr (PASS == 2) mr.load(p, seg, nstat);
+#pragma unroll
+  for (int j = 0; j < PD - 1; ++j) issue(ring(j), j);
 
-  // Consumes tile ti from `cur` after refilling `nxt` (the slot of tile
-  // ti - 1) with tile ti + 3.
-  auto step = [&](const int ti, const char *cur, char *nxt) {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(kWaitTile);  // this wave's part of tile ti is in LDS
-    __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): this wave's reads of tile ti - 1 are done
-    __builtin_amdgcn_s_barrier();           // every wave's part has landed; nxt is free
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    issue_tile(nxt, tile_src(ti + 3), last - (ti + 3) * KT, rowstride, wave, lane);
-    if (ti >= ntile) return;  // padding step of the last group of four
-    const char *slot = cur;
-    const int i0 = kb0 + ti * KT;
-    if (my_rt == 0) {  // this wave owns no rows (fewer than four row tiles in all)
-      if constexpr (PASS == 2)
-        if (hf == 0) red[wave * p.key_block + ti * KT + lr] = 0.0f;
-      return;
+  if constexpr (PASS == 2) {
+    // The row biases, merged while the first tiles load.
+    __shared__ float bias_s[kMaxRows];
+    mr.finish(p, nstat, bias_s);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < RT; ++k) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = (wave + NW * k) * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+        bias[k][i] = (k < my_rt) ? bias_s[row] : INFINITY;
+      }
     }
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bias5[i] = bias_s[srow + 4 * s4 + i];
+    }
+  }
 
-    f32x16 acc[RT];
+  // Two stages per key tile: its MFMAs (reading the tile from its LDS slot)
+  // and its exp / sum work on the accumulators.  With PIPE, step t issues
+  // tile t's MFMAs and then does tile t - 1's exp / sum work, which depends
+  // only on registers, so the wave's VALU work runs while its matrix core
+  // works (two accumulator sets alternate); without PIPE (many row tiles per
+  // wave, where registers are short) both stages of tile t run in step t.
+  constexpr bool PIPE = RT <= 2;
+  static_assert(!PIPE || PD % 2 == 0, "accumulator sets alternate with the slot parity");
+  f32x16 accs[PIPE ? 2 : 1][RT];
+  f32x4 saccs[PIPE ? 2 : 1];
+
+  auto mfma_tile = [&](const char *slot, f32x16 (&acc)[RT], f32x4 &sacc) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const bf16x8 kf = as_frag(*reinterpret_cast<const uint4 *>(slot + rd_base + (((2 * j + hf) ^ sw) << 4)));
@@ -284,7 +561,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SPLIT ? (RT 
         }
       }
     }
-    f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    sacc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (SPLIT) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -295,7 +572,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SPLIT ? (RT 
           sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qs[j], kf, sacc, 0, 0, 0);
       }
     }
-    const bool need_mask = (i0 + KT - 1) > minlim;
+  };
+
+  // The exp / sum stage of tile ti from its accumulators.
+  auto valu_tile = [&](const int ti, const f32x16 (&acc)[RT], const f32x4 &sacc) {
+    const int i0 = kb0 + ti * KT;
+    // The halo step: key x of the tile is kb1 + x or kb0 - 2 HALO + x.
+    const bool hstep = halo && ti == ntile;
+    auto key_at = [&](int x) { return hstep ? ((x < kPoolHalo) ? kb1 + x : kb0 - 2 * kPoolHalo + x) : i0 + x; };
+    const int rbase = wave * rs + (hstep ? p.key_block : ti * KT);  // this tile's keys in red
+    if (my_rt == 0) {  // this wave owns no rows (fewer than four row tiles in all)
+      if constexpr (PASS == 2)
+        if (hf == 0) red[rbase + lr] = 0.0f;
+      return;
+    }
+    const bool need_mask = hstep || (i0 + KT - 1) > minlim;
 
     if constexpr (PASS == 1) {
       // acc[k][i]: key i0 + 8*(i/4) + 4*hf + i%4, row of this lane.
@@ -379,7 +670,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SPLIT ? (RT 
 #pragma unroll
           for (int i = 0; i < 16; ++i) e[i] = fast_exp2(fmaf(acc[k][i], cl2, -bias[k][i]));
         } else {
-          const int key = i0 + lr;
+          const int key = key_at(lr);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int row = (wave + NW * k) * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
@@ -401,27 +692,50 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SPLIT ? (RT 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float v = fast_exp2(fmaf(sacc[i], cl2, -bias5[i]));
-          s5 += (need_mask && (i0 + skey + s16) > row_limit(srow + 4 * s4 + i, p, L)) ? 0.0f : v;
+          s5 += (need_mask && key_at(skey + s16) > row_limit(srow + 4 * s4 + i, p, L)) ? 0.0f : v;
         }
         s5 += __shfl_xor(s5, 16);
         s5 += __shfl_xor(s5, 32);
         s += ((lr >> 4) == (wave & 1)) ? s5 : 0.0f;
       }
-      if (hf == 0) red[wave * p.key_block + ti * KT + lr] = s;
+      if (hf == 0) red[rbase + lr] = s;
     }
   };
-  for (int t0 = 0; t0 < ntile; t0 += PD) {
-    step(t0, tile0, tile3);
-    step(t0 + 1, tile1, tile0);
-    step(t0 + 2, tile2, tile1);
-    step(t0 + 3, tile3, tile2);
+
+  // Step ti: waits for tile ti, refills the slot of tile ti - 1 with tile
+  // ti + PD - 1, then runs the stages due (j: ti mod PD, known after
+  // unrolling).
+  auto step = [&](const int ti, const int j, const char *cur, char *nxt) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(kWaitTile);  // this wave's part of tile ti is in LDS
+    __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): this wave's reads of tile ti - 1 are done
+    __builtin_amdgcn_s_barrier();           // every wave's part has landed; nxt is free
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    issue(nxt, ti + PD - 1);
+    if constexpr (PIPE) {
+      if (ti < nsteps && my_rt > 0) mfma_tile(cur, accs[j & 1], saccs[j & 1]);
+      if (ti >= 1 && ti <= nsteps) valu_tile(ti - 1, accs[(j + 1) & 1], saccs[(j + 1) & 1]);
+    } else {
+      if (ti < nsteps) {
+        if (my_rt > 0) mfma_tile(cur, accs[0], saccs[0]);
+        valu_tile(ti, accs[0], saccs[0]);
+      }
+    }
+  };
+  const int nloop = PIPE ? nsteps + 1 : nsteps;  // PIPE: one more step for the last tile's exp / sum
+  for (int t0 = 0; t0 < nloop; t0 += PD) {
+#pragma unroll
+    for (int j = 0; j < PD; ++j) step(t0 + j, j, ring(j), ring((j + PD - 1) % PD));
   }
   // The last steps issued loads for tiles past the block that nobody
   // consumes; they write LDS, so drain them before the workgroup can end.
   __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0)
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
-  if constexpr (PASS == 2) {
+  if constexpr (PASS == 2 && TAB) {
+    __syncthreads();
+    tables_epilogue(p, red, rs, reinterpret_cast<uint32_t *>(g_ring0), seg, h, key0, L, kb0, kb1);
+  } else if constexpr (PASS == 2) {
     __syncthreads();
     const int n = kb1 - kb0;
     // The public layout, or (streaming) one window of out_stride floats per
@@ -436,7 +750,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SPLIT ? (RT 
     }
   } else {
     // Merge the two lane halves that share each row and publish this
-    // block's per-row state; the blocks are merged by merge_kernel.
+    // block's per-row state; pass 2 merges the blocks.
     float2 *part = p.partials + ((int64_t)seg * p.nblk1_max + blk) * p.Rpad;
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
@@ -466,28 +780,23 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SPLIT ? (RT 
   }
 }
 
-// Merge of the pass-1 block states of every (sequence, head) into the
-// per-row bias = r + log2(Z) - log2(c_r) that pass 2 subtracts.  A separate
-// launch: the kernel boundary makes every block's partials visible, with no
-// per-workgroup cache write-backs.  Workgroup (row group of 16, segment):
-// sixteen threads share a row, each merging every sixteenth block with 16
-// loads in flight; the shares are combined in a fixed order through LDS.
+// The streaming form's fold (TideKV §4.2 with a bounded workspace): the
+// block states of the step's keys [key_begin, key_end) merged, in a fixed
+// order, into the running state `run` of each row (its first step starts
+// it).  Workgroup (row group of 16, segment): sixteen threads share a row,
+// each merging every sixteenth block with 16 loads in flight; the shares
+// are combined in a fixed order through LDS.
 constexpr int MERGE_ROWS = 16;
 constexpr int MERGE_SPLIT = NT / MERGE_ROWS;
 
-// FOLD (the streaming form, TideKV §4.2 with a bounded workspace): merge the
-// block states of the step's keys [key_begin, key_end) and the running
-// state `run` (unless this is the first step) back into `run` instead.
-template <bool FOLD>
-__global__ __launch_bounds__(NT) void merge_kernel(ScoreParams p, SegTable t, float2 *run, int first) {
+__global__ __launch_bounds__(NT) void fold_kernel(ScoreParams p, SegTable t, float2 *run, int first) {
   __shared__ float2 shares[MERGE_SPLIT][MERGE_ROWS];
   const int sl = blockIdx.y;  // local segment: sequence-major, head-minor
   const int sb = sl / p.Hkv;
   const int seg = t.seg0 + sl;
   const int L = (int)(t.key_off[sb + 1] - t.key_off[sb]);
   const int kend = min(L, p.key_end);
-  const int nblk = FOLD ? ((kend > p.key_begin) ? (kend - p.key_begin + p.key_block - 1) / p.key_block : 0)
-                        : (L + p.key_block - 1) / p.key_block;
+  const int nblk = (kend > p.key_begin) ? (kend - p.key_begin + p.key_block - 1) / p.key_block : 0;
   const int lrow = threadIdx.x % MERGE_ROWS;
   const int sh = threadIdx.x / MERGE_ROWS;
   const int row = blockIdx.x * MERGE_ROWS + lrow;
@@ -510,48 +819,32 @@ __global__ __launch_bounds__(NT) void merge_kernel(ScoreParams p, SegTable t, fl
   if (sh != 0 || row >= p.Rpad) return;
 #pragma unroll
   for (int k = 1; k < MERGE_SPLIT; ++k) lse_merge(r, z, shares[k][lrow].x, shares[k][lrow].y);
-  if constexpr (FOLD) {
-    float2 *mine = run + (int64_t)seg * p.Rpad + row;
-    if (!first) {
-      const float2 prev = *mine;
-      lse_merge(r, z, prev.x, prev.y);
-    }
-    *mine = make_float2(r, z);
-    return;
+  float2 *mine = run + (int64_t)seg * p.Rpad + row;
+  if (!first) {
+    const float2 prev = *mine;
+    lse_merge(r, z, prev.x, prev.y);
   }
-  const int wr = row / p.G;  // observation row: window rows 0 .. w-1, then the decode row
-  float lc;                  // log2 of the row's weight c_r
-  if (p.weighting == 1) {
-    // c_r = 2^(lambda log2(e) (r - r_max)) / norm, relative position r = wr - (w - 1)
-    lc = p.lam2 * (float)(wr - (p.w - 1) - p.has_decode) - p.log2norm;
-  } else {
-    float c = 1.0f;
-    if (p.has_decode) c = (wr < p.w) ? (1.0f - p.alpha) : p.alpha;
-    lc = (c > 0.0f) ? log2f(c) : -INFINITY;
-  }
-  float out = INFINITY;  // a row of weight 0 (or without visible keys) contributes nothing
-  if (row < p.R && lc > -INFINITY && z > 0.0f) out = r + log2f(z) - lc;
-  p.bias[(int64_t)seg * p.Rpad + row] = out;
+  *mine = make_float2(r, z);
 }
 
-template <int PASS>
+template <int PASS, bool TAB = false>
 hipError_t launch_pass(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s, size_t lds) {
   const dim3 grid(nblk, p.Hkv, t.nseq);
   const dim3 block(NT);
   if (p.nrt % NW == 1 && p.nrt > NW) {  // whole row tiles per wave plus a split one
     switch (p.nrt / NW) {
-      case 1: hipLaunchKernelGGL((score_kernel<PASS, 1, true>), grid, block, lds, s, p, t); break;
-      case 2: hipLaunchKernelGGL((score_kernel<PASS, 2, true>), grid, block, lds, s, p, t); break;
-      default: hipLaunchKernelGGL((score_kernel<PASS, 3, true>), grid, block, lds, s, p, t); break;
+      case 1: hipLaunchKernelGGL((score_kernel<PASS, 1, true, TAB>), grid, block, lds, s, p, t); break;
+      case 2: hipLaunchKernelGGL((score_kernel<PASS, 2, true, TAB>), grid, block, lds, s, p, t); break;
+      default: hipLaunchKernelGGL((score_kernel<PASS, 3, true, TAB>), grid, block, lds, s, p, t); break;
     }
     return hipGetLastError();
   }
   const int rt = (p.nrt + NW - 1) / NW;
   switch (rt) {
-    case 1: hipLaunchKernelGGL((score_kernel<PASS, 1>), grid, block, lds, s, p, t); break;
-    case 2: hipLaunchKernelGGL((score_kernel<PASS, 2>), grid, block, lds, s, p, t); break;
-    case 3: hipLaunchKernelGGL((score_kernel<PASS, 3>), grid, block, lds, s, p, t); break;
-    default: hipLaunchKernelGGL((score_kernel<PASS, 4>), grid, block, lds, s, p, t); break;
+    case 1: hipLaunchKernelGGL((score_kernel<PASS, 1, false, TAB>), grid, block, lds, s, p, t); break;
+    case 2: hipLaunchKernelGGL((score_kernel<PASS, 2, false, TAB>), grid, block, lds, s, p, t); break;
+    case 3: hipLaunchKernelGGL((score_kernel<PASS, 3, false, TAB>), grid, block, lds, s, p, t); break;
+    default: hipLaunchKernelGGL((score_kernel<PASS, 4, false, TAB>), grid, block, lds, s, p, t); break;
   }
   return hipGetLastError();
 }
@@ -562,20 +855,22 @@ hipError_t launch_score_pass1(const ScoreParams &p, const SegTable &t, int nblk,
   return launch_pass<1>(p, t, nblk, s, 0);
 }
 
-hipError_t launch_score_merge(const ScoreParams &p, const SegTable &t, hipStream_t s) {
-  const dim3 grid((p.Rpad + MERGE_ROWS - 1) / MERGE_ROWS, t.nseq * p.Hkv);
-  hipLaunchKernelGGL(merge_kernel<false>, grid, dim3(NT), 0, s, p, t, (float2 *)nullptr, 0);
-  return hipGetLastError();
-}
-
 hipError_t launch_stream_stats(const ScoreParams &p, const SegTable &t, float2 *run, int first, hipStream_t s) {
   const dim3 grid((p.Rpad + MERGE_ROWS - 1) / MERGE_ROWS, t.nseq * p.Hkv);
-  hipLaunchKernelGGL(merge_kernel<true>, grid, dim3(NT), 0, s, p, t, run, first);
+  hipLaunchKernelGGL(fold_kernel, grid, dim3(NT), 0, s, p, t, run, first);
   return hipGetLastError();
 }
 
 hipError_t launch_score_pass2(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
   return launch_pass<2>(p, t, nblk, s, (size_t)NW * p.key_block * sizeof(float));
+}
+
+hipError_t launch_score_pass2_tables(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
+  if (p.key_block % kTabBlock != 0 || p.pool_r < 0 || p.pool_r > kPoolHalo || !p.pooled || !p.tab || !p.bucket ||
+      !p.seg_hist)
+    return hipErrorInvalidValue;
+  const size_t rs = (size_t)p.key_block + 2 * kPoolHalo;
+  return launch_pass<2, true>(p, t, nblk, s, (NW + 1) * rs * sizeof(float));
 }
 
 }  // namespace kvsel

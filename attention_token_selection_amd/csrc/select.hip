@@ -564,8 +564,8 @@ __global__ __launch_bounds__(NT) void select_chunk_kernel(SelectParams p, SegTab
 }
 
 
-// ---------------------------------------------------------------- selection from the resident scoring's tables
-// The resident scoring leaves, per block of RBP = 512 positions, the
+// ---------------------------------------------------------------- selection from pass 2's tables
+// Pass 2 with tables leaves, per block of RBP = 256 positions, the
 // exclusive prefix of the block's first-digit histogram (a monotone
 // function of the order key; tab_fine, u16 [NB2]) and the block's keys
 // grouped by digit (bucket, u32 [RBP]), plus each segment's whole digit
@@ -575,9 +575,9 @@ __global__ __launch_bounds__(NT) void select_chunk_kernel(SelectParams p, SegTab
 // whole 32-bit keys in three radix rounds (11 + 11 + 10 bits) over those
 // candidates; per-block kept counts; the chunk's ordered compaction and,
 // with K_out, the copy.  The digit function itself is never needed here.
-constexpr int RBP = kResBlock;
+constexpr int RBP = kTabBlock;
 constexpr int CPB = CH / RBP;            // blocks per chunk
-constexpr int NB2 = kResBins;
+constexpr int NB2 = kTabBins;
 constexpr int BPT = 16;                  // blocks per thread in the per-block scans
 constexpr int MAXB = BPT * NT;           // blocks per segment: 4096, so up to 2^20 positions
 static_assert(CPB == 8 && BPT == 2 * CPB, "a chunk's blocks are one half of a thread's share");
@@ -601,8 +601,6 @@ __global__ __launch_bounds__(NT) void select_block_kernel(SelectParams p, SegTab
   __shared__ int tmp[NWAVE];
   __shared__ int sh[4];
 
-  // The next call's token (the scoring that ran before has finished).
-  if ((blockIdx.x | blockIdx.y | blockIdx.z) == 0 && threadIdx.x == 0) p.sync[0] = p.sync[1] + 1;
   const Segment g = segment_of(p, t, blockIdx.y, blockIdx.z);
   const int c = GATHER ? (blockIdx.x >> 1) : blockIdx.x;
   const int half = GATHER ? (blockIdx.x & 1) : 0;
@@ -638,27 +636,13 @@ __global__ __launch_bounds__(NT) void select_block_kernel(SelectParams p, SegTab
       sh[1] = 0;
     }
     {
-      uint32_t cnt[8];
-      if (p.sync[kSyncIncomplete + g.seg] != p.sync[1] + 1) {
-        const uint4 *SH = reinterpret_cast<const uint4 *>(p.seg_hist + (int64_t)g.seg * NB2);
+      uint32_t cnt[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int cp = 0; cp < kTabHistCopies; ++cp) {  // the histogram's copies add up to it
+        const uint4 *SH = reinterpret_cast<const uint4 *>(p.seg_hist + ((int64_t)g.seg * kTabHistCopies + cp) * NB2);
         const uint4 a0 = SH[2 * tid], a1 = SH[2 * tid + 1];
-        cnt[0] = a0.x; cnt[1] = a0.y; cnt[2] = a0.z; cnt[3] = a0.w;
-        cnt[4] = a1.x; cnt[5] = a1.y; cnt[6] = a1.z; cnt[7] = a1.w;
-      } else {
-        // Some block stopped waiting for its segment and left the histogram
-        // incomplete: rebuild it from every block's exclusive prefix table.
-#pragma unroll
-        for (int u = 0; u < 8; ++u) cnt[u] = 0u;
-        for (int j = 0; j < nb; ++j) {
-          const int len = min(RBP, g.L - j * RBP);
-          const uint16_t *row = TF + (int64_t)j * NB2 + 8 * tid;
-          uint32_t e[9];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) e[u] = row[u];
-          e[8] = (8 * tid + 8 < NB2) ? (uint32_t)row[8] : (uint32_t)len;
-#pragma unroll
-          for (int u = 0; u < 8; ++u) cnt[u] += e[u + 1] - e[u];
-        }
+        cnt[0] += a0.x; cnt[1] += a0.y; cnt[2] += a0.z; cnt[3] += a0.w;
+        cnt[4] += a1.x; cnt[5] += a1.y; cnt[6] += a1.z; cnt[7] += a1.w;
       }
       int own = 0;
 #pragma unroll

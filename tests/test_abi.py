@@ -117,10 +117,8 @@ def test_longest_supported_sequence_plans():
 
 def test_key_chunk_caps_the_pass1_block():
     """key_chunk bounds the pass-1 block (TideKV's b_s): a chunk at or above
-    the library's own block sizes changes nothing; one below the resident
-    scoring's 512-key block leaves only the two-launch scoring (no resident
-    tables in the workspace), and a smaller one still means more blocks and
-    so more per-block row records."""
+    the library's own block size changes nothing, and a smaller one means
+    more blocks and so more per-block row records."""
     base = dict(Hq=32, Hkv=8, w=32, seq_lens=[4100, 2500], k=200)
     ws0 = kv.kvsel_plan(kv.Problem(**base))[0]
     assert kv.kvsel_plan(kv.Problem(**base, key_chunk=8192))[0] == ws0
