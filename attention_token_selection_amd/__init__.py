@@ -14,6 +14,7 @@ from .kvsel import (  # noqa: F401
     exported_functions,
     kvsel_allocate_budgets,
     kvsel_compress,
+    kvsel_compress_noalloc,
     kvsel_gather,
     kvsel_plan,
     kvsel_pool_topk,

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvsel.so")
 
-SOURCES = ["kvsel_api.cpp", "score.hip", "select.hip", "gather.hip", "qmean.hip", "warmup.hip", "budget.hip", "stream.hip"]
+SOURCES = ["kvsel_api.cpp", "score.hip", "select.hip", "gather.hip", "qmean.hip", "warmup.hip", "budget.hip", "stream.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

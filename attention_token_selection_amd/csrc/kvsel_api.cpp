@@ -655,6 +655,8 @@ kvsel_status reject_streaming(const Plan &P, const char *fn) {
 
 }  // namespace
 
+kvsel_status kvsel::set_error(kvsel_status s, const char *msg) { return fail(s, msg); }
+
 KVSEL_API int kvsel_abi_version(void) { return KVSEL_ABI_VERSION; }
 
 KVSEL_API const char *kvsel_status_string(kvsel_status s) {

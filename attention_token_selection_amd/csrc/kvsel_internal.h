@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kvsel.h"
+
 namespace kvsel {
 
 constexpr int kHeadDim = 128;        // d supported by this build
@@ -153,6 +155,9 @@ struct GatherParams {
   uint4 *V_out;
   int Hkv;
 };
+
+// Sets kvsel_last_error's message (this thread) and returns s.
+kvsel_status set_error(kvsel_status s, const char *msg);
 
 hipError_t launch_query_mean(const QueryMeanParams &p, hipStream_t s);
 hipError_t launch_profile(const ProfileParams &p, const SegTable &t, int64_t lmax, hipStream_t s);

@@ -79,6 +79,8 @@ _lib.kvsel_gather.restype = ctypes.c_int
 _lib.kvsel_gather.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.kvsel_compress.restype = ctypes.c_int
 _lib.kvsel_compress.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.kvsel_compress_noalloc.restype = ctypes.c_int
+_lib.kvsel_compress_noalloc.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.kvsel_profile_layer.restype = ctypes.c_int
 _lib.kvsel_profile_layer.argtypes = [_P, _vp, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]
 _lib.kvsel_tier_rank.restype = ctypes.c_int
@@ -306,6 +308,23 @@ def kvsel_compress(problem: Problem, Q, K, V, idx, K_out, V_out, pooled, ws, str
     with torch.cuda.device(dev):
         _check(_lib.kvsel_compress(problem.ref(), *args, ctypes.c_size_t(ws.numel()), _stream(stream, dev)),
                "kvsel_compress")
+
+def kvsel_compress_noalloc(problem: Problem, Q, K, V, idx, K_out, V_out, pooled, stream=None):
+    """kvsel_compress with the library's own per-GPU scratch as workspace
+    (no allocation; calls that overlap on one GPU race)."""
+    torch = _torch()
+    n = _sizes(problem)
+    dev = K.device
+    kept = n["kept"]
+    args = (_ptr(Q, "Q", torch.bfloat16, n["Q"], dev), _ptr(K, "K", torch.bfloat16, n["K"], dev),
+            _ptr(V, "V", torch.bfloat16, n["K"], dev),
+            _ptr(idx, "idx", torch.int32, kept, dev) if kept else None,
+            _ptr(K_out, "K_out", torch.bfloat16, kept * problem.d, dev) if kept else None,
+            _ptr(V_out, "V_out", torch.bfloat16, kept * problem.d, dev) if kept else None,
+            _ptr(pooled, "pooled", torch.float32, n["scores"], dev))
+    with torch.cuda.device(dev):
+        _check(_lib.kvsel_compress_noalloc(problem.ref(), *args, _stream(stream, dev)), "kvsel_compress_noalloc")
+
 
 def kvsel_profile_layer(problem: Problem, Q, K, profile, ws, accumulate: bool = False, stream=None):
     """One layer's contribution to the warm-up importance profile [sum L]."""

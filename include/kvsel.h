@@ -229,6 +229,25 @@ kvsel_status kvsel_compress(const kvsel_problem *p, const void *Q, const void *K
                             void *ws, size_t ws_bytes, kvsel_stream_t stream);
 
 /*
+ * kvsel_compress without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It allocates nothing: its
+ * workspace is a 64 MiB array in device memory that the library holds on
+ * each GPU it runs on, from the first call there until the process ends.
+ * Arguments, layouts and results are those of kvsel_compress.
+ *
+ * Every call on one GPU uses that GPU's array, so calls that overlap on a
+ * GPU (on other streams or host threads) race; order them.
+ *
+ * Errors as for kvsel_compress, and KVSEL_EUNSUPPORTED (message in
+ * kvsel_last_error) for a problem whose kvsel_plan workspace exceeds
+ * 64 MiB; KVSEL_EHIP if the array's device address cannot be obtained.
+ */
+kvsel_status kvsel_compress_noalloc(const kvsel_problem *p, const void *Q, const void *K, const void *V,
+                                    int32_t *idx, void *K_out, void *V_out, float *pooled,
+                                    kvsel_stream_t stream);
+
+/*
  * Importance-guided warm-up (KVDrive, "A Holistic Multi-Tier KV Cache
  * Management System for Long-Context LLM Inference", §7.1): the observation
  * rows' attention over every prefix key, aggregated over the heads and the
