@@ -505,8 +505,10 @@ kvsel_status run_compress_fused(const Plan &P, const void *Q, const void *K, con
     sp.key_block = P.kb2t;
     hipError_t e = launch_score_pass2_tables(sp, t, (int)((lmax + P.kb2t - 1) / P.kb2t), st);
     if (e != hipSuccess) return hip_fail(e, "score pass 2 launch");
-    e = launch_select_blocks(sel, t, st);
-    if (e != hipSuccess) return hip_fail(e, "selection launch");
+    if (t.kmax > 0) {  // some segment of the group keeps a row
+      e = launch_select_blocks(sel, t, st);
+      if (e != hipSuccess) return hip_fail(e, "selection launch");
+    }
     return KVSEL_OK;
   });
 }

@@ -452,7 +452,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT > 1 ? 1 :
   for (int k = 0; k < RT; ++k) {
     ref[k] = -INFINITY;
     zs[k] = 0.0f;
-    lim[k] = row_limit((wave + NW * k) * 32 + lr, p, L);
+    // pass 1: a key past the block's end (a re-read of its last key) is
+    // masked like a key past the row's causal limit
+    lim[k] = min(row_limit((wave + NW * k) * 32 + lr, p, L), kb1 - 1);
   }
 
   // The split tile.  Lane l supplies, at k-step j (32 wide), row (or key)
@@ -479,7 +481,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT > 1 ? 1 :
 #pragma unroll
       for (int j = 0; j < 4; ++j) qs[j] = as_frag(make_uint4(0u, 0u, 0u, 0u));
     }
-    lim5 = row_limit(row, p, L);
+    lim5 = min(row_limit(row, p, L), kb1 - 1);
   }
   // LDS byte offsets of this lane's split-tile key operand at k-step j: key
   // skey + s16 of the tile, chunk 4 j + s4, swizzled like the 32-wide reads.
@@ -586,7 +588,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT > 1 ? 1 :
         if (hf == 0) red[rbase + lr] = 0.0f;
       return;
     }
-    const bool need_mask = hstep || (i0 + KT - 1) > minlim;
+    const bool need_mask = hstep || (i0 + KT - 1) > ((PASS == 1) ? min(minlim, kb1 - 1) : minlim);
 
     if constexpr (PASS == 1) {
       // acc[k][i]: key i0 + 8*(i/4) + 4*hf + i%4, row of this lane.

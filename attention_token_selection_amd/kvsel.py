@@ -398,8 +398,16 @@ def alloc_outputs(problem: Problem, device, pooled: bool = True):
 
 
 def compress(problem: Problem, Q, K, V, pooled: bool = True, stream=None):
-    """Allocate outputs, run kvsel_compress, return them in a dict."""
-    out = alloc_outputs(problem, K.device, pooled=pooled)
+    """Allocate outputs, run kvsel_compress, return them in a dict.  With a
+    stream given, the outputs and workspace are allocated on that stream (so
+    that torch's caching allocator ties their reuse to the work that writes
+    them there)."""
+    torch = _torch()
+    if stream is None:
+        out = alloc_outputs(problem, K.device, pooled=pooled)
+    else:
+        with torch.cuda.stream(stream):
+            out = alloc_outputs(problem, K.device, pooled=pooled)
     kvsel_compress(problem, Q, K, V, out["idx"], out["K_out"], out["V_out"], out["pooled"], out["ws"], stream)
     return out
 

@@ -155,7 +155,11 @@ int kvsel_abi_version(void);
  * returns the workspace size, in bytes, that kvsel_score, kvsel_pool_topk
  * and kvsel_compress need for this problem (one size serves all three), and,
  * if out_offsets_h is not NULL, the B*Hkv+1 output segment offsets
- * (out_offsets_h[0] = 0, last = total kept rows).
+ * (out_offsets_h[0] = 0, last = total kept rows): the compact layout of the
+ * kept rows with per-head offsets (TideKV, "Delayed KV Eviction via
+ * Layer-Wise Chunked Prefill", §4.1: each KV head keeps its own number of
+ * tokens, stored flattened with offsets).  Segment (b, h) holds
+ * min(k_bh, L_b) rows.
  * Errors: KVSEL_EINVAL for an invalid problem or NULL workspace_bytes.
  */
 kvsel_status kvsel_plan(const kvsel_problem *p, size_t *workspace_bytes, int64_t *out_offsets_h);

@@ -11,6 +11,10 @@ Tolerances (fp32 accumulation of exact bf16 products, fp32 exp2; fp64 oracle):
   with the budget left after them;
 * gathered K/V: bit-exact copies of the rows the GPU chose.
 A second, tighter band (DIAG_RTOL) is reported, not enforced.
+
+Every output buffer and workspace the GPU tests hand to the library sits
+between two guard bands of a known byte pattern (``Guarded``); the bands are
+checked after the calls, so a write past either end of a buffer fails.
 """
 
 from __future__ import annotations
@@ -19,6 +23,72 @@ import numpy as np
 
 RTOL = 2e-3
 DIAG_RTOL = 1e-5
+
+
+class Guarded:
+    """Device buffers with GUARD bytes of a fixed pattern on each side.
+
+    ``empty(n, dtype)`` returns an n-element view (256-byte aligned) inside a
+    larger allocation; ``check()`` asserts that no guard byte changed."""
+
+    GUARD = 4096
+
+    def __init__(self, device):
+        import torch
+
+        self.device = device
+        self.bufs = []
+        self.pattern = (torch.arange(self.GUARD, dtype=torch.int32, device=device) * 37 % 251 + 3).to(torch.uint8)
+
+    def empty(self, n, dtype, fill=None):
+        import torch
+
+        elt = torch.empty((), dtype=dtype).element_size()
+        nbytes = (n * elt + 255) // 256 * 256
+        raw = torch.empty(self.GUARD + nbytes + self.GUARD, dtype=torch.uint8, device=self.device)
+        raw[:self.GUARD] = self.pattern
+        raw[self.GUARD + nbytes:] = self.pattern
+        view = raw[self.GUARD:self.GUARD + n * elt].view(dtype)
+        if fill is not None:
+            view.fill_(fill)
+        self.bufs.append((raw, nbytes))
+        return view
+
+    def outputs(self, kv, problem, pooled=True):
+        """Like kvsel.alloc_outputs, every buffer guarded."""
+        import torch
+
+        ws, offs = kv.kvsel_plan(problem)
+        kept = offs[-1]
+        n = sum(problem.seq_lens) * problem.Hkv
+        return {
+            "idx": self.empty(max(kept, 1), torch.int32),
+            "K_out": self.empty(max(kept, 1) * problem.d, torch.bfloat16).view(max(kept, 1), problem.d),
+            "V_out": self.empty(max(kept, 1) * problem.d, torch.bfloat16).view(max(kept, 1), problem.d),
+            "pooled": self.empty(max(n, 1), torch.float32) if pooled else None,
+            "ws": self.empty(ws, torch.uint8),
+            "out_offsets": offs,
+        }
+
+    def check(self):
+        import torch
+
+        torch.cuda.synchronize()
+        for i, (raw, nbytes) in enumerate(self.bufs):
+            head = raw[:self.GUARD]
+            tail = raw[self.GUARD + nbytes:]
+            assert torch.equal(head, self.pattern), f"guarded buffer {i}: bytes before it were written"
+            assert torch.equal(tail, self.pattern), f"guarded buffer {i}: bytes past its end were written"
+
+
+def compress_guarded(kv, problem, Q, K, V, pooled=True):
+    """kvsel_compress on guarded outputs and workspace; checks the guards."""
+    g = Guarded(K.device)
+    out = g.outputs(kv, problem, pooled=pooled)
+    kv.kvsel_compress(problem, Q, K, V, out["idx"], out["K_out"], out["V_out"], out["pooled"], out["ws"])
+    g.check()
+    out["guard"] = g
+    return out
 
 
 def to_np64(t):

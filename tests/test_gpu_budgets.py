@@ -12,7 +12,7 @@ import torch
 
 import oracle.kvsel_oracle as O
 import workloads as W
-from parity import check_against_oracle, check_scores, segments, to_np64
+from parity import Guarded, check_against_oracle, check_scores, compress_guarded, segments, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -34,10 +34,11 @@ def _say(msg):
 
 def _mass(kv, p, pooled, sizes):
     ws_bytes, _ = kv.kvsel_plan(p)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
-    mass = torch.full((p.batch * p.Hkv * len(sizes),), float("nan"), device=DEV)
+    g = Guarded(DEV)
+    ws = g.empty(ws_bytes, torch.uint8)
+    mass = g.empty(p.batch * p.Hkv * len(sizes), torch.float32, fill=float("nan"))
     kv.kvsel_topk_mass(p, pooled, sizes, mass, ws)
-    torch.cuda.synchronize()
+    g.check()
     return mass.cpu().numpy().reshape(p.batch * p.Hkv, len(sizes))
 
 
@@ -70,7 +71,7 @@ def test_adaptive_budgets_end_to_end(kv):
     cases = [W.make_case(spec, layer=l) for l in range(2)]
     benefit = []
     for case in cases:
-        out = kv.compress(p, *(case[x].to(DEV) for x in "QKV"))
+        out = compress_guarded(kv, p, *(case[x].to(DEV) for x in "QKV"))
         torch.cuda.synchronize()
         m = _mass(kv, p, out["pooled"], sizes)
         ref = O.compress(to_np64(case["Q"]), to_np64(case["K"]), to_np64(case["V"]), **W.oracle_kwargs(spec))
@@ -89,7 +90,7 @@ def test_adaptive_budgets_end_to_end(kv):
         bl = budgets[l * per:(l + 1) * per].reshape(spec.batch, spec.Hkv).tolist()
         s2 = W.Spec(**{**spec.__dict__, "budgets": bl})
         p2 = kv.Problem(**W.problem_kwargs(s2))
-        out = kv.compress(p2, *(case[x].to(DEV) for x in "QKV"))
+        out = compress_guarded(kv, p2, *(case[x].to(DEV) for x in "QKV"))
         torch.cuda.synchronize()
         ref = O.compress(to_np64(case["Q"]), to_np64(case["K"]), to_np64(case["V"]), **W.oracle_kwargs(s2))
         st = check_against_oracle(s2, case, out, ref)
@@ -101,7 +102,7 @@ def test_topk_mass_full_size(kv):
     spec = W.config(2)
     case = W.make_case(spec, layer=0, device=DEV)
     p = kv.Problem(**W.problem_kwargs(spec))
-    out = kv.compress(p, case["Q"], case["K"], case["V"])
+    out = compress_guarded(kv, p, case["Q"], case["K"], case["V"])
     sizes = [256, 512, 1024, 2048, 4096]
     m = _mass(kv, p, out["pooled"], sizes)
     gp = out["pooled"].cpu().numpy()

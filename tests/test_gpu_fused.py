@@ -26,7 +26,7 @@ import torch
 
 import oracle.kvsel_oracle as O
 import workloads as W
-from parity import check_against_oracle, to_np64
+from parity import check_against_oracle, compress_guarded, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -66,7 +66,7 @@ class _env:
 
 def _compress(kv, spec, case):
     p = kv.Problem(**W.problem_kwargs(spec))
-    out = kv.compress(p, *(case[x].to(DEV) for x in "QKV"), pooled=True)
+    out = compress_guarded(kv, p, *(case[x].to(DEV) for x in "QKV"), pooled=True)
     torch.cuda.synchronize()
     return out
 

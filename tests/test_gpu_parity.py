@@ -1,9 +1,9 @@
 """HIP path vs the fp64 oracle, through the C ABI, on an MI355X.
 
-Small shapes are checked on every segment; the full-size workloads on
-sampled segments (the oracle computes one (sequence, KV head) at a time)
-plus properties that hold on every segment: exact top-k of the GPU's own
-pooled scores and bit-exact gathered rows.
+Every segment is compared with the oracle, the full-size workloads' too
+(the oracle computes one (sequence, KV head) at a time), besides properties
+checked on every segment: exact top-k of the GPU's own pooled scores and
+bit-exact gathered rows.
 """
 
 import json
@@ -18,7 +18,8 @@ import torch
 
 import oracle.kvsel_oracle as O
 import workloads as W
-from parity import check_against_oracle, check_scores, check_select_exact, reserved_mask, segments, to_np64
+from parity import (Guarded, check_against_oracle, check_scores, check_select_exact, compress_guarded, reserved_mask,
+                    segments, to_np64)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -40,13 +41,18 @@ def _say(msg):
 
 
 def _run(kv, spec, case, with_scores=True):
+    """kvsel_compress, then (optionally) kvsel_score on the same workspace,
+    every output and the workspace between guard bands (checked)."""
     p = kv.Problem(**W.problem_kwargs(spec))
     Q, K, V = (case[x].to(DEV) for x in "QKV")
-    out = kv.compress(p, Q, K, V, pooled=True)
+    out = compress_guarded(kv, p, Q, K, V, pooled=True)
     scores = None
     if with_scores:
-        scores = torch.empty(sum(spec.seq_lens) * spec.Hkv, dtype=torch.float32, device=DEV)
+        g = Guarded(DEV)
+        scores = g.empty(sum(spec.seq_lens) * spec.Hkv, torch.float32)
         kv.kvsel_score(p, Q, K, scores, out["ws"])
+        g.check()
+        out["guard"].check()
     torch.cuda.synchronize()
     return p, out, scores
 
@@ -92,16 +98,7 @@ def test_small_parity(kv, spec):
     assert st["max_rel"] < 1e-4, st
 
 
-# ---------------------------------------------------------------- full-size workloads
-SAMPLED = {
-    1: [(0, 0), (0, 3), (0, 7)],
-    2: [(0, 0), (0, 7)],
-    3: [(0, 0), (0, 5)],
-    4: [(0, 1), (3, 6)],
-    5: [(0, 0), (4, 3), (7, 7)],
-}
-
-
+# ---------------------------------------------------------------- full-size workloads, every segment
 @pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
 def test_config_parity(kv, i):
     spec = W.config(i)
@@ -109,12 +106,12 @@ def test_config_parity(kv, i):
     case = W.make_case(spec, layer=0, device=DEV)
     _say(f"config {i}: running kvsel_compress")
     _, out, scores = _run(kv, spec, case)
-    _say(f"config {i}: oracle on {SAMPLED[i]}")
+    _say(f"config {i}: oracle on all {spec.batch * spec.Hkv} segments")
     case_cpu = {k: v.cpu() for k, v in case.items()}
-    ref = _oracle(spec, case_cpu, heads=SAMPLED[i])
-    st = check_against_oracle(spec, case_cpu, out, ref, heads=SAMPLED[i], scores=scores)
+    ref = _oracle(spec, case_cpu)
+    st = check_against_oracle(spec, case_cpu, out, ref, scores=scores)
     _say(f"config {i}: {st}")
-    assert st["segments"] == len(SAMPLED[i])
+    assert st["segments"] == spec.batch * spec.Hkv
 
 
 @pytest.mark.parametrize("pool,width", [("max", 11), ("avg", 255)])
@@ -135,8 +132,9 @@ def test_config2_last_layer(kv):
     case = W.make_case(spec, layer=31, device=DEV)
     _, out, _ = _run(kv, spec, case, with_scores=False)
     case_cpu = {k: v.cpu() for k, v in case.items()}
-    ref = _oracle(spec, case_cpu, heads=[(0, 2)])
-    check_against_oracle(spec, case_cpu, out, ref, heads=[(0, 2)])
+    ref = _oracle(spec, case_cpu)
+    st = check_against_oracle(spec, case_cpu, out, ref)
+    assert st["segments"] == spec.batch * spec.Hkv
 
 
 # ---------------------------------------------------------------- entry points compose, determinism
@@ -149,16 +147,17 @@ def test_entry_points_compose_and_repeat(kv):
     again = kv.compress(p, Q, K, V)
     ws, offs = kv.kvsel_plan(p)
     n = sum(spec.seq_lens) * spec.Hkv
-    scores = torch.empty(n, device=DEV)
-    pooled = torch.empty(n, device=DEV)
-    idx = torch.empty(max(1, offs[-1]), dtype=torch.int32, device=DEV)
-    Ko = torch.empty(max(1, offs[-1]), 128, dtype=torch.bfloat16, device=DEV)
-    Vo = torch.empty_like(Ko)
-    wsb = torch.full((ws,), 0xAB, dtype=torch.uint8, device=DEV)  # arbitrary initial bytes are fine
+    g = Guarded(DEV)
+    scores = g.empty(n, torch.float32)
+    pooled = g.empty(n, torch.float32)
+    idx = g.empty(max(1, offs[-1]), torch.int32)
+    Ko = g.empty(max(1, offs[-1]) * 128, torch.bfloat16).view(-1, 128)
+    Vo = g.empty(max(1, offs[-1]) * 128, torch.bfloat16).view(-1, 128)
+    wsb = g.empty(ws, torch.uint8, fill=0xAB)  # arbitrary initial bytes are fine
     kv.kvsel_score(p, Q, K, scores, wsb)
     kv.kvsel_pool_topk(p, scores, pooled, idx, wsb)
     kv.kvsel_gather(p, idx, K, V, Ko, Vo)
-    torch.cuda.synchronize()
+    g.check()
     kept = offs[-1]
     assert torch.equal(full["idx"][:kept], idx[:kept])
     assert torch.equal(again["idx"][:kept], idx[:kept])
@@ -176,14 +175,15 @@ def test_two_passes_equal_score(kv):
         case = W.make_case(spec)
         Q, K = (case[x].to(DEV) for x in "QK")
         n = sum(spec.seq_lens) * spec.Hkv
-        one = torch.empty(n, device=DEV)
-        two = torch.empty(n, device=DEV)
+        g = Guarded(DEV)
+        one = g.empty(n, torch.float32)
+        two = g.empty(n, torch.float32)
         p = kv.Problem(**W.problem_kwargs(spec))
-        ws = torch.empty(kv.kvsel_plan(p)[0], dtype=torch.uint8, device=DEV)
+        ws = g.empty(kv.kvsel_plan(p)[0], torch.uint8)
         kv.kvsel_score(p, Q, K, one, ws)
         kv.kvsel_row_stats(p, Q, K, ws)
         kv.kvsel_score_from_stats(p, Q, K, two, ws)
-        torch.cuda.synchronize()
+        g.check()
         assert torch.equal(one, two), spec.name
 
 
@@ -232,10 +232,11 @@ def test_select_exact_on_given_scores(kv, kind, pool, kernel):
     ws, offs = kv.kvsel_plan(p)
     S = np.concatenate([_adversarial_scores(kind, L, rng) for L in lens for _ in range(Hkv)])
     scores = torch.from_numpy(S).to(DEV)
-    pooled = torch.empty_like(scores)
-    idx = torch.empty(offs[-1], dtype=torch.int32, device=DEV)
-    kv.kvsel_pool_topk(p, scores, pooled, idx, torch.empty(ws, dtype=torch.uint8, device=DEV))
-    torch.cuda.synchronize()
+    g = Guarded(DEV)
+    pooled = g.empty(scores.numel(), torch.float32)
+    idx = g.empty(offs[-1], torch.int32)
+    kv.kvsel_pool_topk(p, scores, pooled, idx, g.empty(ws, torch.uint8))
+    g.check()
     P = pooled.cpu().numpy()
     I = idx.cpu().numpy()
     spec = W.Spec("given", lens, Hq=2, Hkv=Hkv, pool=pool, pool_kernel=kernel, budgets=budgets)
@@ -266,10 +267,11 @@ def test_select_reserved_on_given_scores(kv, kind, sink, recent):
     ws, offs = kv.kvsel_plan(p)
     S = np.concatenate([_adversarial_scores(kind, L, rng) for L in lens for _ in range(Hkv)])
     scores = torch.from_numpy(S).to(DEV)
-    pooled = torch.empty_like(scores)
-    idx = torch.empty(offs[-1], dtype=torch.int32, device=DEV)
-    kv.kvsel_pool_topk(p, scores, pooled, idx, torch.empty(ws, dtype=torch.uint8, device=DEV))
-    torch.cuda.synchronize()
+    g = Guarded(DEV)
+    pooled = g.empty(scores.numel(), torch.float32)
+    idx = g.empty(offs[-1], torch.int32)
+    kv.kvsel_pool_topk(p, scores, pooled, idx, g.empty(ws, torch.uint8))
+    g.check()
     P = pooled.cpu().numpy()
     I = idx.cpu().numpy()
     spec = W.Spec("given", lens, Hq=2, Hkv=Hkv, pool="max", pool_kernel=7, budgets=budgets)
@@ -289,16 +291,15 @@ def test_deferkv_full_size(kv, make):
     32 prompt rows and the decode row, 16 sinks and 32 recent kept; with the
     per-head sum, and with the guide's mean query per group."""
     spec = make()
-    heads = [(0, 0), (0, 5)]
     _say(f"{spec.name}: generating")
     case = W.make_case(spec, layer=0, device=DEV)
     _, out, scores = _run(kv, spec, case)
-    _say(f"{spec.name}: oracle on {heads}")
+    _say(f"{spec.name}: oracle on every segment")
     case_cpu = {k: v.cpu() for k, v in case.items()}
-    ref = _oracle(spec, case_cpu, heads=heads)
-    st = check_against_oracle(spec, case_cpu, out, ref, heads=heads, scores=scores)
+    ref = _oracle(spec, case_cpu)
+    st = check_against_oracle(spec, case_cpu, out, ref, scores=scores)
     _say(f"{spec.name}: {st}")
-    assert st["segments"] == len(heads)
+    assert st["segments"] == spec.batch * spec.Hkv
 
 
 def test_exp_weights_closed_forms(kv):
@@ -313,9 +314,10 @@ def test_exp_weights_closed_forms(kv):
     def score(**kw):
         p = kv.Problem(**base, **kw)
         ws, _ = kv.kvsel_plan(p)
-        out = torch.empty(n, device=DEV)
-        kv.kvsel_score(p, Q, K, out, torch.empty(ws, dtype=torch.uint8, device=DEV))
-        torch.cuda.synchronize()
+        g = Guarded(DEV)
+        out = g.empty(n, torch.float32)
+        kv.kvsel_score(p, Q, K, out, g.empty(ws, torch.uint8))
+        g.check()
         return out.cpu().numpy().astype(np.float64)
 
     # prompt rows only: there the alpha weighting gives every row weight 1
@@ -323,12 +325,13 @@ def test_exp_weights_closed_forms(kv):
     p_alpha = kv.Problem(**base)
     p_exp0 = kv.Problem(**base, weighting="exp", lam=0.0)
     ws, _ = kv.kvsel_plan(p_alpha)
-    a = torch.empty(n, device=DEV)
-    e = torch.empty(n, device=DEV)
-    wsb = torch.empty(ws, dtype=torch.uint8, device=DEV)
+    g = Guarded(DEV)
+    a = g.empty(n, torch.float32)
+    e = g.empty(n, torch.float32)
+    wsb = g.empty(ws, torch.uint8)
     kv.kvsel_score(p_alpha, Qp, K, a, wsb)
     kv.kvsel_score(p_exp0, Qp, K, e, wsb)
-    torch.cuda.synchronize()
+    g.check()
     check_scores(8.0 * e.cpu().numpy().astype(np.float64), a.cpu().numpy().astype(np.float64), "lambda=0")
     # lambda huge: the decode row alone, which is alpha = 1
     big = score(has_decode=True, weighting="exp", lam=1000.0)
@@ -350,10 +353,11 @@ def test_gather_given_indices(kv):
     spec = W.Spec("given", lens, Hq=4, Hkv=Hkv, budgets=budgets)
     for (b, h, L, soff, ooff, keff) in segments(spec, offs):
         idx[ooff:ooff + keff] = rng.integers(-3, L + 3, keff)  # includes out-of-range entries
-    Ko = torch.full((offs[-1], 128), 7, dtype=torch.bfloat16, device=DEV)
-    Vo = torch.full_like(Ko, 7)
+    g = Guarded(DEV)
+    Ko = g.empty(offs[-1] * 128, torch.bfloat16, fill=7).view(-1, 128)
+    Vo = g.empty(offs[-1] * 128, torch.bfloat16, fill=7).view(-1, 128)
     kv.kvsel_gather(p, torch.from_numpy(idx).to(DEV), K.to(DEV), V.to(DEV), Ko, Vo)
-    torch.cuda.synchronize()
+    g.check()
     Ko, Vo = Ko.cpu(), Vo.cpu()
     starts = np.concatenate([[0], np.cumsum(lens)])
     for (b, h, L, soff, ooff, keff) in segments(spec, offs):

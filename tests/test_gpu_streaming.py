@@ -10,7 +10,7 @@ import torch
 
 import oracle.kvsel_oracle as O
 import workloads as W
-from parity import check_against_oracle, kth_value, reserved_mask, segments, to_np64
+from parity import check_against_oracle, compress_guarded, kth_value, reserved_mask, segments, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -32,14 +32,14 @@ def _say(msg):
 
 def _streamed(kv, spec, case, C):
     p = kv.Problem(**W.problem_kwargs(spec), stream_keys=C)
-    out = kv.compress(p, *(case[x].to(DEV) for x in "QKV"), pooled=False)
+    out = compress_guarded(kv, p, *(case[x].to(DEV) for x in "QKV"), pooled=False)
     torch.cuda.synchronize()
     return out
 
 
 def _whole(kv, spec, case):
     p = kv.Problem(**W.problem_kwargs(spec))
-    out = kv.compress(p, *(case[x].to(DEV) for x in "QKV"), pooled=True)
+    out = compress_guarded(kv, p, *(case[x].to(DEV) for x in "QKV"), pooled=True)
     torch.cuda.synchronize()
     return out
 
@@ -100,10 +100,9 @@ def test_streaming_full_size(kv):
     case = W.make_case(spec, layer=0, device=DEV)
     s_out = _streamed(kv, spec, case, 8192)
     d = _check_same_as_whole(spec, s_out, _whole(kv, spec, case))
-    heads = [(0, 0), (0, 6)]
     case_cpu = {k: v.cpu() for k, v in case.items()}
-    ref = O.compress(to_np64(case_cpu["Q"]), to_np64(case_cpu["K"]), to_np64(case_cpu["V"]), heads=heads,
+    ref = O.compress(to_np64(case_cpu["Q"]), to_np64(case_cpu["K"]), to_np64(case_cpu["V"]),
                      **W.oracle_kwargs(spec))
-    st = check_against_oracle(spec, case_cpu, {**s_out, "pooled": None}, ref, heads=heads)
+    st = check_against_oracle(spec, case_cpu, {**s_out, "pooled": None}, ref)
     _say(f"streaming full size: differs from whole-prefix at {d}; oracle {st}")
-    assert st["segments"] == len(heads)
+    assert st["segments"] == spec.batch * spec.Hkv

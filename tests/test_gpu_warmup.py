@@ -11,7 +11,7 @@ import torch
 
 import oracle.kvsel_oracle as O
 import workloads as W
-from parity import RTOL, check_finite, check_scores, to_np64
+from parity import RTOL, Guarded, check_finite, check_scores, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -36,14 +36,15 @@ def _profile(kv, spec, n_layers, pool="none", pool_kernel=1):
     kw.update(pool=pool, pool_kernel=pool_kernel)
     p = kv.Problem(**kw)
     ws_bytes, _ = kv.kvsel_plan(p)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
-    prof = torch.full((sum(spec.seq_lens),), float("nan"), device=DEV)  # every value must be written
+    g = Guarded(DEV)
+    ws = g.empty(ws_bytes, torch.uint8)
+    prof = g.empty(sum(spec.seq_lens), torch.float32, fill=float("nan"))  # every value must be written
     layers = []
     for layer in range(n_layers):
         case = W.make_case(spec, layer=layer, device=DEV)
         kv.kvsel_profile_layer(p, case["Q"], case["K"], prof, ws, accumulate=layer > 0)
         layers.append((to_np64(case["Q"]), to_np64(case["K"])))
-    torch.cuda.synchronize()
+    g.check()
     return p, ws, prof, layers
 
 
@@ -55,9 +56,10 @@ def _oracle_profile(spec, layers):
 
 
 def _tiers(kv, p, ws, prof, n_fast, n_mid):
-    tier = torch.full((prof.numel(),), 7, dtype=torch.int8, device=DEV)
+    g = Guarded(DEV)
+    tier = g.empty(prof.numel(), torch.int8, fill=7)
     kv.kvsel_tier_rank(p, prof, n_fast, n_mid, tier, ws)
-    torch.cuda.synchronize()
+    g.check()
     return tier.cpu().numpy()
 
 

@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import workloads as W
+from parity import Guarded
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -31,9 +32,10 @@ def _run_both(kv, spec):
     Q, K, V = (case[x].to(DEV) for x in "QKV")
     p = kv.Problem(**W.problem_kwargs(spec))
     ref = kv.compress(p, Q, K, V, pooled=True)
-    out = kv.alloc_outputs(p, DEV, pooled=True)
+    g = Guarded(DEV)
+    out = g.outputs(kv, p, pooled=True)
     kv.kvsel_compress_noalloc(p, Q, K, V, out["idx"], out["K_out"], out["V_out"], out["pooled"])
-    torch.cuda.synchronize()
+    g.check()
     kept = out["out_offsets"][-1]
     assert torch.equal(out["idx"][:kept], ref["idx"][:kept])
     assert torch.equal(out["K_out"][:kept], ref["K_out"][:kept])
