@@ -391,7 +391,7 @@ __device__ void tables_epilogue(const ScoreParams &p, float *red, int rs, uint32
 // carries a whole extra tile (the slowest wave sets every step's pace).
 // TAB (pass 2 only): the halo tile, pool and selection tables (see top).
 template <int PASS, int RT, bool SPLIT = false, bool TAB = false>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT > 1 ? 1 : 2))) void score_kernel(ScoreParams p, SegTable t) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 2 && RT == 1) ? 2 : SPLIT ? (RT > 2 ? 1 : 2) : RT > 1 ? 1 : 4))) void score_kernel(ScoreParams p, SegTable t) {
   extern __shared__ float red[];  // pass 2: [NW][rs] partial sums (TAB: then S by position)
 
   const int blk = blockIdx.x;
@@ -541,9 +541,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(RT > 1 ? 1 :
   // and its exp / sum work on the accumulators.  With PIPE, step t issues
   // tile t's MFMAs and then does tile t - 1's exp / sum work, which depends
   // only on registers, so the wave's VALU work runs while its matrix core
-  // works (two accumulator sets alternate); without PIPE (many row tiles per
-  // wave, where registers are short) both stages of tile t run in step t.
-  constexpr bool PIPE = RT <= 2;
+  // works (two accumulator sets alternate); without PIPE both stages of
+  // tile t run in step t.  PIPE is used where it measured faster: pass 2
+  // with one row tile per wave.
+  constexpr bool PIPE = PASS == 2 && RT == 1;  // measured: helps there, costs pass 1 and two-tile waves
   static_assert(!PIPE || PD % 2 == 0, "accumulator sets alternate with the slot parity");
   f32x16 accs[PIPE ? 2 : 1][RT];
   f32x4 saccs[PIPE ? 2 : 1];
