@@ -579,6 +579,7 @@ constexpr int RBP = kTabBlock;
 constexpr int CPB = CH / RBP;            // blocks per chunk
 constexpr int NB2 = kTabBins;
 constexpr int BPT = 16;                  // blocks per thread in the per-block scans
+constexpr int kRankCands = 512;          // at most this many candidates: tau by direct ranking
 constexpr int MAXB = BPT * NT;           // blocks per segment: 4096, so up to 2^20 positions
 static_assert(CPB == 8 && BPT == 2 * CPB, "a chunk's blocks are one half of a thread's share");
 static_assert(NB2 == 8 * NT, "eight bins per thread");
@@ -586,7 +587,7 @@ static_assert((int64_t)MAXB * RBP >= (int64_t)MAXCH * CH, "every supported seque
 
 template <bool GATHER>
 __global__ __launch_bounds__(NT) void select_block_kernel(SelectParams p, SegTable t) {
-  __shared__ uint32_t candk[MAXC];       // keys of bin b1
+  __shared__ __attribute__((aligned(16))) uint32_t candk[MAXC];  // keys of bin b1
   __shared__ uint16_t candb[MAXC];       // their blocks
   __shared__ uint32_t hist[2048];
   // Per-block arrays in dynamic LDS, sized for the launch's longest sequence.
@@ -743,43 +744,77 @@ __global__ __launch_bounds__(NT) void select_block_kernel(SelectParams p, SegTab
       }
     };
 
-    // ---- radix rounds over the candidates' keys: bits [21, 32), [10, 21), [0, 10)
-    int rest = need;
-    uint32_t pre = 0u;
-    for (int hi = 32, lo = 21;; hi = lo, lo = (lo > 11) ? lo - 11 : 0) {
-      for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
+    // ---- tau, the need-th largest candidate key, and take_eq, how many of
+    // the keys equal to it are kept (the lowest-positioned ones).  Few
+    // candidates (held in LDS): each candidate's count of larger and equal
+    // keys, by direct comparison with all of them (every thread reads the
+    // same LDS words, which the LDS broadcasts); the candidate whose larger
+    // count is below need and whose larger-or-equal count reaches it holds
+    // tau (every such candidate holds the same key).  Otherwise radix rounds
+    // over the candidates' keys: bits [21, 32), [10, 21), [0, 10).
+    uint32_t tau;
+    int take_eq;
+    if (in_lds && m <= kRankCands) {
+      for (int i = m; i < ((m + 3) & ~3); ++i)  // pad to whole uint4 reads with keys below every key
+        if (tid == 0) candk[i] = 0u;
       __syncthreads();
-      const uint32_t dmask = (1u << (hi - lo)) - 1u;
-      visit([&](uint32_t k, int) {
-        if (hi == 32 || (k >> hi) == pre) atomicAdd(&hist[(k >> lo) & dmask], 1u);
-      });
-      __syncthreads();
-      // The bin holding the rest-th largest: thread tid owns bins [8 tid, 8 tid + 8).
-      uint32_t hc[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) hc[u] = hist[8 * tid + u];
-      int own = 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) own += (int)hc[u];
-      int tot;
-      const int ex = block_exscan(own, tmp, tot);
-      int ab = tot - ex - own;  // keys in bins above this thread's
-#pragma unroll
-      for (int u = 7; u >= 0; --u) {
-        if (ab < rest && ab + (int)hc[u] >= rest) {
-          sh[2] = 8 * tid + u;
-          sh[3] = ab;
+      for (int i = tid; i < m; i += NT) {
+        const uint32_t ki = candk[i];
+        int gt = 0, eq = 0;
+        const uint4 *c4 = reinterpret_cast<const uint4 *>(candk);
+        for (int j = 0; j < (m + 3) >> 2; ++j) {
+          const uint4 kj = c4[j];
+          gt += (kj.x > ki) + (kj.y > ki) + (kj.z > ki) + (kj.w > ki);
+          eq += (kj.x == ki) + (kj.y == ki) + (kj.z == ki) + (kj.w == ki);
         }
-        ab += (int)hc[u];
+        eq -= (ki == 0u) ? (((m + 3) & ~3) - m) : 0;  // the padding keys are 0
+        if (gt < need && gt + eq >= need) {
+          sh[2] = (int)ki;
+          sh[3] = need - gt;
+        }
       }
       __syncthreads();
-      rest -= sh[3];
-      pre = (pre << (hi - lo)) | (uint32_t)sh[2];
-      __syncthreads();
-      if (lo == 0) break;
+      tau = (uint32_t)sh[2];
+      take_eq = sh[3];
+    } else {
+      // ---- radix rounds over the candidates' keys: bits [21, 32), [10, 21), [0, 10)
+      int rest = need;
+      uint32_t pre = 0u;
+      for (int hi = 32, lo = 21;; hi = lo, lo = (lo > 11) ? lo - 11 : 0) {
+        for (int i = tid; i < 2048; i += NT) hist[i] = 0u;
+        __syncthreads();
+        const uint32_t dmask = (1u << (hi - lo)) - 1u;
+        visit([&](uint32_t k, int) {
+          if (hi == 32 || (k >> hi) == pre) atomicAdd(&hist[(k >> lo) & dmask], 1u);
+        });
+        __syncthreads();
+        // The bin holding the rest-th largest: thread tid owns bins [8 tid, 8 tid + 8).
+        uint32_t hc[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) hc[u] = hist[8 * tid + u];
+        int own = 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) own += (int)hc[u];
+        int tot;
+        const int ex = block_exscan(own, tmp, tot);
+        int ab = tot - ex - own;  // keys in bins above this thread's
+#pragma unroll
+        for (int u = 7; u >= 0; --u) {
+          if (ab < rest && ab + (int)hc[u] >= rest) {
+            sh[2] = 8 * tid + u;
+            sh[3] = ab;
+          }
+          ab += (int)hc[u];
+        }
+        __syncthreads();
+        rest -= sh[3];
+        pre = (pre << (hi - lo)) | (uint32_t)sh[2];
+        __syncthreads();
+        if (lo == 0) break;
+      }
+      tau = pre;
+      take_eq = rest;
     }
-    const uint32_t tau = pre;
-    const int take_eq = rest;  // keys equal to tau to keep (the lowest-positioned), >= 1
 
     // ---- per-block kept counts; this chunk's first output slot and its
     // share of the keys equal to tau
