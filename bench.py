@@ -572,10 +572,12 @@ def main():
         stage[name] = {k: (v * 1e3 / len(cases) if k != "n" else v) for k, v in st.items()}  # us per layer
     del ws0
     stage_us = {k: v["median"] for k, v in stage.items()}
-    # The two score kernels' launch times: pass 1 alone, and pass 2 with
-    # tables as the difference (its empty selection launch stays in it).
+    # The chain's three kernels' launch times: pass 1 alone, pass 2 with
+    # tables as the difference (its empty selection launch stays in it), and
+    # the selection as the rest of the whole step.
     t_pass1 = stage_us["pass1"]
     t_pass2 = stage_us["pass1+2t"] - stage_us["pass1"]
+    t_select = stage_us["compress"] - stage_us["pass1+2t"]
     traffic = counted_traffic() or {}
     kernels = {
         "pass1": {
@@ -593,6 +595,13 @@ def main():
             "algorithmic_bytes": ab["K"] + ab["Q"] + ab["scores_out"] + sum(spec.seq_lens) * spec.Hkv * 20,
             "what_bytes": "K + Q read; pooled scores (4 B) and selection tables (20 B) per position written",
             "traffic": (traffic.get("pass2_tables") or {}).get("bytes_per_launch"),
+        },
+        "select_block": {
+            "kernel": "selection from the tables, ordered compaction and K/V gather (select_block_kernel<true>)",
+            "us_per_launch": t_select,
+            "algorithmic_bytes": ab["path"] - ab["K"] - ab["Q"],
+            "what_bytes": "kept K and V rows read and written, kept indices written",
+            "traffic": (traffic.get("select_block") or {}).get("bytes_per_launch"),
         },
     }
     for k in kernels.values():
