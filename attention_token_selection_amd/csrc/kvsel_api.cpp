@@ -55,7 +55,17 @@ struct Plan {
   bool fused = false;
   int kb2t = 0, ntab_max = 0;
   size_t off_thist = 0, off_ttab = 0, off_tbucket = 0;
+  // The fused streaming form (pools up to 2 kPoolHalo + 1 wide, running
+  // rows up to kStreamRowMax): pass 2's key block per step, and two rows of
+  // order keys and two of running positions per segment.
+  bool sfused = false;
+  int kb2s = 0;
+  size_t off_skeys[2] = {0, 0}, off_spos[2] = {0, 0};
 };
+
+// Pass-1 block states per segment in the fused streaming form: a bound
+// independent of the prefix length.
+constexpr int kStreamStates = 64;
 
 // Test hook read from the environment: KVSEL_UNFUSED=1 sends kvsel_compress
 // through pass 2 without tables, then the separate pool and selection
@@ -89,6 +99,34 @@ kvsel_status plan_streaming(const kvsel_problem *p, Plan &P) {
   P.halo = (P.pool == KVSEL_POOL_NONE) ? 0 : (P.pool_kernel - 1) / 2;
   int32_t kmax = 0;
   for (int32_t k : P.keff) kmax = std::max(kmax, k);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  const int kslot4 = (kmax + 3) / 4 * 4;
+  P.sfused = P.halo <= kPoolHalo && (int64_t)kslot4 + P.stream <= kStreamRowMax && !env_unfused();
+  if (P.sfused) {
+    // Pass 1 runs once over the whole prefix with at most kStreamStates
+    // block states per segment: blocks of the whole-prefix size, or longer
+    // when the prefix needs more than kStreamStates of them.
+    const int64_t span = (P.Lmax + kStreamStates - 1) / kStreamStates;
+    P.kb1 = (int)std::max<int64_t>(P.kb1, (span + kKeyTile - 1) / kKeyTile * kKeyTile);
+    P.nblk1_max = kStreamStates;  // the states' stride: the same workspace for every prefix length
+    P.kb2s = auto_key_block((int64_t)P.stream * P.B * P.Hkv, 2048);
+    P.kslot = kslot4;
+    P.lv = kslot4 + P.stream;
+    P.off_partials = take(nseg * P.nblk1_max * P.Rpad * sizeof(float2));
+    P.off_run = take(nseg * P.Rpad * sizeof(float2));
+    for (int i = 0; i < 2; ++i) P.off_skeys[i] = take(nseg * P.lv * sizeof(uint32_t));
+    for (int i = 0; i < 2; ++i) P.off_spos[i] = take(nseg * std::max(4, P.kslot) * sizeof(int32_t));
+    P.off_qmean = off;
+    if (P.gqa == KVSEL_GQA_MEAN_QUERY) take((size_t)P.B * P.wp * P.Hkv * p->d * sizeof(uint16_t));
+    P.off_scores = P.off_pooled = 0;  // no whole-prefix buffers in this form
+    P.ws_bytes = off;
+    return KVSEL_OK;
+  }
   P.kslot = kmax;
   const int64_t lv = (int64_t)P.kslot + P.stream;
   if (lv > (int64_t)kMaxChunks * kSelectChunk)
@@ -103,12 +141,6 @@ kvsel_status plan_streaming(const kvsel_problem *p, Plan &P) {
   P.nblk1_c = (P.stream + P.kb1 - 1) / P.kb1;
   P.nblk1_max = P.nblk1_c;
   P.nchunk_max = (P.lv + kSelectChunk - 1) / kSelectChunk;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t at = off;
-    off = align_up(off + bytes, 256);
-    return at;
-  };
   P.off_partials = take(nseg * P.nblk1_c * P.Rpad * sizeof(float2));
   P.off_run = take(nseg * P.Rpad * sizeof(float2));
   P.off_sbuf = take(nseg * ((size_t)P.stream + 2 * P.halo) * sizeof(float));
@@ -457,6 +489,22 @@ kvsel_status run_gather(const Plan &P, const int32_t *idx, const void *K, const 
 bool any_kept(const Plan &P) { return P.out_off.back() > 0; }
 
 
+// The pool and reserved positions of pass 2 with the pool, and the sum of
+// S over a segment's positions.
+void set_pool_params(const Plan &P, ScoreParams &sp) {
+  sp.pool = P.pool;
+  sp.pool_r = (P.pool == KVSEL_POOL_NONE) ? 0 : (P.pool_kernel - 1) / 2;
+  sp.pool_width = (float)P.pool_kernel;
+  sp.sink = P.sink;
+  sp.recent = P.recent;
+  // sum of the row weights: 1 each, or 1 - alpha and alpha with a decode
+  // row, or the exponential weights normalised to 1
+  double cw = P.w;
+  if (P.weighting == KVSEL_WEIGHT_EXP) cw = 1.0;
+  else if (P.has_decode) cw = (1.0 - P.alpha) * P.w + P.alpha;
+  sp.wsum = (float)(P.G * cw);
+}
+
 kvsel_status run_compress_fused(const Plan &P, const void *Q, const void *K, const void *V, int32_t *idx, void *K_out,
                                 void *V_out, float *pooled, char *ws, hipStream_t st) {
   uint32_t *seg_hist = reinterpret_cast<uint32_t *>(ws + P.off_thist);
@@ -468,19 +516,7 @@ kvsel_status run_compress_fused(const Plan &P, const void *Q, const void *K, con
   sp.bucket = reinterpret_cast<uint32_t *>(ws + P.off_tbucket);
   sp.seg_hist = seg_hist;
   sp.ntab_max = P.ntab_max;
-  sp.pool = P.pool;
-  sp.pool_r = (P.pool == KVSEL_POOL_NONE) ? 0 : (P.pool_kernel - 1) / 2;
-  sp.pool_width = (float)P.pool_kernel;
-  sp.sink = P.sink;
-  sp.recent = P.recent;
-  {
-    // sum of the row weights: 1 each, or 1 - alpha and alpha with a decode
-    // row, or the exponential weights normalised to 1
-    double cw = P.w;
-    if (P.weighting == KVSEL_WEIGHT_EXP) cw = 1.0;
-    else if (P.has_decode) cw = (1.0 - P.alpha) * P.w + P.alpha;
-    sp.wsum = (float)(P.G * cw);
-  }
+  set_pool_params(P, sp);
 
   SelectParams sel;
   std::memset(&sel, 0, sizeof(sel));
@@ -649,6 +685,72 @@ kvsel_status run_compress_streaming(const Plan &P, const void *Q, const void *K,
   return any_kept(P) ? run_gather(P, idx, K, V, K_out, V_out, st) : KVSEL_OK;
 }
 
+// The fused streaming form: pass 1 once over the whole prefix; then per
+// step of C keys, pass 2 with the pool writes the step's order keys behind
+// the running ones and one selection launch keeps the best keff of each
+// row; the last step's selection writes idx, and the gather follows.
+kvsel_status run_compress_stream_fused(const Plan &P, const void *Q, const void *K, const void *V, int32_t *idx,
+                                       void *K_out, void *V_out, char *ws, hipStream_t st) {
+  kvsel_status s = run_row_stats(P, Q, K, ws, st);  // (and the mean queries)
+  if (s != KVSEL_OK) return s;
+  ScoreParams sp = score_params(P, Q, K, nullptr, ws);
+  // The block states merged once into one state per row, which every step's
+  // pass 2 then takes as its only block state.
+  float2 *run = reinterpret_cast<float2 *>(ws + P.off_run);
+  sp.key_block = P.kb1;
+  s = for_each_group(P, [&](const SegTable &t, int64_t) {
+    hipError_t e = launch_stream_stats(sp, t, run, 1, st);
+    if (e != hipSuccess) return hip_fail(e, "row statistics merge launch");
+    return KVSEL_OK;
+  });
+  if (s != KVSEL_OK) return s;
+  sp.partials = run;
+  sp.nblk1_max = 1;
+  sp.stat_block = 1 << 30;
+  set_pool_params(P, sp);
+  sp.step_stride = P.lv;
+  sp.key_block = P.kb2s;
+  uint32_t *keys[2];
+  int32_t *pos[2];
+  for (int i = 0; i < 2; ++i) {
+    keys[i] = reinterpret_cast<uint32_t *>(ws + P.off_skeys[i]);
+    pos[i] = reinterpret_cast<int32_t *>(ws + P.off_spos[i]);
+  }
+  StreamSelectParams q;
+  std::memset(&q, 0, sizeof(q));
+  q.idx = idx;
+  q.lv = P.lv;
+  q.kslot = P.kslot;
+  q.stream = P.stream;
+  q.Hkv = P.Hkv;
+  q.wsum = sp.wsum;
+  s = for_each_group(P, [&](const SegTable &t, int64_t lmax) {
+    const int nsteps = (int)((lmax + P.stream - 1) / P.stream);
+    for (int c = 0; c < nsteps; ++c) {
+      const int c0 = c * P.stream;
+      sp.key_begin = c0;
+      sp.key_end = c0 + P.stream;
+      sp.step_keys = keys[c & 1] + P.kslot;
+      sp.step_origin = c0;
+      const int64_t hi = std::min<int64_t>(lmax, (int64_t)c0 + P.stream);
+      hipError_t e = launch_score_pass2_keys(sp, t, (int)((hi - c0 + P.kb2s - 1) / P.kb2s), st);
+      if (e != hipSuccess) return hip_fail(e, "score pass 2 launch");
+      if (t.kmax <= 0) continue;  // no segment of the group keeps a row
+      q.keys_in = keys[c & 1];
+      q.pos_in = pos[c & 1];
+      q.keys_out = keys[(c + 1) & 1];
+      q.pos_out = pos[(c + 1) & 1];
+      q.c0 = c0;
+      q.last = (c == nsteps - 1) ? 1 : 0;
+      e = launch_stream_select(q, t, st);
+      if (e != hipSuccess) return hip_fail(e, "streaming selection launch");
+    }
+    return KVSEL_OK;
+  });
+  if (s != KVSEL_OK) return s;
+  return any_kept(P) ? run_gather(P, idx, K, V, K_out, V_out, st) : KVSEL_OK;
+}
+
 kvsel_status reject_streaming(const Plan &P, const char *fn) {
   if (P.stream > 0)
     return fail(KVSEL_EINVAL, std::string(fn) + " needs whole-prefix buffers; stream_keys applies to kvsel_compress only");
@@ -781,6 +883,7 @@ KVSEL_API kvsel_status kvsel_compress(const kvsel_problem *p, const void *Q, con
   if (s != KVSEL_OK) return s;
   char *wsb = static_cast<char *>(ws);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (P.stream > 0 && P.sfused) return run_compress_stream_fused(P, Q, K, V, idx, K_out, V_out, wsb, st);
   if (P.stream > 0) return run_compress_streaming(P, Q, K, V, idx, K_out, V_out, wsb, st);
   float *scores = reinterpret_cast<float *>(wsb + P.off_scores);
   float *pool_buf = pooled ? pooled : reinterpret_cast<float *>(wsb + P.off_pooled);

@@ -76,6 +76,12 @@ struct ScoreParams {
   float pool_width;
   int sink, recent;
   float wsum;                   // sum of S over a segment's positions: G * sum_r c_r
+  // Pass 2 with the pool in the streaming form of kvsel_compress (tab null):
+  // the order keys of the pooled scores (select_key) of positions
+  // step_origin onwards go to step_keys + seg * step_stride.
+  uint32_t *step_keys;
+  int64_t step_stride;
+  int step_origin;
 };
 
 // The mean query of every (sequence, observation row, KV head): the G query
@@ -147,6 +153,23 @@ struct StreamParams {
   int sink, recent;
 };
 
+// The running top-k of the streaming form, one workgroup per segment: a
+// row of lv order keys per segment holds the running set in slots
+// [0, kslot) (its first min(keff, keys before c0) valid, positions in
+// pos_in) and the step's keys in [kslot, kslot + stream) (positions c0 ..);
+// the best keff of the valid ones, in slot order, become the next running
+// set (keys_out, pos_out) or, at the last step, the result (idx).
+struct StreamSelectParams {
+  const uint32_t *keys_in;  // [nseg][lv]
+  const int32_t *pos_in;    // [nseg][kslot]
+  uint32_t *keys_out;       // [nseg][lv]: slots [0, kslot) written
+  int32_t *pos_out;         // [nseg][kslot]
+  int32_t *idx;             // last step: the public layout (SegTable::out_off)
+  int lv, kslot, stream, c0, Hkv;
+  float wsum;               // sum of S over a segment's positions (the first digit's centre)
+  int last;                 // 1: write idx instead of keys_out / pos_out
+};
+
 struct GatherParams {
   const int32_t *idx;
   const uint4 *K;   // rows of d bf16 = 16 x uint4
@@ -169,6 +192,12 @@ hipError_t launch_score_pass2(const ScoreParams &p, const SegTable &t, int nblk,
 // Pass 2 with the pool and the selection tables (p.pooled, p.tab, ...);
 // key_block a multiple of kTabBlock, pool radius <= kPoolHalo.
 hipError_t launch_score_pass2_tables(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s);
+// Pass 2 with the pool, writing the pooled scores' order keys
+// (p.step_keys); key_block a multiple of kKeyTile, pool radius <= kPoolHalo.
+hipError_t launch_score_pass2_keys(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s);
+hipError_t launch_stream_select(const StreamSelectParams &p, const SegTable &t, hipStream_t s);
+// Largest row (kslot + stream) launch_stream_select takes.
+constexpr int kStreamRowMax = 32768;
 hipError_t launch_stream_stats(const ScoreParams &p, const SegTable &t, float2 *run, int first, hipStream_t s);
 hipError_t launch_stream_init(const StreamParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_stream_pool(const StreamParams &p, const SegTable &t, hipStream_t s);

@@ -41,7 +41,9 @@
 // kTabBlock positions, counting-sorts the positions by a first digit of
 // their order key: the exclusive prefix of the digit histogram, the keys
 // grouped by digit, and the histogram added to the segment's.  The
-// selection launch finishes the top-k from these tables.
+// selection launch finishes the top-k from these tables.  In the streaming
+// form the epilogue stops after the pool and writes each pooled score's
+// order key, for the running top-k, in place of the tables.
 //
 // The first digit.  A segment's scores sum to W = G * sum_r c_r, so they
 // centre near the mean W / L; the digit counts steps of 2^16 in the order
@@ -333,7 +335,12 @@ __device__ void tables_epilogue(const ScoreParams &p, float *red, int rs, uint32
         for (int j = -r; j <= r; ++j) sum += c[j];
         P = sum / p.pool_width;
       }
-      p.pooled[segbase + kb0 + x] = P;
+      if (p.pooled) p.pooled[segbase + kb0 + x] = P;
+    }
+    if (p.step_keys) {
+      // the streaming form: the pooled scores' order keys, no tables
+      if (x < n) p.step_keys[(int64_t)seg * p.step_stride + (kb0 + x - p.step_origin)] = select_key(P, kb0 + x, L, p.sink, p.recent);
+      continue;
     }
 
     // ---- counting sort of the table block by first digit; the segment
@@ -786,7 +793,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 2 &
 // The streaming form's fold (TideKV §4.2 with a bounded workspace): the
 // block states of the step's keys [key_begin, key_end) merged, in a fixed
 // order, into the running state `run` of each row (its first step starts
-// it).  Workgroup (row group of 16, segment): sixteen threads share a row,
+// it); the fused streaming form merges all of a segment's block states at
+// once this way, so that its steps' pass 2 each read one state per row.
+// Workgroup (row group of 16, segment): sixteen threads share a row,
 // each merging every sixteenth block with 16 loads in flight; the shares
 // are combined in a fixed order through LDS.
 constexpr int MERGE_ROWS = 16;
@@ -870,7 +879,15 @@ hipError_t launch_score_pass2(const ScoreParams &p, const SegTable &t, int nblk,
 
 hipError_t launch_score_pass2_tables(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
   if (p.key_block % kTabBlock != 0 || p.pool_r < 0 || p.pool_r > kPoolHalo || !p.pooled || !p.tab || !p.bucket ||
-      !p.seg_hist)
+      !p.seg_hist || p.step_keys)
+    return hipErrorInvalidValue;
+  const size_t rs = (size_t)p.key_block + 2 * kPoolHalo;
+  return launch_pass<2, true>(p, t, nblk, s, (NW + 1) * rs * sizeof(float));
+}
+
+hipError_t launch_score_pass2_keys(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
+  if (p.key_block <= 0 || p.key_block % kKeyTile != 0 || p.pool_r < 0 || p.pool_r > kPoolHalo || !p.step_keys ||
+      p.tab || p.pooled || p.scores || p.step_stride <= 0)
     return hipErrorInvalidValue;
   const size_t rs = (size_t)p.key_block + 2 * kPoolHalo;
   return launch_pass<2, true>(p, t, nblk, s, (NW + 1) * rs * sizeof(float));

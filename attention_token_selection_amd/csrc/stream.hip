@@ -9,7 +9,14 @@
 // positions (sinks, recent window) enter with +inf, above every score;
 // unused slots hold -inf and are never kept (a step keeps at most as many
 // slots as hold candidates).
+//
+// The fused streaming form (pools up to 2 kPoolHalo + 1 wide) keeps the
+// running set in a row of order keys instead: pass 2 with the pool writes
+// each step's keys behind the running ones, and stream_select_kernel, one
+// workgroup per segment with every key of the row in registers, picks the
+// best keff in one launch per step (see there).
 #include "kvsel_internal.h"
+#include "kvsel_device.h"
 
 namespace kvsel {
 namespace {
@@ -83,7 +90,248 @@ __global__ __launch_bounds__(NT) void stream_final_kernel(StreamParams p, SegTab
   if (j < t.keff[sl]) idx[t.out_off[sl] + j] = p.pos_in[(int64_t)seg * p.kslot + j];
 }
 
+// ---------------------------------------------------------------- fused running top-k
+constexpr int ST = 1024;       // threads of stream_select_kernel
+constexpr int SW = ST / 64;    // its waves
+constexpr int kRankMax = 512;  // candidates of the threshold bin ranked directly
+
+// Exclusive prefix sum over the workgroup; also returns the total.
+__device__ inline uint32_t exscan_st(uint32_t v, uint32_t *tmp, uint32_t &total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) tmp[wid] = x;
+  __syncthreads();
+  uint32_t before = 0u, tot = 0u;
+#pragma unroll
+  for (int i = 0; i < SW; ++i) {
+    const uint32_t s = tmp[i];
+    before += (i < wid) ? s : 0u;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return before + x - v;
+}
+
+// One step of the running top-k of one segment (TideKV §4.2, streaming
+// form): the best keep = min(keff, keys seen) of the row's valid keys, ties
+// to the lower slot (the lower position: running slots hold ascending
+// positions, all before the step's).  Thread tid holds slots
+// [IPT tid, IPT tid + IPT) in registers.  The threshold key tau is found as
+// in the whole-prefix selection: the bin b1 of the keep-th largest key by
+// the first digit (steps of 2^16 from the key of the mean score), then tau
+// among the keys of bin b1, by direct ranking when at most kRankMax, else by
+// three radix rounds (11 + 11 + 10 bits); then one ordered compaction.
+template <int IPT>
+__global__ __launch_bounds__(ST) void stream_select_kernel(StreamSelectParams p, SegTable t) {
+  static_assert(IPT % 4 == 0 && IPT <= 32, "whole uint4 loads; one validity bit per slot");
+  __shared__ uint32_t hist[kTabBins];
+  __shared__ __attribute__((aligned(16))) uint32_t cand[kRankMax];
+  __shared__ uint32_t tmp[SW];
+  __shared__ int sh[5];
+  const int sl = blockIdx.x;
+  const int sb = sl / p.Hkv;
+  const int seg = t.seg0 + sl;
+  const int L = (int)(t.key_off[sb + 1] - t.key_off[sb]);
+  const int keff = t.keff[sl];
+  if (keff <= 0) return;  // the whole workgroup leaves together
+  const int n_in = min(keff, min(L, p.c0));          // running keys
+  const int m = max(0, min(p.stream, L - p.c0));     // this step's keys
+  const int keep = min(keff, n_in + m);
+  const int tid = threadIdx.x;
+  const int i0 = tid * IPT;
+
+  // ---- the thread's slots (past the row: a clamped re-read, invalid)
+  const uint32_t *row = p.keys_in + (int64_t)seg * p.lv;
+  uint32_t k[IPT];
+#pragma unroll
+  for (int j = 0; j < IPT; j += 4) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(row + min(i0 + j, p.lv - 4));
+    k[j] = u.x;
+    k[j + 1] = u.y;
+    k[j + 2] = u.z;
+    k[j + 3] = u.w;
+  }
+  uint32_t vm = 0u;  // bit j: slot i0 + j holds a key
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const int i = i0 + j;
+    vm |= (i < n_in || (i >= p.kslot && i < p.kslot + m)) ? (1u << j) : 0u;
+  }
+
+  // ---- tau and take_eq (keys equal to tau to keep, the first in slot
+  // order); keeping every valid key: tau = 0, below every valid key
+  uint32_t tau = 0u;
+  int take_eq = 0;
+  if (keep < n_in + m) {
+    const uint32_t centre = order_key(p.wsum / (float)L);
+    auto digit = [&](uint32_t key) {
+      const int64_t rel = ((int64_t)key - (int64_t)centre) >> kTabDigitShift;
+      return (int)min<int64_t>(kTabBins - 1, max<int64_t>(0, rel + kTabBins / 2));
+    };
+    for (int i = tid; i < kTabBins; i += ST) hist[i] = 0u;
+    if (tid == 0) sh[2] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < IPT; ++j)
+      if ((vm >> j) & 1u) atomicAdd(&hist[digit(k[j])], 1u);
+    __syncthreads();
+    // b1: thread tid owns bins 2 tid, 2 tid + 1
+    const uint32_t h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
+    uint32_t tot;
+    uint32_t below = exscan_st(h0 + h1, tmp, tot);  // keys in lower bins
+    {
+      const int ge0 = (int)(tot - below);  // keys in bins >= 2 tid
+      const int ge1 = ge0 - (int)h0;       // ... >= 2 tid + 1
+      const int ge2 = ge1 - (int)h1;       // ... >= 2 tid + 2
+      if (ge0 >= keep && ge1 < keep) {
+        sh[0] = 2 * tid;
+        sh[1] = ge1;
+      }
+      if (ge1 >= keep && ge2 < keep) {
+        sh[0] = 2 * tid + 1;
+        sh[1] = ge2;
+      }
+    }
+    __syncthreads();
+    const int b1 = sh[0];
+    int rest = keep - sh[1];  // keys of bin b1 to keep, >= 1
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      if (((vm >> j) & 1u) && digit(k[j]) == b1) {
+        const int c = atomicAdd(&sh[2], 1);
+        if (c < kRankMax) cand[c] = k[j];
+      }
+    }
+    __syncthreads();
+    const int mc = sh[2];  // keys in bin b1
+    if (mc <= kRankMax) {
+      // each candidate's count of larger and equal candidates; the one whose
+      // larger count is below rest and larger-or-equal count reaches it is tau
+      const int m4 = (mc + 3) & ~3;
+      if (tid < m4 - mc) cand[mc + tid] = 0u;  // padding below every key
+      __syncthreads();
+      for (int i = tid; i < mc; i += ST) {
+        const uint32_t ki = cand[i];
+        int gt = 0, eq = 0;
+        const uint4 *c4 = reinterpret_cast<const uint4 *>(cand);
+        for (int q = 0; q < (m4 >> 2); ++q) {
+          const uint4 kq = c4[q];
+          gt += (kq.x > ki) + (kq.y > ki) + (kq.z > ki) + (kq.w > ki);
+          eq += (kq.x == ki) + (kq.y == ki) + (kq.z == ki) + (kq.w == ki);
+        }
+        eq -= (ki == 0u) ? (m4 - mc) : 0;  // the padding
+        if (gt < rest && gt + eq >= rest) {
+          sh[3] = (int)ki;
+          sh[4] = rest - gt;
+        }
+      }
+      __syncthreads();
+      tau = (uint32_t)sh[3];
+      take_eq = sh[4];
+    } else {
+      uint32_t pre = 0u;
+      for (int hi = 32, lo = 21;; hi = lo, lo = (lo > 11) ? lo - 11 : 0) {
+        for (int i = tid; i < kTabBins; i += ST) hist[i] = 0u;
+        __syncthreads();
+        const uint32_t dmask = (1u << (hi - lo)) - 1u;
+#pragma unroll
+        for (int j = 0; j < IPT; ++j) {
+          if (((vm >> j) & 1u) && digit(k[j]) == b1 && (hi == 32 || (k[j] >> hi) == pre))
+            atomicAdd(&hist[(k[j] >> lo) & dmask], 1u);
+        }
+        __syncthreads();
+        const uint32_t g0 = hist[2 * tid], g1 = hist[2 * tid + 1];
+        uint32_t gt2;
+        const uint32_t ex = exscan_st(g0 + g1, tmp, gt2);
+        int ab = (int)(gt2 - ex - g0 - g1);  // keys in bins above this thread's
+        if (ab < rest && ab + (int)g1 >= rest) {
+          sh[3] = 2 * tid + 1;
+          sh[4] = ab;
+        }
+        ab += (int)g1;
+        if (ab < rest && ab + (int)g0 >= rest) {
+          sh[3] = 2 * tid;
+          sh[4] = ab;
+        }
+        __syncthreads();
+        rest -= sh[4];
+        pre = (pre << (hi - lo)) | (uint32_t)sh[3];
+        __syncthreads();
+        if (lo == 0) break;
+      }
+      tau = pre;
+      take_eq = rest;
+    }
+  }
+
+  // ---- ordered compaction: slot order is position order.  The running
+  // slots' positions are loaded for every slot first (clamped, unused past
+  // the running slots), so that the loads go out together.
+  int32_t pv[IPT];
+  if (p.kslot >= 4) {
+    const int32_t *pin = p.pos_in + (int64_t)seg * p.kslot;
+#pragma unroll
+    for (int j = 0; j < IPT; j += 4) {
+      const int4 u = *reinterpret_cast<const int4 *>(pin + min(i0 + j, p.kslot - 4));
+      pv[j] = u.x;
+      pv[j + 1] = u.y;
+      pv[j + 2] = u.z;
+      pv[j + 3] = u.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) pv[j] = 0;
+  }
+  uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const bool v = (vm >> j) & 1u;
+    gt += (v && k[j] > tau) ? 1u : 0u;
+    eq += (v && k[j] == tau) ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t packed = exscan_st((gt << 16) | eq, tmp, tot);  // both counts stay below 2^16
+  int eb = (int)(packed & 0xffffu);  // keys equal to tau in earlier threads' slots
+  int slot = (int)(packed >> 16) + min(eb, take_eq);
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const int i = i0 + j;
+    const bool v = (vm >> j) & 1u;
+    const bool is_eq = v && k[j] == tau;
+    const bool kp = (v && k[j] > tau) || (is_eq && eb < take_eq);
+    if (kp && slot < keep) {
+      const int pos = (i < p.kslot) ? pv[j] : p.c0 + (i - p.kslot);
+      if (p.last) {
+        p.idx[t.out_off[sl] + slot] = pos;
+      } else {
+        p.keys_out[(int64_t)seg * p.lv + slot] = k[j];
+        p.pos_out[(int64_t)seg * p.kslot + slot] = pos;
+      }
+    }
+    slot += kp ? 1 : 0;
+    eb += is_eq ? 1 : 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_stream_select(const StreamSelectParams &p, const SegTable &t, hipStream_t s) {
+  if (p.lv < 4 || p.lv % 4 != 0 || p.kslot % 4 != 0 || p.lv > kStreamRowMax || p.kslot + p.stream > p.lv)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(t.nseq * p.Hkv));
+  const int ipt = (p.lv + ST - 1) / ST;
+  if (ipt <= 4) hipLaunchKernelGGL(stream_select_kernel<4>, grid, dim3(ST), 0, s, p, t);
+  else if (ipt <= 8) hipLaunchKernelGGL(stream_select_kernel<8>, grid, dim3(ST), 0, s, p, t);
+  else if (ipt <= 16) hipLaunchKernelGGL(stream_select_kernel<16>, grid, dim3(ST), 0, s, p, t);
+  else hipLaunchKernelGGL(stream_select_kernel<32>, grid, dim3(ST), 0, s, p, t);
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_init(const StreamParams &p, const SegTable &t, hipStream_t s) {
   if (p.kslot <= 0) return hipSuccess;

@@ -216,10 +216,15 @@ kvsel_status kvsel_gather(const kvsel_problem *p, const int32_t *idx, const void
  *
  * With p->stream_keys = C > 0 (a multiple of 2048) it takes TideKV's
  * memory-bounded form instead (§4.2, two-pass blockwise streaming top-k):
- * pass 1 visits the prefix C keys at a time, folding each step's row
- * statistics into running ones; pass 2 visits it again C keys at a time
+ * the row statistics are gathered into a bounded number of states per
+ * (sequence, KV head); pass 2 then visits the prefix C keys at a time
  * (plus the pool's half width on each side), pools the step's scores and
- * merges them into a running top-k of each (sequence, KV head).  The
+ * merges them into a running top-k of each (sequence, KV head).  With a
+ * pool up to 33 wide and C plus the largest budget at most 32768, pass 1
+ * runs once over the prefix with at most 64 states per (sequence, KV
+ * head), a state folding ceil(L / 64) keys where that exceeds key_chunk;
+ * otherwise pass 1 also visits the prefix C keys at a time, folding each
+ * step's statistics into running ones.  The
  * workspace (kvsel_plan's size) then depends on C, the budgets, B, Hkv and
  * the rows, not on the prefix length; no whole-prefix score buffer exists,
  * so `pooled` must be NULL, and the other workspace entry points reject

@@ -238,6 +238,30 @@ int main() {
     shapes.push_back(s);
   }
   {
+    Shape s{"streaming 8192, pool 255 wide", base_problem(), {}, {}};
+    s.p.L = 20000;
+    s.p.k = 700;
+    s.p.pool = 1;
+    s.p.pool_kernel = 255;
+    s.p.stream_keys = 8192;
+    shapes.push_back(s);
+  }
+  {
+    Shape s{"streaming 32768, row past the fused limit", base_problem(), {}, {}};
+    s.p.L = 40000;
+    s.p.k = 64;
+    s.p.stream_keys = 32768;
+    shapes.push_back(s);
+  }
+  {
+    Shape s{"streaming 16384 over 2^20 keys", base_problem(), {}, {}};
+    s.p.L = 1 << 20;
+    s.p.k = 4096;
+    s.p.key_chunk = 1024;
+    s.p.stream_keys = 16384;
+    shapes.push_back(s);
+  }
+  {
     Shape s{"2^20 keys", base_problem(), {}, {}};
     s.p.L = 1 << 20;
     s.p.k = 4096;

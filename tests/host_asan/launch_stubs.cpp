@@ -146,6 +146,33 @@ hipError_t launch_score_pass2_tables(const ScoreParams &p, const SegTable &t, in
   return hipSuccess;
 }
 
+hipError_t launch_score_pass2_keys(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t) {
+  ++g_launches;
+  score_common(p, t, nblk, 2);
+  expect(p.pool_r >= 0 && p.pool_r <= kPoolHalo, "pass 2 keys: pool within the halo");
+  expect(p.key_begin >= p.step_origin, "pass 2 keys: window starts at or after its origin");
+  const int64_t last = std::min<int64_t>(lmax(t), p.key_end);
+  expect(last - p.step_origin <= p.step_stride, "pass 2 keys: a row holds the step");
+  need(p.step_keys, ((seg_end(t, p.Hkv) - 1) * p.step_stride + (last - p.step_origin)) * 4, "pass 2 keys: rows");
+  return hipSuccess;
+}
+
+hipError_t launch_stream_select(const StreamSelectParams &p, const SegTable &t, hipStream_t) {
+  ++g_launches;
+  expect(p.lv % 4 == 0 && p.kslot % 4 == 0 && p.kslot + p.stream <= p.lv && p.lv <= kStreamRowMax,
+         "streaming selection: row layout");
+  expect(t.kmax <= p.kslot, "streaming selection: running slots hold every budget");
+  need(p.keys_in, seg_end(t, p.Hkv) * p.lv * 4, "streaming selection: rows in");
+  if (p.kslot > 0) need(p.pos_in, seg_end(t, p.Hkv) * p.kslot * 4, "streaming selection: positions in");
+  if (p.last) {
+    need(p.idx, out_rows(t, p.Hkv) * 4, "streaming selection: kept positions");
+  } else {
+    need(p.keys_out, seg_end(t, p.Hkv) * p.lv * 4, "streaming selection: rows out");
+    if (p.kslot > 0) need(p.pos_out, seg_end(t, p.Hkv) * p.kslot * 4, "streaming selection: positions out");
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_stream_stats(const ScoreParams &p, const SegTable &t, float2 *run, int, hipStream_t) {
   ++g_launches;
   need(p.partials, seg_end(t, p.Hkv) * p.nblk1_max * p.Rpad * 8, "fold: block states");

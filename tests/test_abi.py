@@ -240,13 +240,16 @@ def test_allocate_budgets_hand_and_validation():
 
 def test_streaming_workspace_is_bounded():
     """With stream_keys the workspace does not grow with the prefix length."""
-    sizes = []
-    for L in (4096, 65536, 1 << 20):
-        p = kv.Problem(Hq=32, Hkv=8, w=32, L=L, pool="max", pool_kernel=7, k=2048, stream_keys=32768)
-        sizes.append(kv.kvsel_plan(p)[0])
-    assert sizes[0] == sizes[1] == sizes[2]
     whole = kv.kvsel_plan(kv.Problem(Hq=32, Hkv=8, w=32, L=1 << 20, pool="max", pool_kernel=7, k=2048))[0]
-    assert sizes[0] * 8 < whole
+    # 32768 keys per step: the step-wise form (the running row exceeds the
+    # fused selection's); 8192 and 16384: the fused form
+    for C in (32768, 8192, 16384):
+        sizes = []
+        for L in (4000, 4096, 65536, 1 << 20):
+            p = kv.Problem(Hq=32, Hkv=8, w=32, L=L, pool="max", pool_kernel=7, k=2048, stream_keys=C)
+            sizes.append(kv.kvsel_plan(p)[0])
+        assert len(set(sizes)) == 1, (C, sizes)
+        assert sizes[0] * 8 < whole
     # budgets too large for one candidate row
     p = kv.Problem(Hq=4, Hkv=1, w=1, L=1 << 20, k=1 << 20, stream_keys=2048)
     assert _status(p) == kv.KVSEL_EUNSUPPORTED

@@ -79,6 +79,14 @@ STREAM_CASES = [
     (W.Spec("st_wide_pool", [4500], Hq=8, Hkv=2, w=8, pool="avg", pool_kernel=255, k=600, recipe="plant"), 2048),
     (W.Spec("st_reserve_over", [3000], Hq=8, Hkv=2, w=8, pool="max", pool_kernel=3, budgets=[[20, 3000]],
             sink=10, recent=2100, recipe="plain"), 2048),
+    # running rows of 4096 < kslot + C <= 8192 slots (eight per thread of the selection)
+    (W.Spec("st_rows8", [9000], Hq=8, Hkv=2, w=16, pool="avg", pool_kernel=9, k=3000, recipe="zipf"), 4096),
+    # every score equal (logits scaled to nothing, no mask): the threshold bin holds every
+    # key, so the running selection takes its radix rounds; ties go to the lower position
+    (W.Spec("st_ties", [6000], Hq=8, Hkv=2, w=8, causal=False, scale=1e-30, pool="max", pool_kernel=3, k=700,
+            recipe="plain"), 2048),
+    # a running row longer than the fused selection takes (the step-wise path)
+    (W.Spec("st_long_row", [3000], Hq=8, Hkv=2, w=8, pool="max", pool_kernel=5, k=100, recipe="plant"), 32768),
 ]
 
 
