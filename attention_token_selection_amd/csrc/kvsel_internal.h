@@ -197,7 +197,7 @@ hipError_t launch_score_pass2_tables(const ScoreParams &p, const SegTable &t, in
 hipError_t launch_score_pass2_keys(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s);
 hipError_t launch_stream_select(const StreamSelectParams &p, const SegTable &t, hipStream_t s);
 // Largest row (kslot + stream) launch_stream_select takes.
-constexpr int kStreamRowMax = 32768;
+constexpr int kStreamRowMax = 16384;
 hipError_t launch_stream_stats(const ScoreParams &p, const SegTable &t, float2 *run, int first, hipStream_t s);
 hipError_t launch_stream_init(const StreamParams &p, const SegTable &t, hipStream_t s);
 hipError_t launch_stream_pool(const StreamParams &p, const SegTable &t, hipStream_t s);

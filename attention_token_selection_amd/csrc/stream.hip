@@ -129,7 +129,7 @@ __device__ inline uint32_t exscan_st(uint32_t v, uint32_t *tmp, uint32_t &total)
 // three radix rounds (11 + 11 + 10 bits); then one ordered compaction.
 template <int IPT>
 __global__ __launch_bounds__(ST) void stream_select_kernel(StreamSelectParams p, SegTable t) {
-  static_assert(IPT % 4 == 0 && IPT <= 32, "whole uint4 loads; one validity bit per slot");
+  static_assert(IPT % 4 == 0 && IPT <= 16, "whole uint4 loads; at most 16 keys in registers");
   __shared__ uint32_t hist[kTabBins];
   __shared__ __attribute__((aligned(16))) uint32_t cand[kRankMax];
   __shared__ uint32_t tmp[SW];
@@ -157,6 +157,23 @@ __global__ __launch_bounds__(ST) void stream_select_kernel(StreamSelectParams p,
     k[j + 2] = u.z;
     k[j + 3] = u.w;
   }
+  // the running slots' positions (clamped; unused past the running
+  // slots), loaded with the keys so that their latency overlaps the rest
+  int32_t pv[IPT];
+  if (p.kslot >= 4) {
+    const int32_t *pin = p.pos_in + (int64_t)seg * p.kslot;
+#pragma unroll
+    for (int j = 0; j < IPT; j += 4) {
+      const int4 u = *reinterpret_cast<const int4 *>(pin + min(i0 + j, p.kslot - 4));
+      pv[j] = u.x;
+      pv[j + 1] = u.y;
+      pv[j + 2] = u.z;
+      pv[j + 3] = u.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) pv[j] = 0;
+  }
   uint32_t vm = 0u;  // bit j: slot i0 + j holds a key
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
@@ -170,9 +187,10 @@ __global__ __launch_bounds__(ST) void stream_select_kernel(StreamSelectParams p,
   int take_eq = 0;
   if (keep < n_in + m) {
     const uint32_t centre = order_key(p.wsum / (float)L);
+    // monotone in the key: steps of 2^16 counted from the centre's step
+    const int cstep = (int)(centre >> kTabDigitShift);
     auto digit = [&](uint32_t key) {
-      const int64_t rel = ((int64_t)key - (int64_t)centre) >> kTabDigitShift;
-      return (int)min<int64_t>(kTabBins - 1, max<int64_t>(0, rel + kTabBins / 2));
+      return min(kTabBins - 1, max(0, (int)(key >> kTabDigitShift) - cstep + kTabBins / 2));
     };
     for (int i = tid; i < kTabBins; i += ST) hist[i] = 0u;
     if (tid == 0) sh[2] = 0;
@@ -201,9 +219,15 @@ __global__ __launch_bounds__(ST) void stream_select_kernel(StreamSelectParams p,
     __syncthreads();
     const int b1 = sh[0];
     int rest = keep - sh[1];  // keys of bin b1 to keep, >= 1
+    // bin b1's keys as a key range (the edge bins take everything beyond;
+    // a bin that holds a key has a step in [0, 2^16))
+    const uint32_t b1step = (uint32_t)(b1 - kTabBins / 2 + cstep) << kTabDigitShift;
+    const uint32_t klo = (b1 == 0) ? 0u : b1step;
+    const uint32_t khi = (b1 == kTabBins - 1) ? 0xffffffffu : (b1step | ((1u << kTabDigitShift) - 1u));
+    auto in_b1 = [&](uint32_t key) { return key >= klo && key <= khi; };
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
-      if (((vm >> j) & 1u) && digit(k[j]) == b1) {
+      if (((vm >> j) & 1u) && in_b1(k[j])) {
         const int c = atomicAdd(&sh[2], 1);
         if (c < kRankMax) cand[c] = k[j];
       }
@@ -242,7 +266,7 @@ __global__ __launch_bounds__(ST) void stream_select_kernel(StreamSelectParams p,
         const uint32_t dmask = (1u << (hi - lo)) - 1u;
 #pragma unroll
         for (int j = 0; j < IPT; ++j) {
-          if (((vm >> j) & 1u) && digit(k[j]) == b1 && (hi == 32 || (k[j] >> hi) == pre))
+          if (((vm >> j) & 1u) && in_b1(k[j]) && (hi == 32 || (k[j] >> hi) == pre))
             atomicAdd(&hist[(k[j] >> lo) & dmask], 1u);
         }
         __syncthreads();
@@ -270,24 +294,7 @@ __global__ __launch_bounds__(ST) void stream_select_kernel(StreamSelectParams p,
     }
   }
 
-  // ---- ordered compaction: slot order is position order.  The running
-  // slots' positions are loaded for every slot first (clamped, unused past
-  // the running slots), so that the loads go out together.
-  int32_t pv[IPT];
-  if (p.kslot >= 4) {
-    const int32_t *pin = p.pos_in + (int64_t)seg * p.kslot;
-#pragma unroll
-    for (int j = 0; j < IPT; j += 4) {
-      const int4 u = *reinterpret_cast<const int4 *>(pin + min(i0 + j, p.kslot - 4));
-      pv[j] = u.x;
-      pv[j + 1] = u.y;
-      pv[j + 2] = u.z;
-      pv[j + 3] = u.w;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < IPT; ++j) pv[j] = 0;
-  }
+  // ---- ordered compaction: slot order is position order
   uint32_t gt = 0u, eq = 0u;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
@@ -328,8 +335,7 @@ hipError_t launch_stream_select(const StreamSelectParams &p, const SegTable &t, 
   const int ipt = (p.lv + ST - 1) / ST;
   if (ipt <= 4) hipLaunchKernelGGL(stream_select_kernel<4>, grid, dim3(ST), 0, s, p, t);
   else if (ipt <= 8) hipLaunchKernelGGL(stream_select_kernel<8>, grid, dim3(ST), 0, s, p, t);
-  else if (ipt <= 16) hipLaunchKernelGGL(stream_select_kernel<16>, grid, dim3(ST), 0, s, p, t);
-  else hipLaunchKernelGGL(stream_select_kernel<32>, grid, dim3(ST), 0, s, p, t);
+  else hipLaunchKernelGGL(stream_select_kernel<16>, grid, dim3(ST), 0, s, p, t);
   return hipGetLastError();
 }
 

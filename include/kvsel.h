@@ -220,7 +220,7 @@ kvsel_status kvsel_gather(const kvsel_problem *p, const int32_t *idx, const void
  * (sequence, KV head); pass 2 then visits the prefix C keys at a time
  * (plus the pool's half width on each side), pools the step's scores and
  * merges them into a running top-k of each (sequence, KV head).  With a
- * pool up to 33 wide and C plus the largest budget at most 32768, pass 1
+ * pool up to 33 wide and C plus the largest budget at most 16384, pass 1
  * runs once over the prefix with at most 64 states per (sequence, KV
  * head), a state folding ceil(L / 64) keys where that exceeds key_chunk;
  * otherwise pass 1 also visits the prefix C keys at a time, folding each

@@ -254,11 +254,11 @@ int main() {
     shapes.push_back(s);
   }
   {
-    Shape s{"streaming 16384 over 2^20 keys", base_problem(), {}, {}};
+    Shape s{"streaming 8192 over 2^20 keys", base_problem(), {}, {}};
     s.p.L = 1 << 20;
     s.p.k = 4096;
     s.p.key_chunk = 1024;
-    s.p.stream_keys = 16384;
+    s.p.stream_keys = 8192;
     shapes.push_back(s);
   }
   {

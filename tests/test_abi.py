@@ -241,8 +241,8 @@ def test_allocate_budgets_hand_and_validation():
 def test_streaming_workspace_is_bounded():
     """With stream_keys the workspace does not grow with the prefix length."""
     whole = kv.kvsel_plan(kv.Problem(Hq=32, Hkv=8, w=32, L=1 << 20, pool="max", pool_kernel=7, k=2048))[0]
-    # 32768 keys per step: the step-wise form (the running row exceeds the
-    # fused selection's); 8192 and 16384: the fused form
+    # 16384 and 32768 keys per step: the step-wise form (the running row of
+    # the budget plus a step exceeds the fused selection's); 8192: the fused form
     for C in (32768, 8192, 16384):
         sizes = []
         for L in (4000, 4096, 65536, 1 << 20):

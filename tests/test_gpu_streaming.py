@@ -71,7 +71,7 @@ STREAM_CASES = [
     (W.Spec("st_plain", [9000], Hq=8, Hkv=2, w=16, pool="max", pool_kernel=7, k=300, recipe="plant"), 2048),
     (W.Spec("st_ragged", [5000, 700, 12289], Hq=16, Hkv=4, w=12, pool="avg", pool_kernel=5,
             budgets=[[0, 40, 5000, 4096], [700, 1, 30, 2000], [64, 3000, 12289, 129]], recipe="plant",
-            plant_frac=0.03), 4096),
+            plant_frac=0.03), 2048),
     (W.Spec("st_deferkv", [7000], Hq=32, Hkv=8, w=32, has_decode=True, pool="max", pool_kernel=7, k=500,
             weighting="exp", lam=0.1, sink=16, recent=32, recipe="decode_corr"), 2048),
     (W.Spec("st_meanq_nocausal", [6000], Hq=32, Hkv=8, w=20, has_decode=True, alpha=0.5, causal=False,
@@ -114,3 +114,43 @@ def test_streaming_full_size(kv):
     st = check_against_oracle(spec, case_cpu, {**s_out, "pooled": None}, ref)
     _say(f"streaming full size: differs from whole-prefix at {d}; oracle {st}")
     assert st["segments"] == spec.batch * spec.Hkv
+
+
+def test_streaming_graph_replays_match_eager(kv):
+    """The fused streaming form (two alternating key rows per segment, one
+    selection launch per step) captured into a graph for two layers and
+    replayed several times, with eager library work and synchronisations in
+    between: every replay must equal the eager result bit for bit."""
+    spec = W.Spec("st_graph", [20000], Hq=32, Hkv=8, w=32, pool="max", pool_kernel=7, k=700, recipe="runs",
+                  plant_frac=0.01)
+    p = kv.Problem(**W.problem_kwargs(spec), stream_keys=4096)
+    cases = [{k: v.to(DEV) for k, v in W.make_case(spec, layer=l).items()} for l in range(3)]
+    stream = torch.cuda.Stream(device=DEV)
+    with torch.cuda.stream(stream):
+        eager = [kv.compress(p, c["Q"], c["K"], c["V"], pooled=False, stream=stream) for c in cases[:2]]
+    torch.cuda.synchronize()
+    ws = torch.empty(kv.kvsel_plan(p)[0], dtype=torch.uint8, device=DEV)
+    outs = [kv.alloc_outputs(p, DEV, pooled=False) for _ in range(2)]
+    calls = [kv.bind_compress(p, c["Q"], c["K"], c["V"], o["idx"], o["K_out"], o["V_out"], None, ws, stream)
+             for c, o in zip(cases, outs)]
+    with torch.cuda.stream(stream):
+        for call in calls:
+            call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for call in calls:
+            call()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:  # poison the outputs
+            o["idx"].fill_(-7)
+            o["K_out"].fill_(3.0)
+        kv.compress(p, cases[2]["Q"], cases[2]["K"], cases[2]["V"], pooled=False)  # eager work on the library
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, o in zip(eager, outs):
+            assert torch.equal(e["idx"], o["idx"]), f"replay {rep}: idx"
+            assert torch.equal(e["K_out"], o["K_out"]), f"replay {rep}: K_out"
+            assert torch.equal(e["V_out"], o["V_out"]), f"replay {rep}: V_out"
