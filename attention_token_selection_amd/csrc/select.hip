@@ -125,6 +125,19 @@ __device__ int block_count(bool pred, int *tmp) {
   return tot;
 }
 
+// Sum of v over the workgroup (every thread gets it).
+__device__ uint64_t block_sum64(uint64_t v, uint64_t *tmp64) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
+  if ((threadIdx.x & 63) == 0) tmp64[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint64_t tot = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; ++i) tot += tmp64[i];
+  __syncthreads();
+  return tot;
+}
+
 struct Segment {
   const float *S;
   float *P;
@@ -678,17 +691,25 @@ __global__ __launch_bounds__(NT) void select_block_kernel(SelectParams p, SegTab
     }
     __syncthreads();
     {
-      // exclusive prefix over the blocks: thread tid owns blocks
-      // [BPT tid, BPT tid + BPT)
-      int a[BPT], s = 0;
+      // exclusive prefix over the blocks of the candidate counts: thread tid
+      // owns blocks [BPT tid, BPT tid + BPT); and the keys above bin b1 in
+      // the blocks before this chunk's (CPB c onwards: one half of thread
+      // c / 2's share)
+      int a[BPT], s = 0, sa = 0, ah = 0;
+      const int h0 = (c & 1) * CPB;
 #pragma unroll
       for (int u = 0; u < BPT; ++u) {
         const int j = BPT * tid + u;
         a[u] = (j < nb) ? b_cb[j] : 0;
         s += a[u];
+        const int ab = (j < nb) ? b_above[j] : 0;
+        sa += ab;
+        ah += (u < h0) ? ab : 0;
       }
       int tot;
       int ex = block_exscan(s, tmp, tot);
+      int tota;
+      const int exa = block_exscan(sa, tmp, tota);
 #pragma unroll
       for (int u = 0; u < BPT; ++u) {
         const int j = BPT * tid + u;
@@ -696,8 +717,10 @@ __global__ __launch_bounds__(NT) void select_block_kernel(SelectParams p, SegTab
         ex += a[u];
       }
       if (tid == 0) b_cb[nb] = tot;
+      if (tid == (c >> 1)) sh[2] = exa + ah;
     }
     __syncthreads();
+    const int above_before = sh[2];  // keys above bin b1 in blocks [0, CPB c)
     const int m = b_cb[nb];  // keys in bin b1, >= need
 
     // Candidate i lives in block j (the largest j with b_cb[j] <= i).
@@ -762,11 +785,20 @@ __global__ __launch_bounds__(NT) void select_block_kernel(SelectParams p, SegTab
         const uint32_t ki = candk[i];
         int gt = 0, eq = 0;
         const uint4 *c4 = reinterpret_cast<const uint4 *>(candk);
-        for (int j = 0; j < (m + 3) >> 2; ++j) {
-          const uint4 kj = c4[j];
+        const int n4 = (m + 3) >> 2;
+        auto cmp = [&](const uint4 kj) {
           gt += (kj.x > ki) + (kj.y > ki) + (kj.z > ki) + (kj.w > ki);
           eq += (kj.x == ki) + (kj.y == ki) + (kj.z == ki) + (kj.w == ki);
+        };
+        int j = 0;
+        for (; j + 4 <= n4; j += 4) {  // four reads in flight
+          const uint4 k0 = c4[j], k1 = c4[j + 1], k2 = c4[j + 2], k3 = c4[j + 3];
+          cmp(k0);
+          cmp(k1);
+          cmp(k2);
+          cmp(k3);
         }
+        for (; j < n4; ++j) cmp(c4[j]);
         eq -= (ki == 0u) ? (((m + 3) & ~3) - m) : 0;  // the padding keys are 0
         if (gt < need && gt + eq >= need) {
           sh[2] = (int)ki;
@@ -816,50 +848,73 @@ __global__ __launch_bounds__(NT) void select_block_kernel(SelectParams p, SegTab
       take_eq = rest;
     }
 
-    // ---- per-block kept counts; this chunk's first output slot and its
-    // share of the keys equal to tau
-    visit([&](uint32_t k, int j) {
-      if (k > tau) atomicAdd(&b_gt[j], 1);
-      else if (k == tau) atomicAdd(&b_eq[j], 1);
-    });
-    __syncthreads();
-    {
-      int e[BPT], es = 0;
-#pragma unroll
-      for (int u = 0; u < BPT; ++u) {
-        const int j = BPT * tid + u;
-        e[u] = (j < nb) ? b_eq[j] : 0;
-        es += e[u];
+    // ---- this chunk's first output slot and its share of the keys equal
+    // to tau.  Candidates in LDS: the kept keys before the chunk are those
+    // above bin b1 there, the candidates there above tau and the first
+    // take_eq equal to it (lower blocks first); one sum over the
+    // candidates.  Otherwise per-block counts and two scans over the blocks.
+    int take_me;  // keys equal to tau that this chunk keeps
+    if (in_lds) {
+      const int cb0 = CPB * c, cb1 = cb0 + CPB;
+      uint64_t gtb = 0, eqb = 0, eqi = 0;  // candidates > tau before the chunk, == tau before it, == tau in it
+      for (int i = tid; i < m; i += NT) {
+        const uint32_t k = candk[i];
+        const int j = candb[i];
+        gtb += (j < cb0 && k > tau) ? 1u : 0u;
+        eqb += (j < cb0 && k == tau) ? 1u : 0u;
+        eqi += (j >= cb0 && j < cb1 && k == tau) ? 1u : 0u;
       }
-      int tot;
-      int eb = block_exscan(es, tmp, tot);  // equal keys in earlier blocks
-      int tk[BPT], sk[BPT], ss = 0;
-#pragma unroll
-      for (int u = 0; u < BPT; ++u) {
-        const int j = BPT * tid + u;
-        tk[u] = min(e[u], max(0, take_eq - eb));
-        eb += e[u];
-        sk[u] = (j < nb) ? b_above[j] + b_gt[j] + tk[u] : 0;
-        ss += sk[u];
-      }
-      int sb = block_exscan(ss, tmp, tot);
-      // The chunk's blocks CPB c .. CPB c + CPB - 1 are one half of thread
-      // c / 2's share: its first half for even c, its second for odd c.
-      if (tid == (c >> 1)) {
-        const int h0 = (c & 1) * CPB;
-        int tm = 0;
+      __shared__ uint64_t tmp64[NWAVE];
+      const uint64_t packed = block_sum64(gtb | (eqb << 21) | (eqi << 42), tmp64);  // each count <= MAXC < 2^21
+      const int gt_before = (int)(packed & 0x1fffff);
+      const int eq_before = (int)((packed >> 21) & 0x1fffff);
+      const int eq_in = (int)(packed >> 42);
+      base = above_before + gt_before + min(eq_before, take_eq);
+      take_me = max(0, min(eq_in, take_eq - eq_before));
+    } else {
+      visit([&](uint32_t k, int j) {
+        if (k > tau) atomicAdd(&b_gt[j], 1);
+        else if (k == tau) atomicAdd(&b_eq[j], 1);
+      });
+      __syncthreads();
+      {
+        int e[BPT], es = 0;
 #pragma unroll
         for (int u = 0; u < BPT; ++u) {
-          sb += (u < h0) ? sk[u] : 0;
-          tm += (u >= h0 && u < h0 + CPB) ? tk[u] : 0;
+          const int j = BPT * tid + u;
+          e[u] = (j < nb) ? b_eq[j] : 0;
+          es += e[u];
         }
-        sh[2] = sb;
-        sh[3] = tm;
+        int tot;
+        int eb = block_exscan(es, tmp, tot);  // equal keys in earlier blocks
+        int tk[BPT], sk[BPT], ss = 0;
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+          const int j = BPT * tid + u;
+          tk[u] = min(e[u], max(0, take_eq - eb));
+          eb += e[u];
+          sk[u] = (j < nb) ? b_above[j] + b_gt[j] + tk[u] : 0;
+          ss += sk[u];
+        }
+        int sb = block_exscan(ss, tmp, tot);
+        // The chunk's blocks CPB c .. CPB c + CPB - 1 are one half of thread
+        // c / 2's share: its first half for even c, its second for odd c.
+        if (tid == (c >> 1)) {
+          const int h0 = (c & 1) * CPB;
+          int tm = 0;
+#pragma unroll
+          for (int u = 0; u < BPT; ++u) {
+            sb += (u < h0) ? sk[u] : 0;
+            tm += (u >= h0 && u < h0 + CPB) ? tk[u] : 0;
+          }
+          sh[2] = sb;
+          sh[3] = tm;
+        }
+        __syncthreads();
       }
-      __syncthreads();
+      base = sh[2];
+      take_me = sh[3];
     }
-    base = sh[2];
-    const int take_me = sh[3];  // keys equal to tau that this chunk keeps
 
     // ---- ordered compaction of this chunk
     uint32_t k[PER];

@@ -91,6 +91,13 @@ EDGE = [
     W.Spec("f_expw", [2600, 900], Hq=8, Hkv=2, w=8, weighting="exp", lam=0.2, pool="max", pool_kernel=5, k=250,
            recipe="plant"),
     W.Spec("f_pool35_unfused", [2000], Hq=8, Hkv=2, w=8, pool="avg", pool_kernel=35, k=150, recipe="plant"),
+    # every score equal (logits scaled to nothing, no mask), so every key lands in the
+    # threshold's bin: 3000 candidates (held in LDS, past direct ranking) and 9000 (past
+    # the LDS, read from the buckets); ties go to the lower position
+    W.Spec("f_ties_lds", [3000], Hq=8, Hkv=2, w=8, causal=False, scale=1e-30, pool="max", pool_kernel=3, k=500,
+           recipe="plain"),
+    W.Spec("f_ties_mem", [9000], Hq=8, Hkv=2, w=8, causal=False, scale=1e-30, pool="avg", pool_kernel=5, k=700,
+           recipe="plain"),
 ]
 
 
@@ -105,7 +112,7 @@ def test_fused_edges_vs_oracle(kv, spec):
     assert st["max_rel"] < 1e-4, st
 
 
-SAME = [W.small_cases()[i] for i in (2, 3, 5, 6, 7, 15, 19, 20)] + [EDGE[i] for i in (0, 2, 5, 9, 10, 11)]
+SAME = [W.small_cases()[i] for i in (2, 3, 5, 6, 7, 15, 19, 20)] + [EDGE[i] for i in (0, 2, 5, 9, 10, 11, 14, 15)]
 
 
 @pytest.mark.parametrize("spec", SAME, ids=lambda s: s.name)
