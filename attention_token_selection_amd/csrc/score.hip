@@ -214,9 +214,11 @@ __device__ inline float row_log2_weight(const ScoreParams &p, int row) {
 // 0 then takes in share 1.  Every pass-2 workgroup of the segment computes
 // the same bits.  The first batch of loads is issued before the key tiles
 // (so that waiting for it does not mean waiting for them), by
-// MergeRows::load; MergeRows::finish does the rest.
+// MergeRows::load; MergeRows::finish does the rest.  With MB = 32 one batch
+// covers 64 block states (a whole 32K-key prefix in blocks of 512), so the
+// biases are ready about when the first tiles land.
+template <int MB>
 struct MergeRows {
-  static constexpr int MB = 16;
   float2 v[MB];
   int row, sh;
   const float2 *all;
@@ -285,9 +287,9 @@ struct MergeRows {
 
 // The end of pass 2 with tables (see top).  red holds the waves' partial S
 // per key (rs floats per wave: the block's keys, then the halo tile's); hist
-// is 2048 words of LDS the key ring no longer needs.
-__device__ void tables_epilogue(const ScoreParams &p, float *red, int rs, uint32_t *hist, int seg, int h, int64_t key0,
-                                int L, int kb0, int kb1) {
+// and hist1 are 2048 words each of LDS the key ring no longer needs.
+__device__ void tables_epilogue(const ScoreParams &p, float *red, int rs, uint32_t *hist, uint32_t *hist1, int seg,
+                                int h, int64_t key0, int L, int kb0, int kb1) {
   static_assert(NT == kTabBlock, "one thread per position of a table block");
   static_assert(kTabBins == 8 * NT, "eight bins per thread in the block scan");
   constexpr int HALO = kPoolHalo;
@@ -318,76 +320,118 @@ __device__ void tables_epilogue(const ScoreParams &p, float *red, int rs, uint32
 
   const uint32_t centre = order_key(p.wsum / (float)L);  // the key of the mean score
   const int ntb = (n + kTabBlock - 1) / kTabBlock;
-  for (int tb = 0; tb < ntb; ++tb) {
+  uint32_t *hs[2] = {hist, hist1};
+  // Two table blocks at a time (tb0, tb0 + 1), thread tid taking position
+  // tid of each: their histograms in two LDS arrays, one scan for both.
+  for (int tb0 = 0; tb0 < ntb; tb0 += 2) {
     // ---- pool, pooled output
-    const int x = tb * kTabBlock + tid;
-    float P = 0.0f;
-    if (x < n) {
-      const float *c = sbuf + HALO + x;
-      if (r == 0) {
-        P = c[0];
-      } else if (is_max) {
-        float m = c[0];
-        for (int j = -r; j <= r; ++j) m = fmaxf(m, c[j]);
-        P = m;
-      } else {
-        float sum = 0.0f;
-        for (int j = -r; j <= r; ++j) sum += c[j];
-        P = sum / p.pool_width;
+    float P[2];
+    int x[2];
+    bool ok[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      x[e] = (tb0 + e) * kTabBlock + tid;
+      ok[e] = x[e] < n;  // (past the last table block: x >= n)
+      P[e] = 0.0f;
+      if (ok[e]) {
+        const float *c = sbuf + HALO + x[e];
+        if (r == 0) {
+          P[e] = c[0];
+        } else if (is_max) {
+          float m = c[0];
+          for (int j = -r; j <= r; ++j) m = fmaxf(m, c[j]);
+          P[e] = m;
+        } else {
+          float sum = 0.0f;
+          for (int j = -r; j <= r; ++j) sum += c[j];
+          P[e] = sum / p.pool_width;
+        }
+        if (p.pooled) p.pooled[segbase + kb0 + x[e]] = P[e];
       }
-      if (p.pooled) p.pooled[segbase + kb0 + x] = P;
     }
     if (p.step_keys) {
       // the streaming form: the pooled scores' order keys, no tables
-      if (x < n) p.step_keys[(int64_t)seg * p.step_stride + (kb0 + x - p.step_origin)] = select_key(P, kb0 + x, L, p.sink, p.recent);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        if (ok[e])
+          p.step_keys[(int64_t)seg * p.step_stride + (kb0 + x[e] - p.step_origin)] =
+              select_key(P[e], kb0 + x[e], L, p.sink, p.recent);
       continue;
     }
 
-    // ---- counting sort of the table block by first digit; the segment
+    // ---- counting sort of each table block by first digit; the segment
     // histogram
-    reinterpret_cast<uint4 *>(hist)[2 * tid] = make_uint4(0u, 0u, 0u, 0u);
-    reinterpret_cast<uint4 *>(hist)[2 * tid + 1] = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
-    uint32_t key = 0u, dg = 0u, rank = 0u;
-    if (x < n) {
-      key = select_key(P, kb0 + x, L, p.sink, p.recent);
-      const int64_t rel = ((int64_t)key - (int64_t)centre) >> kTabDigitShift;
-      dg = (uint32_t)min<int64_t>(kTabBins - 1, max<int64_t>(0, rel + kTabBins / 2));
-      rank = atomicAdd(&hist[dg], 1u);
-    }
-    __syncthreads();
-    uint32_t cnt[8], pre[8];
-    {
-      const uint4 a0 = reinterpret_cast<const uint4 *>(hist)[2 * tid];
-      const uint4 a1 = reinterpret_cast<const uint4 *>(hist)[2 * tid + 1];
-      cnt[0] = a0.x; cnt[1] = a0.y; cnt[2] = a0.z; cnt[3] = a0.w;
-      cnt[4] = a1.x; cnt[5] = a1.y; cnt[6] = a1.z; cnt[7] = a1.w;
-    }
-    int own = 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) own += (int)cnt[u];
+    for (int e = 0; e < 2; ++e) {
+      reinterpret_cast<uint4 *>(hs[e])[2 * tid] = make_uint4(0u, 0u, 0u, 0u);
+      reinterpret_cast<uint4 *>(hs[e])[2 * tid + 1] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+    uint32_t key[2], dg[2], rank[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      key[e] = 0u;
+      dg[e] = 0u;
+      rank[e] = 0u;
+      if (ok[e]) {
+        key[e] = select_key(P[e], kb0 + x[e], L, p.sink, p.recent);
+        const int64_t rel = ((int64_t)key[e] - (int64_t)centre) >> kTabDigitShift;
+        dg[e] = (uint32_t)min<int64_t>(kTabBins - 1, max<int64_t>(0, rel + kTabBins / 2));
+        rank[e] = atomicAdd(&hs[e][dg[e]], 1u);
+      }
+    }
+    __syncthreads();
+    uint32_t cnt[2][8], pre[2][8];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint4 a0 = reinterpret_cast<const uint4 *>(hs[e])[2 * tid];
+      const uint4 a1 = reinterpret_cast<const uint4 *>(hs[e])[2 * tid + 1];
+      cnt[e][0] = a0.x; cnt[e][1] = a0.y; cnt[e][2] = a0.z; cnt[e][3] = a0.w;
+      cnt[e][4] = a1.x; cnt[e][5] = a1.y; cnt[e][6] = a1.z; cnt[e][7] = a1.w;
+    }
+    int own = 0;  // both blocks' counts in this thread's bins, 16 bits each (at most 256)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) own += (int)(cnt[0][u] | (cnt[1][u] << 16));
     int total;
-    uint32_t run = (uint32_t)block_exscan(own, tmp, total);  // its barriers end the reads above
+    const int ex = block_exscan(own, tmp, total);  // its barriers end the reads above
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      pre[u] = run;
-      run += cnt[u];
+    for (int e = 0; e < 2; ++e) {
+      uint32_t run = (uint32_t)(ex >> (16 * e)) & 0xffffu;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        pre[e][u] = run;
+        run += cnt[e][u];
+      }
+      if (tb0 + e < ntb) {
+        const int64_t tabi = (int64_t)seg * p.ntab_max + kb0 / kTabBlock + tb0 + e;
+        reinterpret_cast<uint4 *>(p.tab + tabi * kTabBins)[tid] =
+            make_uint4(pre[e][0] | (pre[e][1] << 16), pre[e][2] | (pre[e][3] << 16), pre[e][4] | (pre[e][5] << 16),
+                       pre[e][6] | (pre[e][7] << 16));
+      }
     }
-    const int64_t tabi = (int64_t)seg * p.ntab_max + kb0 / kTabBlock + tb;
-    reinterpret_cast<uint4 *>(p.tab + tabi * kTabBins)[tid] =
-        make_uint4(pre[0] | (pre[1] << 16), pre[2] | (pre[3] << 16), pre[4] | (pre[5] << 16), pre[6] | (pre[7] << 16));
     // this workgroup's copy of the segment histogram: consecutive
     // workgroups go to different compute dies, and so do the copies
     const int copy = (int)((blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z)) % kTabHistCopies);
-    uint32_t *sh = p.seg_hist + ((int64_t)seg * kTabHistCopies + copy) * kTabBins + 8 * tid;
+    uint32_t *shc = p.seg_hist + ((int64_t)seg * kTabHistCopies + copy) * kTabBins + 8 * tid;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (cnt[u]) atomicAdd(sh + u, cnt[u]);
-    reinterpret_cast<uint4 *>(hist)[2 * tid] = make_uint4(pre[0], pre[1], pre[2], pre[3]);
-    reinterpret_cast<uint4 *>(hist)[2 * tid + 1] = make_uint4(pre[4], pre[5], pre[6], pre[7]);
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t cu = cnt[0][u] + cnt[1][u];
+      if (cu) atomicAdd(shc + u, cu);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      reinterpret_cast<uint4 *>(hs[e])[2 * tid] = make_uint4(pre[e][0], pre[e][1], pre[e][2], pre[e][3]);
+      reinterpret_cast<uint4 *>(hs[e])[2 * tid + 1] = make_uint4(pre[e][4], pre[e][5], pre[e][6], pre[e][7]);
+    }
     __syncthreads();
-    if (x < n) p.bucket[tabi * kTabBlock + hist[dg] + rank] = key;
-    __syncthreads();  // hist is cleared for the next table block
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      if (ok[e]) {
+        const int64_t tabi = (int64_t)seg * p.ntab_max + kb0 / kTabBlock + tb0 + e;
+        p.bucket[tabi * kTabBlock + hs[e][dg[e]] + rank[e]] = key[e];
+      }
+    }
+    __syncthreads();  // the histograms are cleared for the next pair
   }
 }
 
@@ -519,7 +563,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 2 &
   // at most 2 (PD - 2) loads remain means tile t has landed.
   const uint16_t *kh = p.K + key0 * (int64_t)rowstride + (int64_t)h * kHeadDim;
   auto issue = [&](char *slot, int ti) { issue_keys(slot, kh, halo && ti == ntile, ti, kb0, kb1, L, rowstride, wave, lane); };
-  MergeRows mr;
+  MergeRows<(RT == 1 && !SPLIT) ? 32 : 16> mr;  // (one row tile per wave leaves the registers for 32)
   const int nstat = (int)((L + (int64_t)p.stat_block - 1) / p.stat_block);  // pass-1 block states per row
   if constexpr (PASS == 2) mr.load(p, seg, nstat);
 #pragma unroll
@@ -744,7 +788,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 2 &
 
   if constexpr (PASS == 2 && TAB) {
     __syncthreads();
-    tables_epilogue(p, red, rs, reinterpret_cast<uint32_t *>(g_ring0), seg, h, key0, L, kb0, kb1);
+    tables_epilogue(p, red, rs, reinterpret_cast<uint32_t *>(g_ring0), reinterpret_cast<uint32_t *>(g_ring1), seg, h,
+                    key0, L, kb0, kb1);
   } else if constexpr (PASS == 2) {
     __syncthreads();
     const int n = kb1 - kb0;
