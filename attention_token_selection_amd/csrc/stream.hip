@@ -225,11 +225,19 @@ __global__ __launch_bounds__(ST) void stream_select_kernel(StreamSelectParams p,
     const uint32_t klo = (b1 == 0) ? 0u : b1step;
     const uint32_t khi = (b1 == kTabBins - 1) ? 0xffffffffu : (b1step | ((1u << kTabDigitShift) - 1u));
     auto in_b1 = [&](uint32_t key) { return key >= klo && key <= khi; };
+    // the candidates appended a wave at a time: one LDS atomic per wave and
+    // slot with candidates (same-address atomics from many lanes serialize)
+    const int lane = tid & 63;
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
-      if (((vm >> j) & 1u) && in_b1(k[j])) {
-        const int c = atomicAdd(&sh[2], 1);
-        if (c < kRankMax) cand[c] = k[j];
+      const bool is_c = ((vm >> j) & 1u) && in_b1(k[j]);
+      const uint64_t bal = __ballot(is_c);
+      if (bal) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&sh[2], __popcll(bal));
+        base = __shfl(base, 0);
+        const int c = base + __popcll(bal & ((1ull << lane) - 1ull));
+        if (is_c && c < kRankMax) cand[c] = k[j];
       }
     }
     __syncthreads();
@@ -244,11 +252,20 @@ __global__ __launch_bounds__(ST) void stream_select_kernel(StreamSelectParams p,
         const uint32_t ki = cand[i];
         int gt = 0, eq = 0;
         const uint4 *c4 = reinterpret_cast<const uint4 *>(cand);
-        for (int q = 0; q < (m4 >> 2); ++q) {
-          const uint4 kq = c4[q];
+        auto cmp = [&](const uint4 kq) {
           gt += (kq.x > ki) + (kq.y > ki) + (kq.z > ki) + (kq.w > ki);
           eq += (kq.x == ki) + (kq.y == ki) + (kq.z == ki) + (kq.w == ki);
+        };
+        const int n4 = m4 >> 2;
+        int q = 0;
+        for (; q + 4 <= n4; q += 4) {  // four reads in flight
+          const uint4 k0 = c4[q], k1 = c4[q + 1], k2 = c4[q + 2], k3 = c4[q + 3];
+          cmp(k0);
+          cmp(k1);
+          cmp(k2);
+          cmp(k3);
         }
+        for (; q < n4; ++q) cmp(c4[q]);
         eq -= (ki == 0u) ? (m4 - mc) : 0;  // the padding
         if (gt < rest && gt + eq >= rest) {
           sh[3] = (int)ki;
