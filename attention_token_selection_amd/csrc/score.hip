@@ -214,11 +214,10 @@ __device__ inline float row_log2_weight(const ScoreParams &p, int row) {
 // 0 then takes in share 1.  Every pass-2 workgroup of the segment computes
 // the same bits.  The first batch of loads is issued before the key tiles
 // (so that waiting for it does not mean waiting for them), by
-// MergeRows::load; MergeRows::finish does the rest.  With MB = 32 one batch
-// covers 64 block states (a whole 32K-key prefix in blocks of 512), so the
-// biases are ready about when the first tiles land.
-template <int MB>
+// MergeRows::load; MergeRows::finish does the rest.  One batch covers 32
+// block states (a whole 32K-key prefix in pass 1's blocks of 1024).
 struct MergeRows {
+  static constexpr int MB = 16;
   float2 v[MB];
   int row, sh;
   const float2 *all;
@@ -441,8 +440,12 @@ __device__ void tables_epilogue(const ScoreParams &p, float *red, int rs, uint32
 // keys 16 (v % 2) .. + 15, with v_mfma_f32_16x16x32_bf16, so that no wave
 // carries a whole extra tile (the slowest wave sets every step's pace).
 // TAB (pass 2 only): the halo tile, pool and selection tables (see top).
+// The waves per SIMD the registers are planned for: pass 2 with tables and
+// one whole row tile per wave fits three (168 VGPRs), so that three
+// workgroups share a compute unit and one's prologue and epilogue overlap
+// the others' key streams (measured faster than two); pass 2 otherwise two.
 template <int PASS, int RT, bool SPLIT = false, bool TAB = false>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 2 && RT == 1) ? 2 : SPLIT ? (RT > 2 ? 1 : 2) : RT > 1 ? 1 : 4))) void score_kernel(ScoreParams p, SegTable t) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 2 && RT == 1) ? ((TAB && !SPLIT) ? 3 : 2) : SPLIT ? (RT > 2 ? 1 : 2) : RT > 1 ? 1 : 4))) void score_kernel(ScoreParams p, SegTable t) {
   extern __shared__ float red[];  // pass 2: [NW][rs] partial sums (TAB: then S by position)
 
   const int blk = blockIdx.x;
@@ -563,7 +566,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 2 &
   // at most 2 (PD - 2) loads remain means tile t has landed.
   const uint16_t *kh = p.K + key0 * (int64_t)rowstride + (int64_t)h * kHeadDim;
   auto issue = [&](char *slot, int ti) { issue_keys(slot, kh, halo && ti == ntile, ti, kb0, kb1, L, rowstride, wave, lane); };
-  MergeRows<(RT == 1 && !SPLIT) ? 32 : 16> mr;  // (one row tile per wave leaves the registers for 32)
+  MergeRows mr;
   const int nstat = (int)((L + (int64_t)p.stat_block - 1) / p.stat_block);  // pass-1 block states per row
   if constexpr (PASS == 2) mr.load(p, seg, nstat);
 #pragma unroll
