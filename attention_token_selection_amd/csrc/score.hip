@@ -69,10 +69,12 @@ constexpr int KT = kKeyTile;             // 32 keys per tile
 constexpr int ROWB = kHeadDim * 2;       // 256 bytes per key row
 constexpr int TILE_BYTES = KT * ROWB;    // 8 KiB
 static_assert(TILE_BYTES == 2 * 16 * NT, "each thread moves two 16-byte chunks per tile");
-constexpr int PD = 4;                    // LDS ring slots; tiles in flight = PD - 1
-// s_waitcnt immediate for vmcnt(2 (PD - 2)) with the other counters left alone.
-constexpr int kWaitTile = 0x3F70 | (2 * (PD - 2));
-static_assert(PD >= 3 && PD <= 8 && 2 * (PD - 2) < 16, "at most eight named slots; vmcnt fits the low field");
+// LDS ring slots per pass (tiles in flight = slots - 1).
+constexpr int kRing1 = 4;
+constexpr int kRing2 = 4;
+// s_waitcnt immediate for vmcnt(2 (pd - 2)) with the other counters left alone.
+constexpr int wait_tile(int pd) { return 0x3F70 | (2 * (pd - 2)); }
+static_assert(kRing1 >= 3 && kRing1 <= 8 && kRing2 >= 3 && kRing2 <= 8, "at most eight named slots; vmcnt fits the low field");
 
 // The LDS ring: one array per slot, so that the compiler can tell a slot
 // being read from the slots that loads are landing in (ring(i) is only ever
@@ -447,6 +449,8 @@ __device__ void tables_epilogue(const ScoreParams &p, float *red, int rs, uint32
 template <int PASS, int RT, bool SPLIT = false, bool TAB = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 2 && RT == 1) ? ((TAB && !SPLIT) ? 3 : 2) : SPLIT ? (RT > 2 ? 1 : 2) : RT > 1 ? 1 : 4))) void score_kernel(ScoreParams p, SegTable t) {
   extern __shared__ float red[];  // pass 2: [NW][rs] partial sums (TAB: then S by position)
+  constexpr int PD = (PASS == 1) ? kRing1 : kRing2;  // LDS ring slots
+  constexpr int kWaitTile = wait_tile(PD);
 
   const int blk = blockIdx.x;
   const int h = blockIdx.y;
