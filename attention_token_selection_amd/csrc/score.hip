@@ -445,9 +445,11 @@ __device__ void tables_epilogue(const ScoreParams &p, float *red, int rs, uint32
 // The waves per SIMD the registers are planned for: pass 2 with tables and
 // one whole row tile per wave fits three (168 VGPRs), so that three
 // workgroups share a compute unit and one's prologue and epilogue overlap
-// the others' key streams (measured faster than two); pass 2 otherwise two.
+// the others' key streams (measured faster than two); pass 2 otherwise two;
+// pass 1 with one whole row tile per wave two (room for PIPE's second
+// accumulator set), else as the row tiles allow.
 template <int PASS, int RT, bool SPLIT = false, bool TAB = false>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 2 && RT == 1) ? ((TAB && !SPLIT) ? 3 : 2) : SPLIT ? (RT > 2 ? 1 : 2) : RT > 1 ? 1 : 4))) void score_kernel(ScoreParams p, SegTable t) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 1 && RT == 1 && !SPLIT) ? 2 : (PASS == 2 && RT == 1) ? ((TAB && !SPLIT) ? 3 : 2) : SPLIT ? (RT > 2 ? 1 : 2) : RT > 1 ? 1 : 4))) void score_kernel(ScoreParams p, SegTable t) {
   extern __shared__ float red[];  // pass 2: [NW][rs] partial sums (TAB: then S by position)
   constexpr int PD = (PASS == 1) ? kRing1 : kRing2;  // LDS ring slots
   constexpr int kWaitTile = wait_tile(PD);
@@ -600,9 +602,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 2 &
   // tile t's MFMAs and then does tile t - 1's exp / sum work, which depends
   // only on registers, so the wave's VALU work runs while its matrix core
   // works (two accumulator sets alternate); without PIPE both stages of
-  // tile t run in step t.  PIPE is used where it measured faster: pass 2
-  // with one row tile per wave.
-  constexpr bool PIPE = PASS == 2 && RT == 1;  // measured: helps there, costs pass 1 and two-tile waves
+  // tile t run in step t.  PIPE is used where it measured faster: one row
+  // tile per wave (in pass 1 without a split tile; its registers are then
+  // planned for two waves per SIMD); with two row tiles per wave it is slower.
+  constexpr bool PIPE = RT == 1 && (PASS == 2 || !SPLIT);
   static_assert(!PIPE || PD % 2 == 0, "accumulator sets alternate with the slot parity");
   f32x16 accs[PIPE ? 2 : 1][RT];
   f32x4 saccs[PIPE ? 2 : 1];
