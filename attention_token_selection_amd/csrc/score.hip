@@ -603,9 +603,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 1 &
   // only on registers, so the wave's VALU work runs while its matrix core
   // works (two accumulator sets alternate); without PIPE both stages of
   // tile t run in step t.  PIPE is used where it measured faster: one row
-  // tile per wave (in pass 1 without a split tile; its registers are then
-  // planned for two waves per SIMD); with two row tiles per wave it is slower.
-  constexpr bool PIPE = RT == 1 && (PASS == 2 || !SPLIT);
+  // tile per wave and no split tile (pass 1's registers are then planned for
+  // two waves per SIMD); with two row tiles per wave, or a split tile, it is
+  // slower.
+  constexpr bool PIPE = RT == 1 && !SPLIT;
   static_assert(!PIPE || PD % 2 == 0, "accumulator sets alternate with the slot parity");
   f32x16 accs[PIPE ? 2 : 1][RT];
   f32x4 saccs[PIPE ? 2 : 1];
