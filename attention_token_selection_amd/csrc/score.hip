@@ -528,6 +528,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 1 &
   const int skey = 16 * (wave & 1);                  // first key of this wave's block in a key tile
   bf16x8 qs[4];
   float ref5 = -INFINITY, zs5 = 0.0f, bias5[4];
+  int lim5r[4] = {0, 0, 0, 0};  // pass 2: the split rows' causal limits
   int lim5 = 0;
   if constexpr (SPLIT) {
     const int row = srow + s16;
@@ -593,7 +594,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 1 &
     }
     if constexpr (SPLIT) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bias5[i] = bias_s[srow + 4 * s4 + i];
+      for (int i = 0; i < 4; ++i) {
+        bias5[i] = bias_s[srow + 4 * s4 + i];
+        lim5r[i] = row_limit(srow + 4 * s4 + i, p, L);  // the split rows' causal limits
+      }
     }
   }
 
@@ -754,10 +758,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 1 &
         // then over the four lane groups: every lane then holds the block's
         // sum for key skey + s16, which lane lr adds when that is its key.
         float s5 = 0.0f;
+        if (!need_mask) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = fast_exp2(fmaf(sacc[i], cl2, -bias5[i]));
-          s5 += (need_mask && key_at(skey + s16) > row_limit(srow + 4 * s4 + i, p, L)) ? 0.0f : v;
+          for (int i = 0; i < 4; ++i) s5 += fast_exp2(fmaf(sacc[i], cl2, -bias5[i]));
+        } else {
+          const int key5 = key_at(skey + s16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = fast_exp2(fmaf(sacc[i], cl2, -bias5[i]));
+            s5 += (key5 > lim5r[i]) ? 0.0f : v;
+          }
         }
         s5 += __shfl_xor(s5, 16);
         s5 += __shfl_xor(s5, 32);
