@@ -138,6 +138,31 @@ __device__ uint64_t block_sum64(uint64_t v, uint64_t *tmp64) {
   return tot;
 }
 
+// Exclusive prefix sum of a 64-bit value over the workgroup (two 32-bit
+// counts packed in one scan as one, while neither sum reaches 2^32); also
+// returns the total.
+__device__ uint64_t block_exscan64(uint64_t v, uint64_t *tmp64, uint64_t &total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint64_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) tmp64[wid] = x;
+  __syncthreads();
+  uint64_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; ++i) {
+    const uint64_t s = tmp64[i];
+    before += (i < wid) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return before + x - v;
+}
+
 struct Segment {
   const float *S;
   float *P;
@@ -679,47 +704,72 @@ __global__ __launch_bounds__(NT) void select_block_kernel(SelectParams p, SegTab
     const int need = g.keff - sh[1];  // keys of bin b1 to keep, >= 1
 
     // ---- per-block extent of bin b1, and candidate offsets
-    for (int j = tid; j < nb; j += NT) {
-      const int len = min(RBP, g.L - j * RBP);
-      const int lo = TF[(int64_t)j * NB2 + b1];
-      const int hi = (b1 + 1 < NB2) ? (int)TF[(int64_t)j * NB2 + b1 + 1] : len;
-      b_lo[j] = lo;
-      b_above[j] = len - hi;
-      b_cb[j] = hi - lo;
-      b_gt[j] = 0;
-      b_eq[j] = 0;
-    }
-    __syncthreads();
-    {
-      // exclusive prefix over the blocks of the candidate counts: thread tid
-      // owns blocks [BPT tid, BPT tid + BPT); and the keys above bin b1 in
-      // the blocks before this chunk's (CPB c onwards: one half of thread
-      // c / 2's share)
-      int a[BPT], s = 0, sa = 0, ah = 0;
-      const int h0 = (c & 1) * CPB;
-#pragma unroll
-      for (int u = 0; u < BPT; ++u) {
-        const int j = BPT * tid + u;
-        a[u] = (j < nb) ? b_cb[j] : 0;
-        s += a[u];
-        const int ab = (j < nb) ? b_above[j] : 0;
-        sa += ab;
-        ah += (u < h0) ? ab : 0;
+    if (nb <= NT) {
+      // one block per thread: the prefixes of both counts (candidates; keys
+      // above bin b1) in one packed scan, straight from the loads
+      const int j = tid;
+      uint32_t cbj = 0u, abj = 0u;
+      if (j < nb) {
+        const int len = min(RBP, g.L - j * RBP);
+        const int lo = TF[(int64_t)j * NB2 + b1];
+        const int hi = (b1 + 1 < NB2) ? (int)TF[(int64_t)j * NB2 + b1 + 1] : len;
+        b_lo[j] = lo;
+        b_above[j] = len - hi;
+        b_gt[j] = 0;
+        b_eq[j] = 0;
+        cbj = (uint32_t)(hi - lo);
+        abj = (uint32_t)(len - hi);
       }
-      int tot;
-      int ex = block_exscan(s, tmp, tot);
-      int tota;
-      const int exa = block_exscan(sa, tmp, tota);
-#pragma unroll
-      for (int u = 0; u < BPT; ++u) {
-        const int j = BPT * tid + u;
-        if (j < nb) b_cb[j] = ex;
-        ex += a[u];
+      __shared__ uint64_t tmpx[NWAVE];
+      uint64_t tot;
+      const uint64_t ex = block_exscan64(((uint64_t)abj << 32) | cbj, tmpx, tot);  // each sum < 2^32
+      if (j < nb) b_cb[j] = (int)(uint32_t)ex;
+      if (j == 0) b_cb[nb] = (int)(uint32_t)tot;
+      if (j == CPB * c) sh[2] = (int)(ex >> 32);  // the chunk's first block (< nb)
+      __syncthreads();
+    } else {
+      for (int j = tid; j < nb; j += NT) {
+        const int len = min(RBP, g.L - j * RBP);
+        const int lo = TF[(int64_t)j * NB2 + b1];
+        const int hi = (b1 + 1 < NB2) ? (int)TF[(int64_t)j * NB2 + b1 + 1] : len;
+        b_lo[j] = lo;
+        b_above[j] = len - hi;
+        b_cb[j] = hi - lo;
+        b_gt[j] = 0;
+        b_eq[j] = 0;
       }
-      if (tid == 0) b_cb[nb] = tot;
-      if (tid == (c >> 1)) sh[2] = exa + ah;
+      __syncthreads();
+      {
+        // exclusive prefix over the blocks of the candidate counts: thread tid
+        // owns blocks [BPT tid, BPT tid + BPT); and the keys above bin b1 in
+        // the blocks before this chunk's (CPB c onwards: one half of thread
+        // c / 2's share)
+        int a[BPT], s = 0, sa = 0, ah = 0;
+        const int h0 = (c & 1) * CPB;
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+          const int j = BPT * tid + u;
+          a[u] = (j < nb) ? b_cb[j] : 0;
+          s += a[u];
+          const int ab = (j < nb) ? b_above[j] : 0;
+          sa += ab;
+          ah += (u < h0) ? ab : 0;
+        }
+        int tot;
+        int ex = block_exscan(s, tmp, tot);
+        int tota;
+        const int exa = block_exscan(sa, tmp, tota);
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+          const int j = BPT * tid + u;
+          if (j < nb) b_cb[j] = ex;
+          ex += a[u];
+        }
+        if (tid == 0) b_cb[nb] = tot;
+        if (tid == (c >> 1)) sh[2] = exa + ah;
+      }
+      __syncthreads();
     }
-    __syncthreads();
     const int above_before = sh[2];  // keys above bin b1 in blocks [0, CPB c)
     const int m = b_cb[nb];  // keys in bin b1, >= need
 
@@ -769,43 +819,12 @@ __global__ __launch_bounds__(NT) void select_block_kernel(SelectParams p, SegTab
 
     // ---- tau, the need-th largest candidate key, and take_eq, how many of
     // the keys equal to it are kept (the lowest-positioned ones).  Few
-    // candidates (held in LDS): each candidate's count of larger and equal
-    // keys, by direct comparison with all of them (every thread reads the
-    // same LDS words, which the LDS broadcasts); the candidate whose larger
-    // count is below need and whose larger-or-equal count reaches it holds
-    // tau (every such candidate holds the same key).  Otherwise radix rounds
-    // over the candidates' keys: bits [21, 32), [10, 21), [0, 10).
+    // candidates (held in LDS): by direct ranking (rank_select).  Otherwise
+    // radix rounds over the candidates' keys: bits [21, 32), [10, 21), [0, 10).
     uint32_t tau;
     int take_eq;
     if (in_lds && m <= kRankCands) {
-      for (int i = m; i < ((m + 3) & ~3); ++i)  // pad to whole uint4 reads with keys below every key
-        if (tid == 0) candk[i] = 0u;
-      __syncthreads();
-      for (int i = tid; i < m; i += NT) {
-        const uint32_t ki = candk[i];
-        int gt = 0, eq = 0;
-        const uint4 *c4 = reinterpret_cast<const uint4 *>(candk);
-        const int n4 = (m + 3) >> 2;
-        auto cmp = [&](const uint4 kj) {
-          gt += (kj.x > ki) + (kj.y > ki) + (kj.z > ki) + (kj.w > ki);
-          eq += (kj.x == ki) + (kj.y == ki) + (kj.z == ki) + (kj.w == ki);
-        };
-        int j = 0;
-        for (; j + 4 <= n4; j += 4) {  // four reads in flight
-          const uint4 k0 = c4[j], k1 = c4[j + 1], k2 = c4[j + 2], k3 = c4[j + 3];
-          cmp(k0);
-          cmp(k1);
-          cmp(k2);
-          cmp(k3);
-        }
-        for (; j < n4; ++j) cmp(c4[j]);
-        eq -= (ki == 0u) ? (((m + 3) & ~3) - m) : 0;  // the padding keys are 0
-        if (gt < need && gt + eq >= need) {
-          sh[2] = (int)ki;
-          sh[3] = need - gt;
-        }
-      }
-      __syncthreads();
+      rank_select<NT>(candk, m, need, hist, sh + 2);
       tau = (uint32_t)sh[2];
       take_eq = sh[3];
     } else {

@@ -243,36 +243,8 @@ __global__ __launch_bounds__(ST) void stream_select_kernel(StreamSelectParams p,
     __syncthreads();
     const int mc = sh[2];  // keys in bin b1
     if (mc <= kRankMax) {
-      // each candidate's count of larger and equal candidates; the one whose
-      // larger count is below rest and larger-or-equal count reaches it is tau
-      const int m4 = (mc + 3) & ~3;
-      if (tid < m4 - mc) cand[mc + tid] = 0u;  // padding below every key
-      __syncthreads();
-      for (int i = tid; i < mc; i += ST) {
-        const uint32_t ki = cand[i];
-        int gt = 0, eq = 0;
-        const uint4 *c4 = reinterpret_cast<const uint4 *>(cand);
-        auto cmp = [&](const uint4 kq) {
-          gt += (kq.x > ki) + (kq.y > ki) + (kq.z > ki) + (kq.w > ki);
-          eq += (kq.x == ki) + (kq.y == ki) + (kq.z == ki) + (kq.w == ki);
-        };
-        const int n4 = m4 >> 2;
-        int q = 0;
-        for (; q + 4 <= n4; q += 4) {  // four reads in flight
-          const uint4 k0 = c4[q], k1 = c4[q + 1], k2 = c4[q + 2], k3 = c4[q + 3];
-          cmp(k0);
-          cmp(k1);
-          cmp(k2);
-          cmp(k3);
-        }
-        for (; q < n4; ++q) cmp(c4[q]);
-        eq -= (ki == 0u) ? (m4 - mc) : 0;  // the padding
-        if (gt < rest && gt + eq >= rest) {
-          sh[3] = (int)ki;
-          sh[4] = rest - gt;
-        }
-      }
-      __syncthreads();
+      // by direct ranking, the comparisons spread over the workgroup
+      rank_select<ST>(cand, mc, rest, hist, sh + 3);
       tau = (uint32_t)sh[3];
       take_eq = sh[4];
     } else {
