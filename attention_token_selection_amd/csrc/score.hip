@@ -178,6 +178,14 @@ __device__ inline float sum_halves(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+// x + (the same register of lane l ^ 16), the lane-l value first in lanes
+// whose bit 4 is clear (as x + shuffle-xor 16 would add, in the same order
+// up to the commutation of one addition).
+__device__ inline float sum_rows16(float x) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 // The value of x held by lane l ^ 32.
 __device__ inline float other_half(float x) {
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -769,8 +777,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 1 &
             s5 += (key5 > lim5r[i]) ? 0.0f : v;
           }
         }
-        s5 += __shfl_xor(s5, 16);
-        s5 += __shfl_xor(s5, 32);
+        s5 = sum_halves(sum_rows16(s5));
         s += ((lr >> 4) == (wave & 1)) ? s5 : 0.0f;
       }
       if (hf == 0) red[rbase + lr] = s;
