@@ -82,6 +82,11 @@ struct ScoreParams {
   uint32_t *step_keys;
   int64_t step_stride;
   int step_origin;
+  // Pass 2 with the pool: workgroups with linear index in [young_from,
+  // 2 young_from) (the second of two per compute unit) raise their waves'
+  // priority for the first half of their key tiles; 0: off.  Set by the
+  // launch from the device's compute units.
+  int young_from;
 };
 
 // The mean query of every (sequence, observation row, KV head): the G query

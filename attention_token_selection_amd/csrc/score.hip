@@ -53,6 +53,8 @@
 // function of the key, so equal values share a bin and higher bins hold
 // larger keys, and it leaves a few hundred keys in the bin of the k-th
 // largest where a fixed slice of the key's top bits leaves thousands.
+#include <atomic>
+
 #include "kvsel_internal.h"
 #include "kvsel_device.h"
 
@@ -465,6 +467,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 1 &
   const int blk = blockIdx.x;
   const int h = blockIdx.y;
   const int sb = blockIdx.z;
+  // Pass 2 with the pool runs two workgroups per compute unit, and the one
+  // dispatched first wins the issue arbitration (older waves go first): the
+  // second would finish about 4 us later at c2, alone on the unit for that
+  // time.  The second ones take a higher priority for the first half of
+  // their key tiles, which evens the two out.
+  const int wg_lin = blk + (int)gridDim.x * (h + (int)gridDim.y * sb);
+  const bool young = PASS == 2 && TAB && p.young_from > 0 && wg_lin >= p.young_from && wg_lin < 2 * p.young_from;
+  if (young) __builtin_amdgcn_s_setprio(1);
   const int64_t key0 = t.key_off[sb];
   const int L = (int)(t.key_off[sb + 1] - key0);
   // Keys key_begin + blk * key_block onwards, clipped to [key_begin,
@@ -806,6 +816,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 1 &
   };
   const int nloop = PIPE ? nsteps + 1 : nsteps;  // PIPE: one more step for the last tile's exp / sum
   for (int t0 = 0; t0 < nloop; t0 += PD) {
+    if (young && t0 == ((nloop / 2) & ~(PD - 1))) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int j = 0; j < PD; ++j) step(t0 + j, j, ring(j), ring((j + PD - 1) % PD));
   }
@@ -950,12 +961,27 @@ hipError_t launch_score_pass2(const ScoreParams &p, const SegTable &t, int nblk,
   return launch_pass<2>(p, t, nblk, s, (size_t)NW * p.key_block * sizeof(float));
 }
 
+// The compute units of the current device (cached per device; 0 if unknown).
+static int compute_units() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) n = 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 hipError_t launch_score_pass2_tables(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
   if (p.key_block % kTabBlock != 0 || p.pool_r < 0 || p.pool_r > kPoolHalo || !p.pooled || !p.tab || !p.bucket ||
       !p.seg_hist || p.step_keys)
     return hipErrorInvalidValue;
   const size_t rs = (size_t)p.key_block + 2 * kPoolHalo;
-  return launch_pass<2, true>(p, t, nblk, s, (NW + 1) * rs * sizeof(float));
+  ScoreParams q = p;
+  q.young_from = compute_units();
+  return launch_pass<2, true>(q, t, nblk, s, (NW + 1) * rs * sizeof(float));
 }
 
 hipError_t launch_score_pass2_keys(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
@@ -963,7 +989,9 @@ hipError_t launch_score_pass2_keys(const ScoreParams &p, const SegTable &t, int 
       p.tab || p.pooled || p.scores || p.step_stride <= 0)
     return hipErrorInvalidValue;
   const size_t rs = (size_t)p.key_block + 2 * kPoolHalo;
-  return launch_pass<2, true>(p, t, nblk, s, (NW + 1) * rs * sizeof(float));
+  ScoreParams q = p;
+  q.young_from = compute_units();
+  return launch_pass<2, true>(q, t, nblk, s, (NW + 1) * rs * sizeof(float));
 }
 
 }  // namespace kvsel
