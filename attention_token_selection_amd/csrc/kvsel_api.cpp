@@ -268,7 +268,8 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   // as many workgroups): pass 1 itself slows a little, but pass 2 merges
   // half as many block states in its prologue, which gains more (the
   // Llama-shaped 32K layer: 1.96-1.97 against 2.00 ms per 32-layer step);
-  // with more row tiles per wave it loses (c3, c4).
+  // with more row tiles per wave it loses (256 rows per KV head; five row
+  // tiles with a decode row).
   if (P.nrt <= kScoreThreads / 64) P.kb1 = std::min(4096, 2 * auto_key_block(head_keys, 2048));
   if (p->key_chunk > 0) P.kb1 = std::min(P.kb1, p->key_chunk);
   P.kb2 = auto_key_block(head_keys, 2048);

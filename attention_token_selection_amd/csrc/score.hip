@@ -467,13 +467,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 1 &
   const int blk = blockIdx.x;
   const int h = blockIdx.y;
   const int sb = blockIdx.z;
-  // Pass 2 with the pool runs two workgroups per compute unit, and the one
-  // dispatched first wins the issue arbitration (older waves go first): the
-  // second would finish about 4 us later at c2, alone on the unit for that
-  // time.  The second ones take a higher priority for the first half of
-  // their key tiles, which evens the two out.
+  // Launches of two workgroups per compute unit (pass 2 with the pool; pass
+  // 1 with two row tiles per wave): the workgroup dispatched first wins the
+  // issue arbitration (older waves go first), and the second finished about
+  // 4 us later on a 32K-key Llama-shaped layer, alone on the unit for that
+  // time.  The second ones (linear index in [young_from, 2 young_from)) take
+  // a higher priority for the first half of their key tiles, which evens
+  // the two out.  Only where it measured faster: the check in the loop cost
+  // pass 1 with one row tile per wave (one workgroup per unit there) 2%.
+  constexpr bool PRIO = (PASS == 2 && TAB) || RT > 1;
   const int wg_lin = blk + (int)gridDim.x * (h + (int)gridDim.y * sb);
-  const bool young = PASS == 2 && TAB && p.young_from > 0 && wg_lin >= p.young_from && wg_lin < 2 * p.young_from;
+  const bool young = PRIO && p.young_from > 0 && wg_lin >= p.young_from && wg_lin < 2 * p.young_from;
   if (young) __builtin_amdgcn_s_setprio(1);
   const int64_t key0 = t.key_off[sb];
   const int L = (int)(t.key_off[sb + 1] - key0);
@@ -947,20 +951,6 @@ hipError_t launch_pass(const ScoreParams &p, const SegTable &t, int nblk, hipStr
 
 }  // namespace
 
-hipError_t launch_score_pass1(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
-  return launch_pass<1>(p, t, nblk, s, 0);
-}
-
-hipError_t launch_stream_stats(const ScoreParams &p, const SegTable &t, float2 *run, int first, hipStream_t s) {
-  const dim3 grid((p.Rpad + MERGE_ROWS - 1) / MERGE_ROWS, t.nseq * p.Hkv);
-  hipLaunchKernelGGL(fold_kernel, grid, dim3(NT), 0, s, p, t, run, first);
-  return hipGetLastError();
-}
-
-hipError_t launch_score_pass2(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
-  return launch_pass<2>(p, t, nblk, s, (size_t)NW * p.key_block * sizeof(float));
-}
-
 // The compute units of the current device (cached per device; 0 if unknown).
 static int compute_units() {
   static std::atomic<int> cached[64];
@@ -972,6 +962,24 @@ static int compute_units() {
     cached[dev].store(n, std::memory_order_relaxed);
   }
   return n;
+}
+
+hipError_t launch_score_pass1(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
+  ScoreParams q = p;
+  q.young_from = compute_units();
+  return launch_pass<1>(q, t, nblk, s, 0);
+}
+
+hipError_t launch_stream_stats(const ScoreParams &p, const SegTable &t, float2 *run, int first, hipStream_t s) {
+  const dim3 grid((p.Rpad + MERGE_ROWS - 1) / MERGE_ROWS, t.nseq * p.Hkv);
+  hipLaunchKernelGGL(fold_kernel, grid, dim3(NT), 0, s, p, t, run, first);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_pass2(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
+  ScoreParams q = p;
+  q.young_from = compute_units();
+  return launch_pass<2>(q, t, nblk, s, (size_t)NW * p.key_block * sizeof(float));
 }
 
 hipError_t launch_score_pass2_tables(const ScoreParams &p, const SegTable &t, int nblk, hipStream_t s) {
