@@ -273,15 +273,16 @@ kvsel_status make_plan(const kvsel_problem *p, Plan &P) {
   if (P.nrt <= kScoreThreads / 64) P.kb1 = std::min(4096, 2 * auto_key_block(head_keys, 2048));
   if (p->key_chunk > 0) P.kb1 = std::min(P.kb1, p->key_chunk);
   // Pass 2 in blocks of at most 2048 keys (its LDS then allows two
-  // workgroups per compute unit), or 1024 for a batch of unequal lengths:
-  // their last, partial blocks leave the launch's last round of workgroups
-  // uneven, and finer blocks even it out (a ragged batch of eight 21K-62K
-  // sequences: 479-491 against 516-518 us per call; equal lengths and one
-  // sequence lose with 1024).
+  // workgroups per compute unit).  A batch of unequal lengths takes at most
+  // 1024 (pass 2) and 2048 (pass 1): the sequences' last, partial blocks
+  // leave a launch's last round of workgroups uneven, and finer blocks even
+  // it out (a ragged batch of eight 21K-62K sequences: 449-455 against
+  // 516-529 us per call; equal lengths and one sequence lose with them).
   bool ragged = false;
   for (int b = 1; b < P.B; ++b)
     ragged |= (P.seq_off[b + 1] - P.seq_off[b]) != (P.seq_off[1] - P.seq_off[0]);
   P.kb2 = auto_key_block(head_keys, ragged ? 1024 : 2048);
+  if (ragged) P.kb1 = std::min(P.kb1, 2048);
   P.nblk1_max = (int)((P.Lmax + P.kb1 - 1) / P.kb1);
   P.nblk2_max = (int)((P.Lmax + P.kb2 - 1) / P.kb2);
 
