@@ -468,14 +468,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu((PASS == 1 &
   const int h = blockIdx.y;
   const int sb = blockIdx.z;
   // Launches of two workgroups per compute unit (pass 2 with the pool; pass
-  // 1 with two row tiles per wave): the workgroup dispatched first wins the
-  // issue arbitration (older waves go first), and the second finished about
-  // 4 us later on a 32K-key Llama-shaped layer, alone on the unit for that
-  // time.  The second ones (linear index in [young_from, 2 young_from)) take
-  // a higher priority for the first half of their key tiles, which evens
-  // the two out.  Only where it measured faster: the check in the loop cost
-  // pass 1 with one row tile per wave (one workgroup per unit there) 2%.
-  constexpr bool PRIO = (PASS == 2 && TAB) || RT > 1;
+  // 1 with two row tiles per wave or a split one): the workgroup dispatched
+  // first wins the issue arbitration (older waves go first), and the second
+  // finished about 4 us later on a 32K-key Llama-shaped layer, alone on the
+  // unit for that time.  The second ones (linear index in [young_from,
+  // 2 young_from)) take a higher priority for the first half of their key
+  // tiles, which evens the two out.  Only where it measured faster: the
+  // check in the loop cost pass 1 with one whole row tile per wave (one
+  // workgroup per unit there) 2%.
+  constexpr bool PRIO = (PASS == 2 && TAB) || RT > 1 || SPLIT;
   const int wg_lin = blk + (int)gridDim.x * (h + (int)gridDim.y * sb);
   const bool young = PRIO && p.young_from > 0 && wg_lin >= p.young_from && wg_lin < 2 * p.young_from;
   if (young) __builtin_amdgcn_s_setprio(1);
